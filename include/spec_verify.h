@@ -1,0 +1,215 @@
+/*
+ * spec_verify.h -- C ABI of libspecverify.so: batched speculative-sampling
+ * verification over full-vocabulary bf16 logits on AMD Instinct MI355X (gfx950).
+ *
+ * Sources, cited by page and section:
+ *   [LT] "Speculative Decoding 为什么是 Lossless 的 -- 详细证明教程" (restates
+ *        Leviathan et al. 2023 App. A.1 and Chen et al. 2023 Thm 1; p = target,
+ *        q = draft).
+ *   [NB] Paper note "Not-a-Bandit: Provably No-Regret Drafter Selection in
+ *        Speculative Decoding for LLMs" (HedgeSpec), Key designs 1-4.
+ *   [CA] Paper note "Cactus: Accelerating Auto-Regressive Decoding with
+ *        Constrained Acceptance Speculative Sampling", Key designs 1-3.
+ *   [NH] Chaudhuri, Freund, Hsu, "A parameter-free hedging algorithm" (2009).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.  Every array pointer is a DEVICE pointer owned by the caller.  The
+ *   library allocates nothing, keeps no pointer after a call returns and has no
+ *   global state; the only memory it writes besides the outputs is the caller's
+ *   workspace.
+ * Streams.  Calls enqueue kernels on `stream` and return at once.  A non-zero
+ *   return means nothing was launched (argument error) or the launch itself
+ *   failed (SPEC_ERR_HIP); device faults surface at the caller's next
+ *   synchronisation.
+ * Logits.  Rows are bf16 (raw bit patterns), V-contiguous.  A row stride is in
+ *   elements, must be >= V and a multiple of 8, and every base pointer must be
+ *   16-byte aligned (rows are streamed with 128-bit loads).  When V is not a
+ *   multiple of 8 the elements of a row from V up to the next multiple of 8 are
+ *   read and ignored, so each row's storage must extend that far.  Logits must
+ *   be finite or -inf, with at least one finite logit per row and
+ *   |logit| / T < 1e30; anything else gives unspecified (but in-bounds) results.
+ * Temperature.  One T > 0 scales every row, target and draft alike ([LT] §8 Q4:
+ *   shaping is folded into both distributions before any ratio is formed).
+ * Uniforms.  r and u are float32 in [0, 1), drawn by the caller: the library
+ *   draws no random numbers.
+ * Workspace.  `workspace` holds per-call ticket counters and per-position
+ *   scratch.  Size it with spec_workspace_bytes() and zero it once with
+ *   spec_workspace_init() (or any zero fill) before first use; every completed
+ *   call leaves it zeroed again, so no per-call clearing is needed.  Calls
+ *   that run concurrently must use different workspaces.
+ * Bad token ids.  A drafted or trajectory token outside [0, V) is reported in
+ *   the outputs (see each call), never by a fault.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t spec_bf16;      /* raw bf16 bits */
+struct ihipStream_t;             /* hipStream_t == struct ihipStream_t* */
+typedef struct ihipStream_t* spec_stream_t;
+
+enum {
+  SPEC_OK = 0,
+  SPEC_ERR_NULL = -1,      /* a required pointer is NULL */
+  SPEC_ERR_SHAPE = -2,     /* B, K, N, V out of range or stride < V / not a multiple of 8 */
+  SPEC_ERR_PARAM = -3,     /* temperature, delta or loss_scale not finite / out of range */
+  SPEC_ERR_ALIGN = -4,     /* a logits base pointer is not 16-byte aligned */
+  SPEC_ERR_WORKSPACE = -5, /* workspace NULL, misaligned or smaller than spec_workspace_bytes() */
+  SPEC_ERR_HIP = -6        /* the HIP launch failed */
+};
+
+/* Limits checked by every call. */
+#define SPEC_MAX_V (1 << 20)   /* vocabulary size */
+#define SPEC_MAX_K 64          /* draft positions per sequence */
+#define SPEC_MAX_N 64          /* drafters */
+
+/* Human-readable text for a status code (static storage). */
+const char* spec_status_str(int status);
+
+/* Bytes of workspace one call with these B, K, N needs (N = 1 for the
+ * verify calls).  256-byte aligned layout; pass the same B, K, N. */
+size_t spec_workspace_bytes(int B, int K, int N);
+
+/* Zero `bytes` of workspace on `stream` with a fill kernel (no memset node). */
+int spec_workspace_init(void* workspace, size_t bytes, spec_stream_t stream);
+
+/*
+ * spec_verify -- lossless speculative sampling, K drafts per sequence.
+ *
+ * Computes, for every sequence b, the standard draft-then-verify round of [LT]
+ * §5.1 (SpecSampleOne) chained over K positions as in [LT] §9.1:
+ *   pt_k = softmax(target[b][k] / T), pd_k = softmax(draft[b][k] / T);
+ *   position k accepts its drafted token t iff r[b][k] < pt_k(t) / pd_k(t)
+ *   (strict; [LT] §2.2 and §5.1);
+ *   A = the first rejected position, or K if every position accepts;
+ *   if A < K: out_token = inverse CDF of (pt_A - pd_A)+ at u[b][A] * Z, with
+ *     Z = sum (pt_A - pd_A)+  ([LT] §2.2, §6.4 Step 3a); if Z is exactly 0
+ *     the token is drawn from pt_A instead;
+ *   if A == K: out_token = inverse CDF of pt_K at u[b][K] (the bonus token of
+ *     the (K+1)-th target position).
+ * The inverse CDF is over ascending token ids: the smallest j with C_j > x.
+ *
+ * target        [B][K+1] rows, row (b,k) at target + (b*(K+1)+k)*target_row_stride
+ * draft         [B][K] rows,   row (b,k) at draft + (b*K+k)*draft_row_stride
+ * draft_tokens  [B][K] int32 drafted ids
+ * r_accept      [B][K] float32 accept uniforms
+ * u_resample    [B][K+1] float32 resample / bonus uniforms
+ * accepted_len  [B] int32 out: A in [0, K], or -1 if any drafted id of the
+ *               sequence is outside [0, V)
+ * out_token     [B] int32 out: the resampled or bonus token, -1 as above
+ * accept_mask   [B][K] uint8 out or NULL: each position's own test (1 accept),
+ *               evaluated at every position, including after the first
+ *               rejection; 0 for an invalid id
+ * Limits: 1 <= B, 1 <= K <= SPEC_MAX_K, 1 <= V <= SPEC_MAX_V, T > 0 finite.
+ */
+int spec_verify(const spec_bf16* target, int64_t target_row_stride,
+                const spec_bf16* draft, int64_t draft_row_stride,
+                const int32_t* draft_tokens, const float* r_accept, const float* u_resample,
+                int B, int K, int V, float temperature,
+                int32_t* accepted_len, int32_t* out_token, uint8_t* accept_mask,
+                void* workspace, size_t workspace_bytes, spec_stream_t stream);
+
+/*
+ * spec_cactus_verify -- Cactus constrained acceptance, m drafts per sequence.
+ *
+ * [CA] Key designs 1-3 with Cactus's q = the verifier softmax pt and p = the
+ * draft softmax pd.  At position k with candidate n = draft_tokens[b][k]:
+ *   c = pt_k(n); gamma* = min(c + sqrt(2 delta c (1 - c)), 1)   (Key design 3);
+ *   accept iff r[b][k] < gamma* / pd_k(n)  (acceptance min(1, h_n / pd(n)));
+ * at the first rejection A the token is drawn from g = (h - pd_A)+ / Z with the
+ * closed-form target h of Key design 2: h_n = gamma*, h_x = s * pt_A(x) for
+ * x != n, s = (1 - gamma*) / (1 - c) (s = 0 when c = 1); if Z is exactly 0
+ * the token is drawn from h.  If all m accept, the bonus is drawn from pt_m.
+ * delta = 0 runs exactly the spec_verify arithmetic (h == pt), so both calls
+ * return bit-identical results on the same inputs.
+ *
+ * Layout and outputs as spec_verify with K = m, plus
+ * gamma_star    [B][m] float32 out or NULL: gamma* at every position.
+ * delta >= 0 and finite.
+ */
+int spec_cactus_verify(const spec_bf16* verifier, int64_t verifier_row_stride,
+                       const spec_bf16* draft, int64_t draft_row_stride,
+                       const int32_t* draft_tokens, const float* r_accept, const float* u_resample,
+                       int B, int m, int V, float delta, float temperature,
+                       int32_t* accepted_len, int32_t* out_token, uint8_t* accept_mask,
+                       float* gamma_star,
+                       void* workspace, size_t workspace_bytes, spec_stream_t stream);
+
+/*
+ * spec_counterfactual_gamma -- HedgeSpec full-information evaluation of N drafters.
+ *
+ * For every sequence b, position k < K and drafter i ([NB] Key design 1, and
+ * [LT] §6.3 for the identity with the acceptance probability):
+ *   gamma[b][k][i] = sum_x min(pt_k(x), pd_{i,k}(x)) = 1 - TV(pt_k, pd_{i,k}).
+ * With the realised trajectory tokens x_k = traj_tokens[b][k] and
+ *   a_k = min(1, pd_{i,k}(x_k) / pt_k(x_k)),
+ * the one-step acceptance-length estimator ([NB] Key design 2; the printed
+ * formula was lost, this is the reading that is unbiased with range [1, K+1])
+ *   est_len[b][i] = 1 + sum_{k<K} gamma[b][k][i] * prod_{j<k} a_j
+ * and the loss ([NB] Key design 3, length objective)
+ *   loss[b][i] = (K + 1) - est_len[b][i].
+ * Only traj_tokens[b][0..K-2] enter; an id outside [0, V) there makes
+ * est_len and loss of that sequence NaN (gamma is still written).
+ *
+ * target        rows (b,k) at target + (b*target_rows_per_seq + k)*target_row_stride,
+ *               k < K (k = K also used by the fused verify below)
+ * drafts        row (i,b,k) at drafts + i*drafter_stride + (b*K+k)*draft_row_stride
+ * gamma [B][K][N], est_len [B][N], loss [B][N]  float32 out.
+ *
+ * Fused verify (one launch for evaluation and verification): when sel is not
+ * NULL, every sequence b is also verified exactly as spec_verify does, using
+ * drafter sel[b]'s rows as the draft, draft_tokens / r_accept / u_resample as
+ * in spec_verify, and target row K of the sequence for the bonus (so
+ * target_rows_per_seq must be K+1); results go to accepted_len / out_token /
+ * accept_mask (accept_mask may be NULL).  A sel[b] outside [0, N) makes that
+ * sequence's accepted_len and out_token -1.
+ * Limits: 1 <= N <= SPEC_MAX_N, target_rows_per_seq >= K (K+1 when fused).
+ * Workspace: spec_workspace_bytes(B, K, N).
+ */
+int spec_counterfactual_gamma(const spec_bf16* target, int64_t target_row_stride, int target_rows_per_seq,
+                              const spec_bf16* drafts, int64_t draft_row_stride, int64_t drafter_stride,
+                              const int32_t* traj_tokens,
+                              int B, int K, int N, int V, float temperature,
+                              float* gamma, float* est_len, float* loss,
+                              const int32_t* sel, const int32_t* draft_tokens,
+                              const float* r_accept, const float* u_resample,
+                              int32_t* accepted_len, int32_t* out_token, uint8_t* accept_mask,
+                              void* workspace, size_t workspace_bytes, spec_stream_t stream);
+
+/*
+ * hedge_update -- one NormalHedge round per sequence ([NH]; named by [NB] Key
+ * design 3 as the full-information learner; one learner per sequence).
+ *
+ * For every b with has_loss[b] != 0 (or every b if has_loss is NULL), with
+ * l_i = loss[b][i] * loss_scale and w = weights[b]:
+ *   lhat = sum_i w_i l_i;  cum_regret[b][i] += lhat - l_i;
+ *   if no cum_regret[b][i] > 0: weights[b] = uniform; otherwise find c > 0 with
+ *   (1/N) sum_i exp([R_i]+^2 / (2c)) = e (fp64 bisection on
+ *   [M^2 / (2(1 + ln N)), M^2 / 2], M = max [R]+) and set
+ *   weights[b][i] proportional to ([R_i]+ / c) exp([R_i]+^2 / (2c)).
+ * Then, if v_select is not NULL, sel_out[b] = the inverse CDF of weights[b]
+ * at v_select[b] (the next drafter, drawn from the weights).
+ *
+ * cum_regret, weights  [B][N] float64 in/out, caller-owned learner state
+ *                      (initialise to 0 and 1/N)
+ * loss [B][N] float32; has_loss [B] uint8 or NULL; loss_scale finite >= 0
+ * (1/K maps the length loss in [0, K] onto [0, 1]); v_select [B] float32 or
+ * NULL; sel_out [B] int32 (required when v_select is given).
+ */
+int hedge_update(double* cum_regret, double* weights,
+                 const float* loss, const uint8_t* has_loss, float loss_scale,
+                 const float* v_select, int32_t* sel_out,
+                 int B, int N, spec_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */
