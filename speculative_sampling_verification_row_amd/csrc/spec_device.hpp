@@ -1,0 +1,173 @@
+// Device building blocks for full-vocabulary speculative-sampling verification
+// on gfx950 (CDNA4, wave64).
+//
+// Rows are bf16 logits streamed with 128-bit loads: a workgroup of kThreads
+// lanes covers a tile of kTile = kThreads * 8 consecutive tokens per load
+// instruction, lane t of the tile owning tokens [8t, 8t + 8).  Wave w's share of
+// a tile is a "sub-tile" of 512 consecutive tokens, so tile order, then wave,
+// then lane, then element is ascending token order -- the order of every
+// cumulative sum used by the inverse-CDF draws.
+//
+// Softmax statistics are kept in base 2.  Each lane carries an integer-valued
+// float reference k and an fp64 sum s of 2^(z*c - k), c = log2(e) / T.  When a
+// larger logit arrives, k moves up to ceil(z*c) and s is rescaled by an exact
+// power of two (ldexp), so the running reference never adds rounding error.
+// Each term is exp2 of one fused multiply-add, evaluated in fp32; sums of eight
+// terms are formed in fp32 and accumulated in fp64.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace specv {
+
+constexpr int kThreads = 256;             // lanes per workgroup
+constexpr int kWaves = kThreads / 64;     // wave64
+constexpr int kVec = 8;                   // bf16 per 16-byte load
+constexpr int kTile = kThreads * kVec;    // tokens per tile
+constexpr int kSub = 64 * kVec;           // tokens per wave sub-tile
+constexpr int kUnroll = 4;                // tiles in flight per row
+constexpr int kMaxV = 1 << 20;
+constexpr int kMaxSub = kMaxV / kSub;     // sub-tiles per row at most
+constexpr float kNoRef = -1.0e30f;        // initial reference: "no finite logit seen"
+
+struct RowAcc {
+  float k;   // integer-valued reference exponent (base 2)
+  double s;  // sum of 2^(z*c - k)
+};
+
+__device__ __forceinline__ RowAcc row_acc_init() { return RowAcc{kNoRef, 0.0}; }
+
+// Eight bf16 (one 16-byte chunk) -> fp32, ascending token order.  Tokens at or
+// beyond `valid` (< 8 only in a row's last chunk) become -inf.
+__device__ __forceinline__ void unpack8(const uint4 v, float z[8], int valid) {
+  z[0] = __uint_as_float(v.x << 16);
+  z[1] = __uint_as_float(v.x & 0xffff0000u);
+  z[2] = __uint_as_float(v.y << 16);
+  z[3] = __uint_as_float(v.y & 0xffff0000u);
+  z[4] = __uint_as_float(v.z << 16);
+  z[5] = __uint_as_float(v.z & 0xffff0000u);
+  z[6] = __uint_as_float(v.w << 16);
+  z[7] = __uint_as_float(v.w & 0xffff0000u);
+  if (valid < 8) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (e >= valid) z[e] = -__builtin_inff();
+  }
+}
+
+__device__ __forceinline__ float bf16_at(const uint16_t* row, int idx) {
+  return __uint_as_float(static_cast<uint32_t>(row[idx]) << 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Fold eight logits into a lane accumulator.
+__device__ __forceinline__ void row_acc_add8(RowAcc& a, const float z[8], float c) {
+  const float gm = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+  const float kn = fmaxf(a.k, ceilf(gm * c));
+  a.s = ldexp(a.s, static_cast<int>(fmaxf(a.k - kn, -2000.0f)));
+  a.k = kn;
+  float e[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) e[i] = fast_exp2(fmaf(z[i], c, -kn));
+  a.s += static_cast<double>(((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7])));
+}
+
+// ---------------------------------------------------------------------------
+// Wave / workgroup reductions
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes (ascending lane order).
+__device__ __forceinline__ double wave_incl_scan(double v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const double o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+struct RowStats {
+  float k;       // row reference (max over lanes), integer-valued
+  double s;      // sum of 2^(z*c - k) over the row
+};
+
+// Combine the lanes' accumulators of one row into the row's (k, s).
+// Every lane of the workgroup must call it; `scratch` holds 2 * kWaves doubles.
+__device__ __forceinline__ RowStats block_row_stats(const RowAcc a, double* scratch) {
+  float km = wave_max(a.k);
+  float* kf = reinterpret_cast<float*>(scratch);
+  if (lane_id() == 0) kf[wave_id()] = km;
+  __syncthreads();
+  km = kf[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) km = fmaxf(km, kf[w]);
+  __syncthreads();
+  double s = ldexp(a.s, static_cast<int>(fmaxf(a.k - km, -2000.0f)));
+  s = wave_sum(s);
+  if (lane_id() == 0) scratch[wave_id()] = s;
+  __syncthreads();
+  double tot = 0.0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) tot += scratch[w];
+  __syncthreads();
+  return RowStats{km, tot};
+}
+
+// fp64 probability of one token of a row: 2^(z*c - k) / s (z*c is exact in fp64).
+__device__ __forceinline__ double token_prob(float z, float c, const RowStats& st) {
+  return exp2(static_cast<double>(z) * static_cast<double>(c) - static_cast<double>(st.k)) / st.s;
+}
+
+// XCD-aware mapping: the dispatcher hands workgroup x to XCD x % 8.  Give each
+// XCD a contiguous block of logical jobs so that jobs that share rows (the N
+// drafters of one position share its target row) run under one L2.
+__device__ __forceinline__ int logical_job(int x, int G) {
+  const int per = G / 8, rem = G % 8;
+  const int xcd = x % 8, q = x / 8;
+  return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + q;
+}
+
+// Agent-scope atomics for the cross-workgroup completion protocol.
+__device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_agent(uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent_i(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_agent_i(int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent_d(double* p, double v) {
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), __double_as_longlong(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double ld_agent_d(double* p) {
+  return __longlong_as_double(static_cast<long long>(
+      __hip_atomic_load(reinterpret_cast<unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+}
+__device__ __forceinline__ uint32_t ticket(uint32_t* p) {
+  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace specv

@@ -1,0 +1,156 @@
+"""The C ABI library loads and exports every function include/spec_verify.h declares;
+argument validation returns the documented status codes before any launch.
+
+Runs without a GPU: only host-side calls are made (status strings, workspace
+sizes, and calls whose arguments are rejected before anything is launched).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+LIB = os.path.join(ROOT, "speculative_sampling_verification_row_amd", "libspecverify.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(\w+)\s*\(", text, flags=re.M)) - {"defined"})
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libspecverify.so is not built (run __graft_entry__.build())")
+    from speculative_sampling_verification_row_amd import binding
+    return binding.load(LIB)
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["spec_verify", "spec_cactus_verify", "spec_counterfactual_gamma", "hedge_update",
+              "spec_workspace_bytes", "spec_workspace_init", "spec_status_str"]:
+        assert n in names, names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in [0, -1, -2, -3, -4, -5, -6]:
+        assert lib.spec_status_str(code)
+    assert lib.spec_status_str(0) == b"ok"
+
+
+def test_workspace_bytes_layout(lib):
+    assert lib.spec_workspace_bytes(0, 5, 1) == 0
+    a = lib.spec_workspace_bytes(64, 5, 1)
+    b = lib.spec_workspace_bytes(64, 8, 21)
+    assert a % 256 == 0 and b % 256 == 0 and b > a
+    # tickets + states + candidates + estimator scratch
+    assert a >= 4 * 64 + 2 * 4 * 64 * 6
+    assert b >= 2 * 8 * 64 * 8 * 21
+
+
+P = ctypes.c_void_p
+
+
+def fake(addr):
+    return P(addr)
+
+
+def verify_args(**kw):
+    a = dict(target=fake(4096), ts=128, draft=fake(8192), ds=128, tok=fake(256), r=fake(512), u=fake(768),
+             B=2, K=3, V=100, T=1.0, A=fake(1024), o=fake(1280), m=None, ws=fake(1 << 20), wsb=16,
+             stream=None)
+    # wsb=16 is always too small, so even a call whose other arguments are all valid is
+    # rejected (SPEC_ERR_WORKSPACE) before anything could be launched on these fake pointers.
+    a.update(kw)
+    return a
+
+
+def call_verify(lib, a):
+    return lib.spec_verify(a["target"], a["ts"], a["draft"], a["ds"], a["tok"], a["r"], a["u"], a["B"], a["K"],
+                           a["V"], a["T"], a["A"], a["o"], a["m"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), -2), (dict(K=0), -2), (dict(K=65), -2), (dict(V=0), -2), (dict(V=(1 << 20) + 1), -2),
+    (dict(T=0.0), -3), (dict(T=-1.0), -3), (dict(T=float("inf")), -3), (dict(T=float("nan")), -3),
+    (dict(target=None), -1), (dict(draft=None), -1), (dict(tok=None), -1), (dict(A=None), -1),
+    (dict(ts=99), -2), (dict(ts=100), -2), (dict(ds=50), -2),
+    (dict(target=fake(4098)), -4), (dict(draft=fake(8200)), -4),
+    (dict(ws=None), -5), (dict(ws=fake((1 << 20) + 8)), -5), (dict(), -5),
+])
+def test_verify_validation(lib, kw, code):
+    assert call_verify(lib, verify_args(**kw)) == code
+
+
+def test_cactus_validation(lib):
+    a = verify_args()
+    args = [a["target"], a["ts"], a["draft"], a["ds"], a["tok"], a["r"], a["u"], a["B"], a["K"], a["V"]]
+    tail = [a["A"], a["o"], None, None, a["ws"], a["wsb"], None]
+    assert lib.spec_cactus_verify(*args, -0.5, 1.0, *tail) == -3
+    assert lib.spec_cactus_verify(*args, float("nan"), 1.0, *tail) == -3
+    assert lib.spec_cactus_verify(*args, 0.5, 0.0, *tail) == -3
+
+
+def test_gamma_validation(lib):
+    def call(**kw):
+        a = dict(t=fake(4096), ts=128, tr=3, d=fake(8192), ds=128, dstr=128 * 6, traj=fake(256), B=2, K=3,
+                 N=4, V=100, T=1.0, g=fake(512), e=fake(768), l=fake(1024), sel=None, tok=None, r=None,
+                 u=None, A=None, o=None, m=None, ws=fake(1 << 20), wsb=64)  # wsb too small: never launches
+        a.update(kw)
+        return lib.spec_counterfactual_gamma(a["t"], a["ts"], a["tr"], a["d"], a["ds"], a["dstr"], a["traj"],
+                                             a["B"], a["K"], a["N"], a["V"], a["T"], a["g"], a["e"], a["l"],
+                                             a["sel"], a["tok"], a["r"], a["u"], a["A"], a["o"], a["m"], a["ws"],
+                                             a["wsb"], None)
+    assert call(N=0) == -2 and call(N=65) == -2
+    assert call(tr=2) == -2                       # fewer target rows than K
+    assert call(sel=fake(64), tok=fake(64), r=fake(64), u=fake(64), A=fake(64), o=fake(64)) == -2  # fused needs K+1
+    assert call(sel=fake(64)) == -1               # fused without its buffers
+    assert call(dstr=130) == -2 and call(dstr=0) == -2
+    assert call(g=None) == -1 and call(traj=None) == -1
+    assert call(wsb=64) == -5
+
+
+def test_hedge_validation(lib):
+    ok = [fake(4096), fake(8192), fake(1024), None, 0.2, None, None, 4, 7, None]  # never called as is
+    bad_n = list(ok)
+    bad_n[8] = 65
+    assert lib.hedge_update(*bad_n) == -2
+    bad_scale = list(ok)
+    bad_scale[4] = float("nan")
+    assert lib.hedge_update(*bad_scale) == -3
+    no_sel = list(ok)
+    no_sel[5] = fake(64)
+    assert lib.hedge_update(*no_sel) == -1
+    no_state = list(ok)
+    no_state[0] = None
+    assert lib.hedge_update(*no_state) == -1
+
+
+def test_product_path_refuses_without_library(tmp_path):
+    from speculative_sampling_verification_row_amd import binding
+    saved = binding._lib
+    binding._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="not built"):
+            binding.load(str(tmp_path / "missing.so"))
+    finally:
+        binding._lib = saved
+
+
+def test_package_imports_no_oracle():
+    import subprocess
+    import sys
+    code = ("import sys; import speculative_sampling_verification_row_amd as p; "
+            "from speculative_sampling_verification_row_amd import binding, inputs, hedge; "
+            "assert not any(m == 'oracle' or m.startswith('oracle.') for m in sys.modules), 'oracle imported'")
+    subprocess.run([sys.executable, "-c", code], check=True, cwd=ROOT)

@@ -1,0 +1,243 @@
+"""GPU parity: spec_verify and spec_cactus_verify against the float64 oracle.
+
+Every case feeds the same seeded bf16 rows, tokens and uniforms to the HIP path
+(through the C ABI) and to the oracle, and compares element by element under
+the rules of tests/parity.py.
+"""
+
+import numpy as np
+import pytest
+from scipy import stats
+
+import oracle
+from speculative_sampling_verification_row_amd import inputs as gen
+
+from gpu_util import banner, bf16_bits_from_f64, dev_bf16, dev_f32, dev_i32
+from parity import assert_rel, compare_verify, to_np
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from speculative_sampling_verification_row_amd import binding
+    binding.load()
+    return binding
+
+
+def run_verify(binding, x, T=1.0, delta=None, ws=None):
+    t, d = dev_bf16(x["target"]), dev_bf16(x["draft"])
+    tok, r, u = dev_i32(x["draft_tokens"]), dev_f32(x["r"]), dev_f32(x["u"])
+    if delta is None:
+        A, o, m = binding.spec_verify(t, d, tok, r, u, T, workspace=ws)
+        torch.cuda.synchronize()
+        return to_np(A), to_np(o), to_np(m), None
+    A, o, m, g = binding.spec_cactus_verify(t, d, tok, r, u, delta, T, workspace=ws)
+    torch.cuda.synchronize()
+    return to_np(A), to_np(o), to_np(m), to_np(g)
+
+
+def oracle_verify(x, T=1.0, delta=None):
+    if delta is None:
+        return oracle.spec_verify(x["target"], x["draft"], x["draft_tokens"], x["r"], x["u"], T)
+    return oracle.spec_cactus_verify(x["target"], x["draft"], x["draft_tokens"], x["r"], x["u"], delta, T)
+
+
+def sps_case(B_, K, V, seed=0, T=1.0, sigma_t=2.5, sigma_d=0.8, peak=0.01):
+    w = gen.SpsWorkload("test", B=B_, K=K, V=V, target_sigma=sigma_t, draft_sigma=sigma_d, peak_frac=peak,
+                        temperature=T, config_id=90)
+    return gen.make_sps_inputs(w, seed=seed)
+
+
+def worked_example_rows(Bn, seed):
+    """bf16(log p), bf16(log q) of the tutorial's cat/dog/fish example, K = 1."""
+    p = np.array([0.6, 0.3, 0.1])
+    q = np.array([0.4, 0.5, 0.1])
+    tb = bf16_bits_from_f64(np.log(p))
+    db = bf16_bits_from_f64(np.log(q))
+    pt = oracle.softmax_t(oracle.widen_bf16(tb), 1.0)
+    pd = oracle.softmax_t(oracle.widen_bf16(db), 1.0)
+    rng = np.random.default_rng(seed)
+    return {
+        "target": np.broadcast_to(tb, (Bn, 2, 3)).copy(),
+        "draft": np.broadcast_to(db, (Bn, 1, 3)).copy(),
+        "draft_tokens": rng.choice(3, size=(Bn, 1), p=pd).astype(np.int32),
+        "r": rng.random((Bn, 1), dtype=np.float32),
+        "u": rng.random((Bn, 2), dtype=np.float32),
+    }, pt, pd
+
+
+def test_worked_example_exact(B):
+    banner("worked example V=3 B=4096 exact")
+    x, pt, pd = worked_example_rows(4096, seed=1)
+    A, o, m, _ = run_verify(B, x)
+    ref = oracle_verify(x)
+    stats_ = compare_verify(ref, A, o, m, "worked")
+    assert stats_["excluded_sequences"] == 0
+
+
+def test_worked_example_lossless_mc(B):
+    """Tutorial §5.2: the first emitted token follows the target.  One million GPU trials."""
+    banner("worked example lossless MC 1M")
+    counts = np.zeros(3)
+    for rep in range(4):
+        x, pt, pd = worked_example_rows(1 << 18, seed=100 + rep)
+        A, o, _, _ = run_verify(B, x)
+        first = np.where(A == 1, x["draft_tokens"][:, 0], o)
+        counts += np.bincount(first, minlength=3)
+    n = counts.sum()
+    assert stats.chisquare(counts, n * pt).pvalue > 1e-4, (counts / n, pt)
+    # and it is not the draft's law, nor the wrong-resample law (P(cat) = 0.52)
+    assert abs(counts[0] / n - pt[0]) < 2e-3 and abs(counts[0] / n - 0.52) > 0.05
+
+
+@pytest.mark.parametrize("V", [1, 2, 3, 7, 8, 9, 100, 511, 512, 513, 2047, 2048, 2049, 4096, 4097, 6143, 10000])
+def test_ragged_vocab(B, V):
+    banner(f"ragged V={V}")
+    K = 3
+    x = sps_case(8, K, V, seed=V)
+    A, o, m, _ = run_verify(B, x)
+    compare_verify(oracle_verify(x), A, o, m, f"V={V}")
+    assert np.all((o >= 0) & (o < V))
+
+
+def test_several_tiles(B):
+    banner("B=16 K=5 V=5000 sigma 2.5/0.8")
+    x = sps_case(16, 5, 5000, seed=3)
+    A, o, m, _ = run_verify(B, x)
+    print(compare_verify(oracle_verify(x), A, o, m, "tiles"))
+
+
+@pytest.mark.parametrize("T", [0.7, 1.6])
+def test_temperature(B, T):
+    banner(f"temperature {T}")
+    x = sps_case(16, 4, 3000, seed=5, T=T)
+    A, o, m, _ = run_verify(B, x, T=T)
+    compare_verify(oracle_verify(x, T=T), A, o, m, f"T={T}")
+
+
+def test_peaked_rows(B):
+    banner("peaked rows 50%")
+    x = sps_case(32, 5, 7000, seed=7, peak=0.5)
+    A, o, m, _ = run_verify(B, x)
+    compare_verify(oracle_verify(x), A, o, m, "peaked")
+
+
+def test_masked_logits(B):
+    """-inf logits (masked tokens): zero mass, never drawn."""
+    banner("masked logits")
+    rng = np.random.default_rng(11)
+    x = sps_case(16, 4, 3001, seed=11)
+    neg = np.uint16(0xFF80)
+    for b in range(16):
+        for k in range(5):
+            x["target"][b, k, rng.choice(3001, 800, replace=False)] = neg
+        for k in range(4):
+            x["draft"][b, k, rng.choice(3001, 800, replace=False)] = neg
+    # drafted tokens must have draft mass: redraw from the masked draft rows
+    x["draft_tokens"] = gen.sample_tokens(x["draft"], 1.0, seed=12, config_id=91)
+    A, o, m, _ = run_verify(B, x)
+    ref = oracle_verify(x)
+    compare_verify(ref, A, o, m, "masked")
+    for b in range(16):
+        a = int(A[b])
+        row = x["target"][b, a] if a == 4 else None
+        if row is not None:
+            assert row[o[b]] != neg
+
+
+def test_equal_rows_always_accept(B):
+    """Tutorial §7.2: q = p never rejects; the bonus comes from target row K."""
+    banner("equal rows")
+    x = sps_case(16, 5, 4000, seed=13)
+    x["draft"] = x["target"][:, :5].copy()
+    x["draft_tokens"] = gen.sample_tokens(x["draft"], 1.0, seed=14, config_id=92)
+    A, o, m, _ = run_verify(B, x)
+    assert np.all(A == 5) and np.all(m == 1)
+    compare_verify(oracle_verify(x), A, o, m, "equal")
+
+
+def test_disjoint_always_reject(B):
+    """Tutorial §7.3: disjoint supports reject at once; the residual is the target itself."""
+    banner("disjoint support")
+    V = 2000
+    x = sps_case(16, 3, V, seed=15)
+    neg = np.uint16(0xFF80)
+    x["target"][:, :, : V // 2] = neg
+    x["draft"][:, :, V // 2:] = neg
+    x["draft_tokens"] = gen.sample_tokens(x["draft"], 1.0, seed=16, config_id=93)
+    A, o, m, _ = run_verify(B, x)
+    assert np.all(A == 0) and np.all(m == 0) and np.all(o >= V // 2)
+    compare_verify(oracle_verify(x), A, o, m, "disjoint")
+
+
+def test_invalid_token_reports_minus_one(B):
+    banner("invalid token ids")
+    x = sps_case(4, 3, 1000, seed=17)
+    x["draft_tokens"][1, 2] = 1000
+    x["draft_tokens"][3, 0] = -5
+    A, o, m, _ = run_verify(B, x)
+    assert A[1] == -1 and o[1] == -1 and A[3] == -1 and o[3] == -1
+    assert m[1, 2] == 0 and m[3, 0] == 0
+    ref = oracle_verify({k: (v[[0, 2]] if isinstance(v, np.ndarray) else v) for k, v in x.items()})
+    compare_verify(ref, A[[0, 2]], o[[0, 2]], m[[0, 2]], "valid rows")
+
+
+def test_full_llama_vocab_config(B):
+    """The benchmarked workload: B=64, K=5, V=128256, 1% peaked rows; every sequence checked."""
+    banner("full B=64 K=5 V=128256")
+    x = gen.make_sps_inputs(gen.LLAMA_SPS)
+    A, o, m, _ = run_verify(B, x)
+    ref = oracle_verify(x)
+    print(compare_verify(ref, A, o, m, "full c2"))
+
+
+def test_repeat_deterministic_and_workspace_clean(B):
+    banner("repeat 20x, workspace returns to zero")
+    from speculative_sampling_verification_row_amd import binding
+    x = sps_case(16, 5, 9000, seed=19)
+    ws = binding.make_workspace(16, 5, 1)
+    first = run_verify(B, x, ws=ws)
+    for _ in range(19):
+        again = run_verify(B, x, ws=ws)
+        for a, b in zip(first[:3], again[:3]):
+            np.testing.assert_array_equal(a, b)
+    assert int(ws.count_nonzero()) == 0
+
+
+# ---------------------------------------------------------------------------
+# Cactus
+# ---------------------------------------------------------------------------
+
+def test_cactus_delta0_bit_identical_to_sps(B):
+    banner("cactus delta=0 == spec_verify")
+    x = sps_case(32, 6, 6000, seed=21, sigma_t=3.0, sigma_d=1.0, peak=0.0)
+    a = run_verify(B, x)
+    c = run_verify(B, x, delta=0.0)
+    for u, v in zip(a[:3], c[:3]):
+        np.testing.assert_array_equal(u, v)
+
+
+@pytest.mark.parametrize("delta", [0.0, 0.5, 1.0])
+def test_cactus_parity(B, delta):
+    banner(f"cactus delta={delta} B=16 m=20 V=4000")
+    x = sps_case(16, 20, 4000, seed=23, sigma_t=3.0, sigma_d=1.0, peak=0.0)
+    A, o, m, g = run_verify(B, x, delta=delta)
+    ref = oracle_verify(x, delta=delta)
+    compare_verify(ref, A, o, m, f"cactus {delta}")
+    valid = x["draft_tokens"] >= 0
+    assert_rel(g[valid], ref["gamma_star"][valid], label="gamma*")
+
+
+def test_cactus_full_qwen_vocab_sampled(B):
+    """Full launch B=64, m=20, V=151936 at delta=1.0; the oracle checks 8 sequences."""
+    banner("cactus full B=64 m=20 V=151936 delta=1")
+    x = gen.make_sps_inputs(gen.QWEN_CACTUS)
+    A, o, m, g = run_verify(B, x, delta=1.0)
+    pick = np.array([0, 9, 17, 25, 33, 41, 52, 63])
+    sub = {k: (v[pick] if isinstance(v, np.ndarray) else v) for k, v in x.items()}
+    ref = oracle_verify(sub, delta=1.0)
+    print(compare_verify(ref, A[pick], o[pick], m[pick], "cactus full"))
+    assert_rel(g[pick], ref["gamma_star"], label="gamma* full")
