@@ -1,0 +1,319 @@
+"""Benchmark of the verification hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama_sps]
+
+One step is one launch of the hot path over one batch of synthetic input
+already resident in HBM.  The default workload is lossless verification of
+B=64 sequences x K=5 drafts over the Llama-3.1 vocabulary (V=128256, 1% of
+target rows peaked); the other workloads (--workload) are available for
+measurement and profiling.
+
+Timing: W untimed warm-up steps, then K timed steps bracketed by device
+synchronisation; every launch is also bracketed by HIP events on the launch
+stream, whose mean is the kernel duration used for the roofline.  To keep the
+256 MB Infinity Cache from serving the inputs, steps rotate over enough
+identical copies of the inputs (>= 1 GiB in total) that each launch reads
+lines no earlier launch left in the cache.
+
+Output: one JSON line on stdout (progress goes to stderr) with the metric,
+the roofline of the dominant kernel (algorithmic bytes per launch / mean
+launch time vs the 8 TB/s HBM peak; `traffic` from the committed rocprofv3
+FETCH_SIZE/WRITE_SIZE summary when it was taken on the current kernel
+sources), and the float64 CPU oracle timed on the host cores on a bounded
+sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+KERNEL = "row_kernel"
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    csrc = os.path.join(ROOT, "speculative_sampling_verification_row_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# Workloads
+# ---------------------------------------------------------------------------
+
+class Workload:
+    key = ""
+    desc = ""
+    positions = 0          # verified draft positions per launch
+    algo_bytes = 0         # bytes the method must move per launch (every logit once + small arrays)
+
+    def setup(self, copies_min_bytes: int):
+        raise NotImplementedError
+
+    def launch(self, i: int):
+        raise NotImplementedError
+
+    def cpu_sample(self, budget_s: float):
+        """Run the oracle on a bounded sample; returns (positions, seconds, cpu_seconds, sample text)."""
+        raise NotImplementedError
+
+
+def _dev(torch, bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+class SpsLike(Workload):
+    """spec_verify (delta None) or spec_cactus_verify over one SpsWorkload."""
+
+    def __init__(self, key, w, delta=None):
+        self.key, self.w, self.delta = key, w, delta
+        B, K, V = w.B, w.K, w.V
+        self.desc = w.name + ("" if delta is None else f" delta={delta}")
+        self.positions = B * K
+        rows = B * (K + 1) + B * K
+        small = B * K * 4 * 2 + B * (K + 1) * 4 + B * 4 * 2 + B * K + (B * K * 4 if delta is not None else 0)
+        self.algo_bytes = 2 * V * rows + small
+
+    def setup(self, copies_min_bytes):
+        import torch
+        from speculative_sampling_verification_row_amd import binding
+        from speculative_sampling_verification_row_amd import inputs as gen
+        self.torch, self.binding = torch, binding
+        log(f"generating inputs: {self.desc}")
+        self.x = gen.make_sps_inputs(self.w)
+        t = _dev(torch, self.x["target"])
+        d = _dev(torch, self.x["draft"])
+        n = max(1, -(-copies_min_bytes // (2 * (t.numel() + d.numel()))))
+        self.copies = [(t, d)] + [(t.clone(), d.clone()) for _ in range(n - 1)]
+        self.tok = torch.from_numpy(self.x["draft_tokens"]).cuda()
+        self.r = torch.from_numpy(self.x["r"]).cuda()
+        self.u = torch.from_numpy(self.x["u"]).cuda()
+        self.ws = binding.make_workspace(self.w.B, self.w.K, 1)
+        log(f"{len(self.copies)} input copies of {2 * (t.numel() + d.numel()) / 1e6:.1f} MB")
+
+    def launch(self, i):
+        t, d = self.copies[i % len(self.copies)]
+        if self.delta is None:
+            self.binding.spec_verify(t, d, self.tok, self.r, self.u, self.w.temperature, workspace=self.ws)
+        else:
+            self.binding.spec_cactus_verify(t, d, self.tok, self.r, self.u, self.delta, self.w.temperature,
+                                            workspace=self.ws)
+
+    def cpu_sample(self, budget_s):
+        import oracle
+        x, B = self.x, self.w.B
+        done, pos, t0, c0 = 0, 0, time.perf_counter(), time.process_time()
+        while True:
+            b = done % B
+            sl = slice(b, b + 1)
+            if self.delta is None:
+                oracle.spec_verify(x["target"][sl], x["draft"][sl], x["draft_tokens"][sl], x["r"][sl], x["u"][sl])
+            else:
+                oracle.spec_cactus_verify(x["target"][sl], x["draft"][sl], x["draft_tokens"][sl], x["r"][sl],
+                                          x["u"][sl], self.delta)
+            done += 1
+            pos += self.w.K
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        return pos, time.perf_counter() - t0, time.process_time() - c0, f"{done} sequences of this batch, one at a time"
+
+
+class GammaLike(Workload):
+    def __init__(self, key, w):
+        self.key, self.w = key, w
+        B, K, N, V = w.B, w.K, w.N, w.V
+        self.desc = w.name
+        self.positions = B * K
+        trows = B * (K + 1) if w.fused else B * K
+        rows = trows + N * B * K
+        small = B * K * 4 + B * K * N * 4 + 2 * B * N * 4
+        if w.fused:
+            small += B * 4 + B * K * 4 * 2 + B * (K + 1) * 4 + B * 4 * 2 + B * K
+        self.algo_bytes = 2 * V * rows + small
+
+    def setup(self, copies_min_bytes):
+        import torch
+        from speculative_sampling_verification_row_amd import binding
+        from speculative_sampling_verification_row_amd import inputs as gen
+        self.torch, self.binding = torch, binding
+        log(f"generating inputs: {self.desc}")
+        self.x = gen.make_gamma_inputs(self.w)
+        t = _dev(torch, self.x["target"])
+        d = _dev(torch, self.x["drafts"])
+        per = 2 * (t.numel() + d.numel())
+        n = max(1, -(-copies_min_bytes // per))
+        self.copies = [(t, d)] + [(t.clone(), d.clone()) for _ in range(n - 1)]
+        i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+        f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+        self.traj = i32(self.x["traj"])
+        self.kw = {}
+        if self.w.fused:
+            self.kw = dict(sel=i32(self.x["sel"]), draft_tokens=i32(self.x["draft_tokens"]), r_accept=f32(self.x["r"]),
+                           u_resample=f32(self.x["u"]))
+        self.ws = binding.make_workspace(self.w.B, self.w.K, self.w.N)
+        log(f"{len(self.copies)} input copies of {per / 1e6:.1f} MB")
+
+    def launch(self, i):
+        t, d = self.copies[i % len(self.copies)]
+        self.binding.spec_counterfactual_gamma(t, d, self.traj, self.w.temperature, workspace=self.ws, **self.kw)
+
+    def cpu_sample(self, budget_s):
+        import oracle
+        x, B, K = self.x, self.w.B, self.w.K
+        done, t0, c0 = 0, time.perf_counter(), time.process_time()
+        while True:
+            b = done % B
+            oracle.spec_counterfactual_gamma(x["target"][b:b + 1, :K], x["drafts"][:, b:b + 1], x["traj"][b:b + 1])
+            if self.w.fused:
+                s = int(x["sel"][b])
+                oracle.spec_verify(x["target"][b:b + 1], x["drafts"][s, b:b + 1], x["draft_tokens"][b:b + 1],
+                                   x["r"][b:b + 1], x["u"][b:b + 1])
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        return done * K, time.perf_counter() - t0, time.process_time() - c0, f"{done} sequences of this batch, one at a time"
+
+
+def workloads():
+    from speculative_sampling_verification_row_amd import inputs as gen
+    return {
+        "llama_sps": lambda: SpsLike("llama_sps", gen.LLAMA_SPS),
+        "qwen_cactus": lambda: SpsLike("qwen_cactus", gen.QWEN_CACTUS, delta=1.0),
+        "qwen_cactus_d0": lambda: SpsLike("qwen_cactus_d0", gen.QWEN_CACTUS, delta=0.0),
+        "qwen_cactus_d05": lambda: SpsLike("qwen_cactus_d05", gen.QWEN_CACTUS, delta=0.5),
+        "hedge_eval": lambda: GammaLike("hedge_eval", gen.HEDGE_EVAL),
+        "pool21": lambda: GammaLike("pool21", gen.POOL21),
+        "small_mixed": lambda: GammaLike("small_mixed", gen.SMALL_MIXED),
+    }
+
+
+def load_traffic(key: str, per_launch_algo: int):
+    """HBM traffic per launch from the committed PMC summary, if taken on these sources."""
+    path = os.path.join(ROOT, "profiles", f"{KERNEL}_{key}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != source_hash():
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama_sps")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline (0: skip)")
+    ap.add_argument("--copies-gib", type=float, default=1.0)
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (PMC calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sequences shard across GPUs with no exchange; see the design notes).", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    from speculative_sampling_verification_row_amd import binding
+    binding.load()
+
+    wl = workloads()[args.workload]()
+    wl.setup(int(args.copies_gib * (1 << 30)))
+    torch.cuda.synchronize()
+
+    if args.copy_calib_mib > 0:
+        n = args.copy_calib_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.copy_calib_mib} MiB x 3")
+
+    for i in range(args.warmup):
+        wl.launch(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        wl.launch(args.warmup + i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ms_step = wall * 1e3 / K
+    mean_launch_s = float(per_launch_ms.mean()) * 1e-3
+    achieved = wl.algo_bytes / mean_launch_s / 1e9
+    log(f"launch ms: mean {per_launch_ms.mean():.4f} median {np.median(per_launch_ms):.4f} "
+        f"p10 {np.percentile(per_launch_ms, 10):.4f} p90 {np.percentile(per_launch_ms, 90):.4f}; "
+        f"wall/step {ms_step:.4f} ms; {achieved:.0f} GB/s algorithmic")
+
+    traffic = load_traffic(wl.key, wl.algo_bytes)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        log(f"oracle CPU baseline, ~{args.cpu_seconds:.0f} s")
+        pos, secs, cpu_secs, sample = wl.cpu_sample(args.cpu_seconds)
+        cores = max(1, int(round(cpu_secs / secs)))
+        cpu = {"value": pos / secs, "unit": "positions/s", "cores": cores, "kind": "oracle",
+               "sample": f"{sample} ({pos} positions in {secs:.1f} s, float64 numpy)"}
+
+    out = {
+        "metric": "verified draft positions/sec at V=128k-152k",
+        "value": wl.positions / (ms_step * 1e-3),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.desc, "positions_per_step": wl.positions,
+                   "algorithmic_bytes_per_step": wl.algo_bytes},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": KERNEL, "mean_launch_ms": mean_launch_s * 1e3},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
