@@ -15,8 +15,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * Memory.  Every array pointer is a DEVICE pointer owned by the caller.  The
- *   library allocates nothing, keeps no pointer after a call returns and has no
- *   global state; the only memory it writes besides the outputs is the caller's
+ *   library allocates nothing and keeps no pointer after a call returns; its
+ *   only memory between calls is a per-device cache of the resident-workgroup
+ *   count.  The only memory it writes besides the outputs is the caller's
  *   workspace.
  * Streams.  Calls enqueue kernels on `stream` and return at once.  A non-zero
  *   return means nothing was launched (argument error) or the launch itself
@@ -33,11 +34,13 @@
  *   shaping is folded into both distributions before any ratio is formed).
  * Uniforms.  r and u are float32 in [0, 1), drawn by the caller: the library
  *   draws no random numbers.
- * Workspace.  `workspace` holds per-call ticket counters and per-position
- *   scratch.  Size it with spec_workspace_bytes() and zero it once with
- *   spec_workspace_init() (or any zero fill) before first use; every completed
- *   call leaves it zeroed again, so no per-call clearing is needed.  Calls
- *   that run concurrently must use different workspaces.
+ * Workspace.  `workspace` holds completion counters and per-call scratch.
+ *   Size it with spec_workspace_bytes(B, K, N) (enough for any V up to
+ *   SPEC_MAX_V) and zero it with spec_workspace_init() (or any zero fill)
+ *   before its first use and again whenever it is reused with a different B
+ *   or K.  Every completed call leaves the counters at zero, so back-to-back
+ *   calls of one (B, K) need no clearing.  Calls that run concurrently must
+ *   use different workspaces.
  * Bad token ids.  A drafted or trajectory token outside [0, V) is reported in
  *   the outputs (see each call), never by a fault.
  */
@@ -66,6 +69,7 @@ enum {
 };
 
 /* Limits checked by every call. */
+#define SPEC_MAX_B 65536       /* sequences per call */
 #define SPEC_MAX_V (1 << 20)   /* vocabulary size */
 #define SPEC_MAX_K 64          /* draft positions per sequence */
 #define SPEC_MAX_N 64          /* drafters */
@@ -76,6 +80,14 @@ const char* spec_status_str(int status);
 /* Bytes of workspace one call with these B, K, N needs (N = 1 for the
  * verify calls).  256-byte aligned layout; pass the same B, K, N. */
 size_t spec_workspace_bytes(int B, int K, int N);
+
+/* Leading bytes of a (B, K) workspace that hold its counters and queue: they
+ * must be zero when a call starts and every completed call leaves them zero.
+ * They depend on B and K only; the rest of the workspace is scratch that each
+ * call overwrites before reading.  Word 3 (bytes 12..15) is a fault flag that
+ * a call sets to non-zero if an internal consistency check fails (its outputs
+ * are then unspecified and the workspace must be re-initialised). */
+size_t spec_workspace_counter_bytes(int B, int K);
 
 /* Zero `bytes` of workspace on `stream` with a fill kernel (no memset node). */
 int spec_workspace_init(void* workspace, size_t bytes, spec_stream_t stream);
@@ -107,7 +119,8 @@ int spec_workspace_init(void* workspace, size_t bytes, spec_stream_t stream);
  * accept_mask   [B][K] uint8 out or NULL: each position's own test (1 accept),
  *               evaluated at every position, including after the first
  *               rejection; 0 for an invalid id
- * Limits: 1 <= B, 1 <= K <= SPEC_MAX_K, 1 <= V <= SPEC_MAX_V, T > 0 finite.
+ * Limits: 1 <= B <= SPEC_MAX_B, 1 <= K <= SPEC_MAX_K, 1 <= V <= SPEC_MAX_V,
+ * T > 0 finite.
  */
 int spec_verify(const spec_bf16* target, int64_t target_row_stride,
                 const spec_bf16* draft, int64_t draft_row_stride,

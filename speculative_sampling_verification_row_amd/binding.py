@@ -20,7 +20,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+# SPECVERIFY_LIB selects another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("SPECVERIFY_LIB") or os.path.join(_HERE, "libspecverify.so")
 
 SPEC_OK = 0
 STATUS = {0: "SPEC_OK", -1: "SPEC_ERR_NULL", -2: "SPEC_ERR_SHAPE", -3: "SPEC_ERR_PARAM",
@@ -37,6 +38,7 @@ _SZ = ctypes.c_size_t
 _SIGNATURES = {
     "spec_status_str": (ctypes.c_char_p, [_I]),
     "spec_workspace_bytes": (_SZ, [_I, _I, _I]),
+    "spec_workspace_counter_bytes": (_SZ, [_I, _I]),
     "spec_workspace_init": (_I, [_P, _SZ, _P]),
     "spec_verify": (_I, [_P, _I64, _P, _I64, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P]),
     "spec_cactus_verify": (_I, [_P, _I64, _P, _I64, _P, _P, _P, _I, _I, _I, _F, _F, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -123,8 +125,13 @@ def workspace_bytes(B: int, K: int, N: int = 1) -> int:
 
 
 def make_workspace(B: int, K: int, N: int = 1, device="cuda") -> torch.Tensor:
-    """A zeroed workspace (calls leave it zeroed again)."""
+    """A zeroed workspace (calls leave its counters zero; re-zero it for another B or K)."""
     return torch.zeros(workspace_bytes(B, K, N), dtype=torch.uint8, device=device)
+
+
+def workspace_fault(ws: torch.Tensor) -> int:
+    """The workspace's fault word (0 = no internal check failed); synchronises."""
+    return int(ws[12:16].view(torch.int32).item())
 
 
 def workspace_init(ws: torch.Tensor, stream=None) -> None:

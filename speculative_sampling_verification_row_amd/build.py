@@ -35,17 +35,17 @@ def common_flags() -> list:
             "-I", INCLUDE, "-I", CSRC]
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     """Compile every source into one shared library; returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + common_flags() + ["-shared"] + SOURCES + ["-o", tmp]
+    tmp = out + ".tmp"
+    cmd = [hipcc()] + common_flags() + [f"-D{d}" for d in defines] + ["-shared"] + SOURCES + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 def dump_asm(out_dir: str) -> None:

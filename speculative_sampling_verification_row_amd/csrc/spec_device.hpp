@@ -145,7 +145,15 @@ __device__ __forceinline__ int logical_job(int x, int G) {
   return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + q;
 }
 
-// Agent-scope atomics for the cross-workgroup completion protocol.
+// Cross-workgroup protocol.  Every value one workgroup hands to another is
+// written and read with device-scope atomic stores / loads, which the hardware
+// keeps coherent across the XCDs' L2 caches without any cache maintenance.  A
+// producer waits until its own stores have completed (vmcnt counts stores on
+// gfx9, and a device-scope store completes once it is visible device-wide),
+// passes a workgroup barrier, then bumps a completion counter with a relaxed
+// atomic; a consumer polls that counter with device-scope loads.  No
+// agent-scope fence is used: on this target it writes back and invalidates the
+// whole L2, which costs far more than the data it protects.
 __device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -166,8 +174,19 @@ __device__ __forceinline__ double ld_agent_d(double* p) {
   return __longlong_as_double(static_cast<long long>(
       __hip_atomic_load(reinterpret_cast<unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
 }
-__device__ __forceinline__ uint32_t ticket(uint32_t* p) {
-  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void st_agent_u64(unsigned long long* p, unsigned long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ unsigned long long ld_agent_u64(unsigned long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ticket(uint32_t* p) {
+  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ticket_n(uint32_t* p, uint32_t n) {
+  return __hip_atomic_fetch_add(p, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this wave issued has completed.
+__device__ __forceinline__ void stores_complete() { __builtin_amdgcn_s_waitcnt(0); }
 
 }  // namespace specv

@@ -27,9 +27,12 @@ def run_gamma(binding, x, fused=False, T=1.0):
     if fused:
         kw = dict(sel=dev_i32(x["sel"]), draft_tokens=dev_i32(x["draft_tokens"]), r_accept=dev_f32(x["r"]),
                   u_resample=dev_f32(x["u"]))
+    N, B_, K = x["drafts"].shape[:3]
+    ws = binding.make_workspace(B_, K, N)
     out = binding.spec_counterfactual_gamma(dev_bf16(x["target"]), dev_bf16(x["drafts"]), dev_i32(x["traj"]), T,
-                                            **kw)
+                                            workspace=ws, **kw)
     torch.cuda.synchronize()
+    assert binding.workspace_fault(ws) == 0, "kernel reported an internal consistency fault"
     return {k: to_np(v) for k, v in out.items()}
 
 
