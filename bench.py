@@ -39,7 +39,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-KERNEL = "row_kernel"
+KERNEL = "flow_kernel"
 
 
 def log(msg: str) -> None:
@@ -220,6 +220,38 @@ def load_traffic(key: str, per_launch_algo: int):
     return d.get("traffic_bytes_per_launch")
 
 
+def summarize_pmc(key: str, fetch_csv: str, write_csv: str, calib_mib: int, command: str) -> dict:
+    """Per-launch HBM traffic of KERNEL from two rocprofv3 --pmc counter_collection CSVs
+    (FETCH_SIZE, WRITE_SIZE, both KiB per dispatch).  Each counter is scaled by what it reads
+    for the plain device copy of `calib_mib` MiB that the same run made (--copy-calib-mib)."""
+    import csv
+
+    def per_kernel(path, counter):
+        mine, calib = [], []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            if r["Kernel_Name"].startswith(f"specv::{KERNEL}("):
+                mine.append(v)
+            elif "copyBuffer" in r["Kernel_Name"] and v > 0.4 * calib_mib * 1024:
+                calib.append(v)
+        if not mine or not calib:
+            raise SystemExit(f"{path}: no {KERNEL} dispatches or no calibration copy for {counter}")
+        return float(np.mean(mine)), float(np.mean(calib[-3:])), len(mine)
+
+    f_k, f_c, nf = per_kernel(fetch_csv, "FETCH_SIZE")
+    w_k, w_c, nw = per_kernel(write_csv, "WRITE_SIZE")
+    expect = calib_mib * 1024.0
+    f_scale, w_scale = expect / f_c, expect / w_c
+    traffic = (f_k * f_scale + w_k * w_scale) * 1024.0
+    return {"kernel": KERNEL, "workload": key, "source_hash": source_hash(),
+            "fetch_kib_raw": f_k, "write_kib_raw": w_k, "dispatches": [nf, nw],
+            "calib_copy_mib": calib_mib, "calib_fetch_kib_raw": f_c, "calib_write_kib_raw": w_c,
+            "fetch_scale": f_scale, "write_scale": w_scale,
+            "traffic_bytes_per_launch": traffic, "command": command}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -230,7 +262,20 @@ def main(argv=None):
     ap.add_argument("--copies-gib", type=float, default=1.0)
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (PMC calibration)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/<kernel>_<workload>_pmc.json from two rocprofv3 --pmc "
+                         "counter_collection CSVs of this script run with --copy-calib-mib, then exit")
+    ap.add_argument("--pmc-command", default="", help="the rocprofv3 command recorded in the summary")
     args = ap.parse_args(argv)
+
+    if args.pmc_summary:
+        d = summarize_pmc(args.workload, *args.pmc_summary, args.copy_calib_mib or 256, args.pmc_command)
+        path = os.path.join(ROOT, "profiles", f"{KERNEL}_{args.workload}_pmc.json")
+        with open(path, "w") as f:
+            json.dump(d, f, indent=1)
+            f.write("\n")
+        print(json.dumps(d, indent=1))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
