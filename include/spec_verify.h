@@ -29,18 +29,22 @@
  *   multiple of 8 the elements of a row from V up to the next multiple of 8 are
  *   read and ignored, so each row's storage must extend that far.  Logits must
  *   be finite or -inf, with at least one finite logit per row and
- *   |logit| / T < 1e30; anything else gives unspecified (but in-bounds) results.
+ *   |logit| / T < 6e8; anything else gives unspecified (but in-bounds) results.
  * Temperature.  One T > 0 scales every row, target and draft alike ([LT] §8 Q4:
  *   shaping is folded into both distributions before any ratio is formed).
  * Uniforms.  r and u are float32 in [0, 1), drawn by the caller: the library
  *   draws no random numbers.
- * Workspace.  `workspace` holds completion counters and per-call scratch.
- *   Size it with spec_workspace_bytes(B, K, N) (enough for any V up to
- *   SPEC_MAX_V) and zero it with spec_workspace_init() (or any zero fill)
- *   before its first use and again whenever it is reused with a different B
- *   or K.  Every completed call leaves the counters at zero, so back-to-back
- *   calls of one (B, K) need no clearing.  Calls that run concurrently must
- *   use different workspaces.
+ * Workspace.  `workspace` holds the values the kernel's workgroups hand to
+ *   one another.  Size it with spec_workspace_bytes(B, K, N) (enough for any V
+ *   up to SPEC_MAX_V) and zero it with spec_workspace_init() (or any zero fill)
+ *   before its first use.  Every completed call leaves it all zero again, so
+ *   back-to-back calls need no clearing, whatever their shapes, as long as
+ *   each fits.  The 32-bit word at byte offset 12 is a fault word: a call sets
+ *   it non-zero when a wait between its workgroups times out (after 2 s; this
+ *   needs the device to be shared with work that keeps part of the grid from
+ *   running, or a workspace that was not zero at launch).  The outputs of that
+ *   call are then unspecified and the workspace must be zeroed again.  Calls
+ *   that run concurrently must use different workspaces.
  * Bad token ids.  A drafted or trajectory token outside [0, V) is reported in
  *   the outputs (see each call), never by a fault.
  */
@@ -78,16 +82,9 @@ enum {
 const char* spec_status_str(int status);
 
 /* Bytes of workspace one call with these B, K, N needs (N = 1 for the
- * verify calls).  256-byte aligned layout; pass the same B, K, N. */
+ * verify calls), for any V up to SPEC_MAX_V; 0 when B, K or N is out of range.
+ * A workspace must be 256-byte aligned. */
 size_t spec_workspace_bytes(int B, int K, int N);
-
-/* Leading bytes of a (B, K) workspace that hold its counters and queue: they
- * must be zero when a call starts and every completed call leaves them zero.
- * They depend on B and K only; the rest of the workspace is scratch that each
- * call overwrites before reading.  Word 3 (bytes 12..15) is a fault flag that
- * a call sets to non-zero if an internal consistency check fails (its outputs
- * are then unspecified and the workspace must be re-initialised). */
-size_t spec_workspace_counter_bytes(int B, int K);
 
 /* Zero `bytes` of workspace on `stream` with a fill kernel (no memset node). */
 int spec_workspace_init(void* workspace, size_t bytes, spec_stream_t stream);

@@ -38,7 +38,6 @@ _SZ = ctypes.c_size_t
 _SIGNATURES = {
     "spec_status_str": (ctypes.c_char_p, [_I]),
     "spec_workspace_bytes": (_SZ, [_I, _I, _I]),
-    "spec_workspace_counter_bytes": (_SZ, [_I, _I]),
     "spec_workspace_init": (_I, [_P, _SZ, _P]),
     "spec_verify": (_I, [_P, _I64, _P, _I64, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P]),
     "spec_cactus_verify": (_I, [_P, _I64, _P, _I64, _P, _P, _P, _I, _I, _I, _F, _F, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -125,12 +124,12 @@ def workspace_bytes(B: int, K: int, N: int = 1) -> int:
 
 
 def make_workspace(B: int, K: int, N: int = 1, device="cuda") -> torch.Tensor:
-    """A zeroed workspace (calls leave its counters zero; re-zero it for another B or K)."""
+    """A zeroed workspace; every completed call leaves it zero again."""
     return torch.zeros(workspace_bytes(B, K, N), dtype=torch.uint8, device=device)
 
 
 def workspace_fault(ws: torch.Tensor) -> int:
-    """The workspace's fault word (0 = no internal check failed); synchronises."""
+    """The workspace's fault word (0 = no wait between workgroups timed out); synchronises."""
     return int(ws[12:16].view(torch.int32).item())
 
 
@@ -138,25 +137,59 @@ def workspace_init(ws: torch.Tensor, stream=None) -> None:
     _check("spec_workspace_init", load().spec_workspace_init(_ptr(ws), ws.numel(), _stream(stream)))
 
 
+class Launcher:
+    """One call with its tensors fixed: launch() only enqueues the kernel -- no
+    allocation and no checks beyond the C ABI's own -- and returns the outputs
+    (overwritten by every launch).  It keeps every tensor it points to alive."""
+
+    def __init__(self, name: str, args: tuple, outputs, keep: tuple):
+        self.name = name
+        self._fn = getattr(load(), name)
+        self._args = args
+        self.outputs = outputs
+        self._keep = keep
+
+    def launch(self, stream=None):
+        st = self._fn(*self._args, _stream(stream))
+        if st != SPEC_OK:
+            raise SpecError(self.name, st)
+        return self.outputs
+
+
 def spec_verify(target, draft, draft_tokens, r_accept, u_resample, temperature: float = 1.0, *,
                 workspace: Optional[torch.Tensor] = None, with_mask: bool = True, stream=None):
     """Lossless verification.  target [B, K+1, V], draft [B, K, V] bf16; draft_tokens [B, K]
     int32; r_accept [B, K], u_resample [B, K+1] float32.  Returns (accepted_len [B],
     out_token [B], accept_mask [B, K] or None)."""
-    return _verify("spec_verify", target, draft, draft_tokens, r_accept, u_resample, None, temperature,
-                   workspace, with_mask, False, stream)
+    return prepare_verify(target, draft, draft_tokens, r_accept, u_resample, temperature, workspace=workspace,
+                          with_mask=with_mask).launch(stream)
 
 
 def spec_cactus_verify(verifier, draft, draft_tokens, r_accept, u_resample, delta: float,
                        temperature: float = 1.0, *, workspace=None, with_mask: bool = True,
                        with_gamma_star: bool = True, stream=None):
     """Cactus verification; returns (accepted_len, out_token, accept_mask, gamma_star)."""
-    return _verify("spec_cactus_verify", verifier, draft, draft_tokens, r_accept, u_resample, delta,
-                   temperature, workspace, with_mask, with_gamma_star, stream)
+    return prepare_cactus_verify(verifier, draft, draft_tokens, r_accept, u_resample, delta, temperature,
+                                 workspace=workspace, with_mask=with_mask,
+                                 with_gamma_star=with_gamma_star).launch(stream)
 
 
-def _verify(name, target, draft, tokens, r, u, delta, temperature, workspace, with_mask, with_gstar, stream):
-    lib = load()
+def prepare_verify(target, draft, draft_tokens, r_accept, u_resample, temperature: float = 1.0, *,
+                   workspace: Optional[torch.Tensor] = None, with_mask: bool = True) -> Launcher:
+    """spec_verify with its tensors fixed (see Launcher)."""
+    return _prepare_verify("spec_verify", target, draft, draft_tokens, r_accept, u_resample, None, temperature,
+                           workspace, with_mask, False)
+
+
+def prepare_cactus_verify(verifier, draft, draft_tokens, r_accept, u_resample, delta: float,
+                          temperature: float = 1.0, *, workspace=None, with_mask: bool = True,
+                          with_gamma_star: bool = True) -> Launcher:
+    """spec_cactus_verify with its tensors fixed (see Launcher)."""
+    return _prepare_verify("spec_cactus_verify", verifier, draft, draft_tokens, r_accept, u_resample, delta,
+                           temperature, workspace, with_mask, with_gamma_star)
+
+
+def _prepare_verify(name, target, draft, tokens, r, u, delta, temperature, workspace, with_mask, with_gstar):
     _need_cuda(target, draft, tokens, r, u)
     B, K1, V = target.shape
     K = K1 - 1
@@ -172,17 +205,15 @@ def _verify(name, target, draft, tokens, r, u, delta, temperature, workspace, wi
     tok = torch.empty(B, dtype=torch.int32, device=dev)
     mask = torch.empty((B, K), dtype=torch.uint8, device=dev) if with_mask else None
     ws = make_workspace(B, K, 1, dev) if workspace is None else workspace
+    keep = (t, d, tokens, r, u, A, tok, mask, ws)
     if name == "spec_verify":
-        st = lib.spec_verify(_ptr(t), ts, _ptr(d), ds, _ptr(tokens), _ptr(r), _ptr(u), B, K, V, float(temperature),
-                             _ptr(A), _ptr(tok), _ptr(mask), _ptr(ws), ws.numel(), _stream(stream))
-        _check(name, st)
-        return A, tok, mask
+        args = (_ptr(t), ts, _ptr(d), ds, _ptr(tokens), _ptr(r), _ptr(u), B, K, V, float(temperature),
+                _ptr(A), _ptr(tok), _ptr(mask), _ptr(ws), ws.numel())
+        return Launcher(name, args, (A, tok, mask), keep)
     gstar = torch.empty((B, K), dtype=torch.float32, device=dev) if with_gstar else None
-    st = lib.spec_cactus_verify(_ptr(t), ts, _ptr(d), ds, _ptr(tokens), _ptr(r), _ptr(u), B, K, V, float(delta),
-                                float(temperature), _ptr(A), _ptr(tok), _ptr(mask), _ptr(gstar), _ptr(ws),
-                                ws.numel(), _stream(stream))
-    _check(name, st)
-    return A, tok, mask, gstar
+    args = (_ptr(t), ts, _ptr(d), ds, _ptr(tokens), _ptr(r), _ptr(u), B, K, V, float(delta), float(temperature),
+            _ptr(A), _ptr(tok), _ptr(mask), _ptr(gstar), _ptr(ws), ws.numel())
+    return Launcher(name, args, (A, tok, mask, gstar), keep + (gstar,))
 
 
 def spec_counterfactual_gamma(target, drafts, traj_tokens, temperature: float = 1.0, *, sel=None,
@@ -191,7 +222,15 @@ def spec_counterfactual_gamma(target, drafts, traj_tokens, temperature: float = 
     """HedgeSpec evaluation.  target [B, R, V] (R >= K; R = K+1 for the fused verify),
     drafts [N, B, K, V], traj_tokens [B, K].  Returns a dict with gamma [B, K, N],
     est_len [B, N], loss [B, N] and, when sel is given, accepted_len, out_token, accept_mask."""
-    lib = load()
+    return prepare_counterfactual_gamma(target, drafts, traj_tokens, temperature, sel=sel,
+                                        draft_tokens=draft_tokens, r_accept=r_accept, u_resample=u_resample,
+                                        workspace=workspace, with_mask=with_mask).launch(stream)
+
+
+def prepare_counterfactual_gamma(target, drafts, traj_tokens, temperature: float = 1.0, *, sel=None,
+                                 draft_tokens=None, r_accept=None, u_resample=None, workspace=None,
+                                 with_mask: bool = True) -> Launcher:
+    """spec_counterfactual_gamma with its tensors fixed (see Launcher)."""
     _need_cuda(target, drafts, traj_tokens, sel, draft_tokens, r_accept, u_resample)
     N, B, K, V = drafts.shape
     if target.shape[0] != B or target.shape[2] != V:
@@ -217,16 +256,13 @@ def spec_counterfactual_gamma(target, drafts, traj_tokens, temperature: float = 
         A = torch.empty(B, dtype=torch.int32, device=dev)
         tok = torch.empty(B, dtype=torch.int32, device=dev)
         mask = torch.empty((B, K), dtype=torch.uint8, device=dev) if with_mask else None
-    ws = make_workspace(B, K, N, dev) if workspace is None else workspace
-    st = lib.spec_counterfactual_gamma(_ptr(t), ts, R, _ptr(d), ds, drafter_stride, _ptr(traj), B, K, N, V,
-                                       float(temperature), _ptr(out["gamma"]), _ptr(out["est_len"]),
-                                       _ptr(out["loss"]), _ptr(sel), _ptr(draft_tokens), _ptr(r_accept),
-                                       _ptr(u_resample), _ptr(A), _ptr(tok), _ptr(mask), _ptr(ws), ws.numel(),
-                                       _stream(stream))
-    _check("spec_counterfactual_gamma", st)
-    if fused:
         out.update(accepted_len=A, out_token=tok, accept_mask=mask)
-    return out
+    ws = make_workspace(B, K, N, dev) if workspace is None else workspace
+    args = (_ptr(t), ts, R, _ptr(d), ds, drafter_stride, _ptr(traj), B, K, N, V, float(temperature),
+            _ptr(out["gamma"]), _ptr(out["est_len"]), _ptr(out["loss"]), _ptr(sel), _ptr(draft_tokens),
+            _ptr(r_accept), _ptr(u_resample), _ptr(A), _ptr(tok), _ptr(mask), _ptr(ws), ws.numel())
+    keep = (t, d, traj, sel, draft_tokens, r_accept, u_resample, ws, out)
+    return Launcher("spec_counterfactual_gamma", args, out, keep)
 
 
 def hedge_update(cum_regret, weights, loss, loss_scale: float, *, has_loss=None, v_select=None,

@@ -81,28 +81,87 @@ __device__ __forceinline__ void row_acc_add8(RowAcc& a, const float z[8], float 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
+// Cross-lane moves use DPP (data-parallel primitives of the VALU) rather than
+// LDS permutes: quad permutations and row mirrors combine lanes within a row of
+// 16, row shifts and row broadcasts build prefix sums, and readlane collects the
+// four row results.  64-bit values move as two 32-bit halves.
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row -> the next row
+constexpr int kDppRowBcast31 = 0x143;  // lane 31 -> rows 2 and 3
+constexpr int kDppWaveShr1 = 0x138;    // lane i <- lane i - 1
+__host__ __device__ constexpr int dpp_row_shr(int n) { return 0x110 + n; }
+
+// Lane values moved by a DPP control; lanes with no source (or outside the row
+// mask) read 0.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, true);
+}
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(dpp_i32<CTRL, ROW_MASK>(__float_as_int(v)));
+}
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = dpp_i32<CTRL, ROW_MASK>(static_cast<int>(b));
+  const int hi = dpp_i32<CTRL, ROW_MASK>(static_cast<int>(b >> 32));
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(b), lane);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), lane);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+__device__ __forceinline__ float readlane_f32(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Maximum over the 64 lanes (every lane gets it).
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
+  v = fmaxf(v, dpp_f32<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppRowMirror>(v));
+  return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)), fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
 }
 
+__device__ __forceinline__ int wave_max_i(int v) {
+  v = max(v, dpp_i32<kDppQuadXor1>(v));
+  v = max(v, dpp_i32<kDppQuadXor2>(v));
+  v = max(v, dpp_i32<kDppRowHalfMirror>(v));
+  v = max(v, dpp_i32<kDppRowMirror>(v));
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// Sum over the 64 lanes in a fixed order (every lane gets it).
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  v += dpp_f64<kDppQuadXor1>(v);
+  v += dpp_f64<kDppQuadXor2>(v);
+  v += dpp_f64<kDppRowHalfMirror>(v);
+  v += dpp_f64<kDppRowMirror>(v);
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
+// Inclusive prefix sum over the 64 lanes (ascending lane order): Hillis-Steele
+// within each row of 16, then the row totals carried across rows.
+__device__ __forceinline__ double wave_incl_scan(double v) {
+  v += dpp_f64<dpp_row_shr(1)>(v);
+  v += dpp_f64<dpp_row_shr(2)>(v);
+  v += dpp_f64<dpp_row_shr(4)>(v);
+  v += dpp_f64<dpp_row_shr(8)>(v);
+  v += dpp_f64<kDppRowBcast15, 0xa>(v);
+  v += dpp_f64<kDppRowBcast31, 0xc>(v);
   return v;
 }
 
-// Inclusive prefix sum over the 64 lanes (ascending lane order).
-__device__ __forceinline__ double wave_incl_scan(double v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const double o = __shfl_up(v, d, 64);
-    if (lane >= d) v += o;
-  }
-  return v;
-}
+// The value of lane i - 1 (0 in lane 0).
+__device__ __forceinline__ double lane_prev(double v) { return dpp_f64<kDppWaveShr1>(v); }
 
 struct RowStats {
   float k;       // row reference (max over lanes), integer-valued

@@ -1,34 +1,40 @@
 // libspecverify: batched speculative-sampling verification on gfx950.
 //
 // One persistent kernel, `flow_kernel`, serves the three verification entry
-// points.  The work of a call is cut into units that workgroups claim from a
-// shared counter:
+// points.  Its grid is the number of workgroups the device holds at once (G),
+// and every workgroup g runs three phases on a fixed schedule; nothing is
+// claimed from a shared counter.
 //
-//   statistics units (claimed first, in sequence order) -- stream a quarter
-//       row (4 slices of 16384 tokens) once from HBM, double-buffered, and
-//       reduce it to an exact base-2 softmax (reference, sum) pair
-//       (spec_device.hpp).  They never wait for anything.
-//   draw units -- published when the last statistics unit of a sequence
-//       finishes: that workgroup merges the sequence's statistics, takes
+//   phase 0 -- statistics slices g, g + G, g + 2G, ... of the call's slice
+//       list.  A slice is 16384 tokens of one row, streamed once from HBM with
+//       128-bit loads while the next slice's loads are in flight.  Each wave
+//       reduces its share to an exact base-2 softmax pair (reference k, sum s)
+//       (spec_device.hpp) and publishes it as one 64-bit word.  The list is
+//       sequence-major, so sequences finish their statistics one after another.
+//   phase 1 -- units g, g + G, ... of the draw / gamma list.  A draw unit (one
+//       per slice of a sequence's rows) merges the sequence's statistics, takes
 //       every accept decision ([LT] §5.1, [CA] Key design 3), finds the first
-//       rejection A and publishes one draw unit per slice.  A draw unit writes
-//       per-512-token sub-tile masses of the sampling weights of the row pair
-//       A ((pt - pd)+, or Cactus's (h - pd)+) or of the bonus row pt; the last
-//       one to finish finds the inverse-CDF crossing and re-reads the single
-//       sub-tile that holds it ([LT] §9.1: accepted length and the resampled
-//       or bonus token).
-//   gamma units -- published when every statistics unit of one position has
-//       finished: sum_x min(pt, pd_i) over one slice for all N drafters (the
-//       target slice stays in registers); the last one of a sequence forms
-//       the HedgeSpec estimator and loss ([NB] Key designs 1-3).
+//       rejection A and publishes per-512-token sub-tile masses of the sampling
+//       weights of its slice of the row pair A ((pt - pd)+, Cactus's (h - pd)+)
+//       or of the bonus row pt; the unit of slice 0 also publishes the decision.
+//       A gamma unit publishes sum_x min(pt, pd_i) over its slice for all N
+//       drafters (the target slice stays in registers).
+//   phase 2 -- units g, g + G, ... of the final-step list: the inverse-CDF
+//       crossing, found from the sub-tile masses and a re-read of the one
+//       sub-tile that holds it ([LT] §9.1), or the HedgeSpec estimator and loss
+//       ([NB] Key designs 1-3).
 //
-// Published units go to a queue whose slots follow the statistics units in
-// claim order, so a workgroup only ever waits when every statistics unit has
-// been claimed and no published work is left.  A draw or gamma unit's
-// sequence had its statistics streamed moments earlier, so its re-reads are
-// served by the Infinity Cache.  Counters are reset by the last unit of each
-// sequence and the claim counters by the last workgroup to exit, so the
-// workspace counters are zero again when the kernel ends.
+// A phase-1 unit reads only phase-0 words and a phase-2 unit only phase-0 and
+// phase-1 words, and every workgroup finishes a phase before it starts the
+// next, so every wait ends (a wait is also bounded by the wall clock; a timeout
+// sets the workspace's fault word).
+//
+// Cross-workgroup data is published with device-scope 64-bit stores of words
+// that are never zero, into a workspace that is zero before the call; a reader
+// polls a word with device-scope loads until it is non-zero.  No counter, queue
+// or fence sits on the streaming path.  The last step of each sequence clears
+// every word the sequence published, so the workspace is zero again when the
+// kernel ends.
 //
 // [LT] "Speculative Decoding 为什么是 Lossless 的 -- 详细证明教程";
 // [NB] HedgeSpec note "Not-a-Bandit: Provably No-Regret Drafter Selection ...";
@@ -50,11 +56,13 @@ enum : int { W_RESID = 0, W_TARGET_H = 1, W_TARGET = 2 };
 constexpr int kTilesPerSlice = 8;
 constexpr int kSliceTok = kTile * kTilesPerSlice;   // 16384 tokens per slice
 constexpr int kSliceChunks = kSliceTok / kVec;      // 16-byte chunks per slice
-constexpr int kSlicesPerUnit = 4;                   // slices one statistics unit streams
 constexpr int kMaxSlices = (kMaxV + kSliceTok - 1) / kSliceTok;  // slices of the longest row
-constexpr unsigned long long kWaitTicks = 200000000ull;  // bounded queue wait: 2 s of the 100 MHz clock
-constexpr int kDecWords = 12;
-enum : int { DYN_DRAW = 1, DYN_GAMMA = 2 };
+constexpr unsigned long long kWaitTicks = 200000000ull;  // bounded wait: 2 s of the 100 MHz clock
+constexpr unsigned long long kValid = 1ull << 63;        // published bit of an fp64 word
+constexpr int kStage = 8 * kThreads;  // statistics words staged in LDS at once
+constexpr int kRowCap = 256;          // merged rows held in LDS at once
+constexpr int kNoK = INT32_MIN;       // statistics word of a share with no finite logit
+constexpr int kDecWords = 6;          // words of a decision record
 
 // Everything a lane needs to turn logits into sampling weights (fp64).
 struct WeightCtx {
@@ -85,16 +93,15 @@ struct Params {
   double delta;
   int mode;
   int fused;
-  // units
-  int R;     // statistic rows per sequence
-  int RT;    // of which target rows
-  int S;     // slices per row
-  int Q;     // statistics units per row (kSlicesPerUnit slices each)
-  int nsub;  // 512-token sub-tiles per row
-  int U1;    // statistics units per sequence
-  int U3;    // final steps per sequence (estimator and / or draw)
-  int n_static, total_units;
-  int queue_cap;  // queue slots in the workspace
+  // schedule
+  int R;       // statistic rows per sequence
+  int RT;      // of which target rows
+  int S;       // slices per row
+  int nsub;    // 512-token sub-tiles per row
+  int P1;      // phase-1 units per sequence
+  int P2;      // phase-2 units per sequence
+  int RS;      // statistics slices per sequence (R * S)
+  int total0;  // statistics slices of the call (B * R * S; below 2^31 since each is 32 KB of logits)
   // outputs
   int32_t* accepted_len;
   int32_t* out_token;
@@ -103,20 +110,13 @@ struct Params {
   float* gamma;
   float* est_len;
   float* loss;
-  // workspace: counters
-  uint32_t* work;    // [0] claim counter, [1] exit counter, [2] queue tail, [3] fault flag
-  uint32_t* p1cnt;   // [B][K+1] finished statistics units per (sequence, position)
-  uint32_t* p1all;   // [B] finished statistics units per sequence
-  uint32_t* p2cnt;   // [B] finished draw units
-  uint32_t* p2gcnt;  // [B] finished gamma units
-  uint32_t* done;    // [B] finished final steps
-  unsigned long long* queue;  // published units (0 = slot not yet filled)
-  // workspace: scratch
-  float* stat_k;   // [B][R][Q]
-  double* stat_s;  // [B][R][Q]
-  double* subsum;  // [B][nsub]
-  double* gpart;   // [B][K][N][S]
-  double* dec;     // [B][kDecWords]
+  // workspace (all zero between calls)
+  uint32_t* flags;            // [3]: fault word
+  uint32_t* done;             // [B] final steps finished (fused calls: two per sequence)
+  unsigned long long* dec;    // [B][kDecWords] draw decision records
+  unsigned long long* part;   // [B][R][S][kWaves] statistics words
+  unsigned long long* mass;   // [B][nsub] sub-tile masses (fp64 | kValid)
+  unsigned long long* gpart;  // [B][K][N][S] gamma partial sums (fp64 | kValid)
 };
 
 __device__ __forceinline__ const uint4* as_chunks(const uint16_t* row) { return reinterpret_cast<const uint4*>(row); }
@@ -133,27 +133,187 @@ __device__ __forceinline__ const uint16_t* stat_row(const Params& p, int b, int 
   const int j = r - p.RT;
   return draft_row(p, b, j / p.K, j % p.K);
 }
-__device__ __forceinline__ int counter_of(const Params& p, int r) {
-  if (p.mode == MODE_VERIFY) return 0;
-  return r < p.RT ? r : (r - p.RT) % p.K;
-}
-__device__ __forceinline__ uint32_t p1_target(const Params& p, int k) {
-  if (p.mode == MODE_VERIFY) return static_cast<uint32_t>(p.R * p.Q);
-  return static_cast<uint32_t>((1 + p.N) * p.Q);  // k < K
+__device__ __forceinline__ unsigned long long* part_row(const Params& p, int b, int r) {
+  return p.part + (static_cast<size_t>(b) * p.R + r) * static_cast<size_t>(p.S) * kWaves;
 }
 
-// Merge the per-unit statistics of one row into (k, s): exact power-of-two rescaling.
-__device__ __forceinline__ RowStats merge_row(const Params& p, int b, int r) {
-  const size_t base = (static_cast<size_t>(b) * p.R + r) * p.Q;
-  uint32_t* kp = reinterpret_cast<uint32_t*>(p.stat_k + base);
-  float km = kNoRef;
-  for (int s = 0; s < p.Q; ++s) km = fmaxf(km, __uint_as_float(ld_agent(kp + s)));
-  double tot = 0.0;
-  for (int s = 0; s < p.Q; ++s) {
-    const float ks = __uint_as_float(ld_agent(kp + s));
-    tot += ldexp(ld_agent_d(p.stat_s + base + s), static_cast<int>(fmaxf(ks - km, -2000.0f)));
+// Statistic row streamed i-th within a sequence.  Verify calls: target 0, draft 0,
+// target 1, draft 1, ..., then the bonus target row K.  Gamma calls: position by
+// position, target row k then every drafter's row k; the fused bonus row last.
+__device__ __forceinline__ int order_row(const Params& p, int i) {
+  if (p.mode == MODE_VERIFY) {
+    if (i >= 2 * p.K) return p.K;
+    const int k = i >> 1;
+    return (i & 1) ? p.RT + k : k;
   }
-  return RowStats{km, tot};
+  const int g1 = p.N + 1;
+  if (i >= p.K * g1) return p.K;
+  const int k = i / g1, m = i - k * g1;
+  return m == 0 ? k : p.RT + (m - 1) * p.K + k;
+}
+
+// ---------------------------------------------------------------------------
+// Published words
+// ---------------------------------------------------------------------------
+
+// Statistics word: low 32 bits the fp32 sum s (>= 1/2 whenever a finite logit was
+// seen), high 32 bits the integer reference k, or kNoK with s = 0.  Never zero.
+__device__ __forceinline__ unsigned long long pack_stats(float km, double s) {
+  if (!(km > kNoRef)) return static_cast<unsigned long long>(static_cast<uint32_t>(kNoK)) << 32;
+  const int k = static_cast<int>(fminf(fmaxf(km, -1.0e9f), 1.0e9f));
+  return (static_cast<unsigned long long>(static_cast<uint32_t>(k)) << 32) |
+         static_cast<unsigned long long>(__float_as_uint(static_cast<float>(s)));
+}
+__device__ __forceinline__ int stats_k(unsigned long long w) { return static_cast<int>(static_cast<uint32_t>(w >> 32)); }
+__device__ __forceinline__ double stats_s(unsigned long long w) {
+  return static_cast<double>(__uint_as_float(static_cast<uint32_t>(w)));
+}
+__device__ __forceinline__ unsigned long long pack_f64(double v) {
+  return static_cast<unsigned long long>(__double_as_longlong(v)) | kValid;
+}
+__device__ __forceinline__ double unpack_f64(unsigned long long w) {
+  return __longlong_as_double(static_cast<long long>(w & ~kValid));
+}
+
+// Re-read a word until it is published.  After the wait bound (or once another
+// wait has timed out) the fault word is set and 0 is returned.
+__device__ __forceinline__ unsigned long long poll_word(uint32_t* flags, unsigned long long* a) {
+  unsigned long long w = ld_agent_u64(a);
+  if (w != 0ull) return w;
+  const unsigned long long t0 = wall_clock64();
+  while (true) {
+    if (ld_agent(&flags[3]) != 0u) return 0ull;
+    __builtin_amdgcn_s_sleep(2);
+    w = ld_agent_u64(a);
+    if (w != 0ull) return w;
+    if (wall_clock64() - t0 > kWaitTicks) {
+      st_agent(&flags[3], 1u);
+      return 0ull;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Phase 0: statistics slices
+// ---------------------------------------------------------------------------
+
+struct SliceLoc {
+  const uint4* row;
+  int c0;                   // first chunk of the slice
+  int full;                 // every chunk of the slice lies inside the row and holds 8 tokens
+  unsigned long long* out;  // the slice's kWaves statistics words
+};
+
+__device__ __forceinline__ SliceLoc slice_loc(const Params& p, int sig) {
+  const int b = sig / p.RS;
+  const int q = sig - b * p.RS;
+  const int i = q / p.S, x = q - i * p.S;
+  const int r = order_row(p, i);
+  SliceLoc L;
+  L.row = as_chunks(stat_row(p, b, r));
+  L.c0 = x * kSliceChunks;
+  L.full = (x + 1) * kSliceTok <= p.V;
+  L.out = part_row(p, b, r) + static_cast<size_t>(x) * kWaves;
+  return L;
+}
+
+__device__ __forceinline__ void slice_load(const Params& p, const SliceLoc& L, uint4 v[kTilesPerSlice]) {
+  const int tid = threadIdx.x;
+  if (L.full) {
+#pragma unroll
+    for (int t = 0; t < kTilesPerSlice; ++t) v[t] = L.row[L.c0 + t * kThreads + tid];
+  } else {
+    const int nchunks = (p.V + kVec - 1) / kVec;
+#pragma unroll
+    for (int t = 0; t < kTilesPerSlice; ++t) {
+      const int ci = L.c0 + t * kThreads + tid;
+      if (ci < nchunks) v[t] = L.row[ci];
+    }
+  }
+}
+
+__device__ __forceinline__ void slice_finish(const Params& p, const SliceLoc& L, const uint4 v[kTilesPerSlice]) {
+  RowAcc a = row_acc_init();
+  if (L.full) {
+#pragma unroll
+    for (int t = 0; t < kTilesPerSlice; ++t) {
+      float z[8];
+      unpack8(v[t], z, 8);
+      row_acc_add8(a, z, p.c);
+    }
+  } else {
+    const int nchunks = (p.V + kVec - 1) / kVec;
+#pragma unroll
+    for (int t = 0; t < kTilesPerSlice; ++t) {
+      const int ci = L.c0 + t * kThreads + static_cast<int>(threadIdx.x);
+      if (ci < nchunks) {
+        float z[8];
+        unpack8(v[t], z, p.V - ci * kVec);
+        row_acc_add8(a, z, p.c);
+      }
+    }
+  }
+  const float km = wave_max(a.k);
+  const double s = wave_sum(ldexp(a.s, static_cast<int>(fmaxf(a.k - km, -2000.0f))));
+  if (lane_id() == 0) st_agent_u64(L.out + wave_id(), pack_stats(km, s));
+}
+
+// ---------------------------------------------------------------------------
+// Merging published statistics (block-wide)
+// ---------------------------------------------------------------------------
+
+struct MergeLds {
+  unsigned long long stage[kStage];
+  float rk[kRowCap];   // merged reference of row i
+  double rs[kRowCap];  // merged sum of row i
+};
+
+// Rows row_of(0..nrows) of sequence b (nrows <= kRowCap) -> M.rk / M.rs.
+template <class RowFn>
+__device__ __forceinline__ void merge_rows(const Params& p, int b, int nrows, RowFn row_of, MergeLds& M) {
+  const int W = p.S * kWaves;
+  const int per = kStage / W > 0 ? kStage / W : 1;
+  const int tid = threadIdx.x;
+  for (int i0 = 0; i0 < nrows; i0 += per) {
+    const int nb = min(per, nrows - i0);
+    const int nw = nb * W;
+    unsigned long long w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int q = tid + e * kThreads;
+      w[e] = 1ull;
+      if (q < nw) w[e] = ld_agent_u64(part_row(p, b, row_of(i0 + q / W)) + q % W);
+    }
+    bool missing = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int q = tid + e * kThreads;
+      if (q < nw) M.stage[q] = w[e];
+      missing |= w[e] == 0ull;
+    }
+    if (missing) {  // not yet published (rare): wait for each missing word
+      for (int q = tid; q < nw; q += kThreads)
+        if (M.stage[q] == 0ull) M.stage[q] = poll_word(p.flags, part_row(p, b, row_of(i0 + q / W)) + q % W);
+    }
+    __syncthreads();
+    for (int i = wave_id(); i < nb; i += kWaves) {
+      const unsigned long long* st = M.stage + i * W;
+      int km = kNoK;
+      for (int q = lane_id(); q < W; q += 64) km = max(km, stats_k(st[q]));
+      km = wave_max_i(km);
+      double s = 0.0;
+      for (int q = lane_id(); q < W; q += 64) {
+        const int kq = stats_k(st[q]);
+        if (kq != kNoK) s += ldexp(stats_s(st[q]), max(kq - km, -2000));
+      }
+      s = wave_sum(s);
+      if (lane_id() == 0) {
+        M.rk[i0 + i] = km == kNoK ? kNoRef : static_cast<float>(km);
+        M.rs[i0 + i] = s;
+      }
+    }
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -192,9 +352,8 @@ __device__ __forceinline__ bool find_subtile(const double* subsum, int nsub, dou
   double ls = 0.0;
   for (int s = lo; s < hi; ++s) ls += subsum[s];
   const double incl = wave_incl_scan(ls);
-  double excl = __shfl_up(incl, 1, 64);
-  if (lane == 0) excl = 0.0;
-  const double Z = __shfl(incl, 63, 64);
+  const double excl = lane_prev(incl);
+  const double Z = readlane_f64(incl, 63);
   if (!(Z > 0.0)) return false;
   const double x = u * Z;
   const unsigned long long m = __ballot(incl > x);
@@ -234,9 +393,9 @@ __device__ __forceinline__ bool find_subtile(const double* subsum, int nsub, dou
       }
     }
   }
-  s_star = __shfl(ss, L, 64);
-  P = __shfl(P, L, 64);
-  lane_clamp = __shfl(lane_clamp, L, 64);
+  s_star = __builtin_amdgcn_readlane(ss, L);
+  P = readlane_f64(P, L);
+  lane_clamp = __builtin_amdgcn_readlane(lane_clamp, L);
   x_rel = (clamp || lane_clamp) ? __builtin_inf() : x - P;
   return s_star >= 0;
 }
@@ -245,8 +404,8 @@ __device__ __forceinline__ bool find_subtile(const double* subsum, int nsub, dou
 // (or the sub-tile's last positive-mass token when x_rel is +inf).  Recomputes
 // the sub-tile's weights and lane scan exactly as the draw pass did.
 template <bool PAIR>
-__device__ __forceinline__ int find_token(const uint16_t* trow, const uint16_t* drow, int V, const WeightCtx& w, int s_star,
-                          double x_rel) {
+__device__ __forceinline__ int find_token(const uint16_t* trow, const uint16_t* drow, int V, const WeightCtx& w,
+                                          int s_star, double x_rel) {
   const int lane = lane_id();
   const int nchunks = (V + kVec - 1) / kVec;
   const int ci = s_star * 64 + lane;
@@ -266,8 +425,7 @@ __device__ __forceinline__ int find_token(const uint16_t* trow, const uint16_t* 
     for (int e = 0; e < 8; ++e) ls += wv[e];
   }
   const double incl = wave_incl_scan(ls);
-  double excl = __shfl_up(incl, 1, 64);
-  if (lane == 0) excl = 0.0;
+  const double excl = lane_prev(incl);
   const unsigned long long pos = __ballot(ls > 0.0);
   if (pos == 0ull) return -1;
   const unsigned long long m = __ballot(incl > x_rel);
@@ -287,29 +445,29 @@ __device__ __forceinline__ int find_token(const uint16_t* trow, const uint16_t* 
     if (e_star < 0) e_star = e_last;
     tok = e_star >= 0 ? ci * kVec + e_star : -1;
   }
-  tok = __shfl(tok, L, 64);
+  tok = __builtin_amdgcn_readlane(tok, L);
   if (tok < 0) {  // rounding put the crossing on a zero-mass lane: last positive token of the sub-tile
     const int Lp = 63 - __clzll(static_cast<long long>(pos));
     int t2 = -1;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       if (wv[e] > 0.0) t2 = ci * kVec + e;
-    tok = __shfl(t2, Lp, 64);
+    tok = __builtin_amdgcn_readlane(t2, Lp);
   }
   return tok;
 }
 
 // Per-sub-tile masses of the sampling weights over tiles [t0, t0 + ntiles) of a
-// row (pair); lane 63 of each wave stores the sub-tile's inclusive scan total.
-// Used for a draw slice (to global memory) and for the whole-row fallback (to LDS).
-template <bool PAIR, bool TO_GLOBAL>
+// row (pair); lane 63 of each wave holds the sub-tile's inclusive scan total.
+// A draw slice publishes them (TO_GLOBAL); the whole-row fallback keeps them in LDS.
+template <bool PAIR, bool TO_GLOBAL, int kBatch>
 __device__ __forceinline__ void weight_subtiles(const uint16_t* trow, const uint16_t* drow, int V, const WeightCtx& w,
-                                                int t0, int ntiles, double* subsum, int nsub) {
+                                                int t0, int ntiles, double* lds_sub, unsigned long long* glob_sub,
+                                                int nsub) {
   const uint4* tr = as_chunks(trow);
   const uint4* dr = as_chunks(drow);
   const int nchunks = (V + kVec - 1) / kVec;
   const int tid = threadIdx.x;
-  constexpr int kBatch = 4;
 #pragma unroll 1
   for (int j0 = 0; j0 < ntiles; j0 += kBatch) {
     uint4 vt[kBatch], vd[kBatch];
@@ -344,9 +502,9 @@ __device__ __forceinline__ void weight_subtiles(const uint16_t* trow, const uint
       const int s = jt * kWaves + wave_id();
       if (lane_id() == 63 && s < nsub) {
         if (TO_GLOBAL)
-          st_agent_d(&subsum[s], incl);
+          st_agent_u64(&glob_sub[s], pack_f64(incl));
         else
-          subsum[s] = incl;
+          lds_sub[s] = incl;
       }
     }
   }
@@ -364,48 +522,70 @@ struct Decision {
 };
 
 struct DecideLds {
-  float rk[2 * SPEC_MAX_K + 1];
-  double rs[2 * SPEC_MAX_K + 1];
   uint32_t state[SPEC_MAX_K];
   double ct[SPEC_MAX_K];
   double gs[SPEC_MAX_K];
   Decision d;
 };
 
+struct Lds {
+  MergeLds m;
+  DecideLds dl;
+  double subsum[kMaxSub];
+  double part[SPEC_MAX_N * kWaves];
+  double gsum[kRowCap];
+  double arat[kRowCap];
+  float lt;
+  float ld[SPEC_MAX_N];
+  int flag;
+};
+
+__device__ __forceinline__ int draw_drafter(const Params& p, int b) { return p.mode == MODE_VERIFY ? 0 : p.sel[b]; }
+
 // Merge the statistics of target rows 0..K and drafter `drafter`'s rows 0..K-1,
 // take every accept decision, and describe the draw.  Writes accept_mask and
-// gamma_star when `write_outputs`.  The result is in L.d after the call.
-__device__ __forceinline__ void decide(const Params& p, int b, int drafter, bool write_outputs, DecideLds& L) {
+// gamma_star when `write_outputs`.  The result is in L.dl.d after the call.
+__device__ __forceinline__ void decide(const Params& p, int b, bool write_outputs, Lds& L) {
   const int K = p.K, V = p.V;
   const int t = threadIdx.x;
+  const int drafter = draw_drafter(p, b);
   const bool bad_sel = drafter < 0 || drafter >= p.N;
-  if (!bad_sel && t < 2 * K + 1) {
-    const int r = t <= K ? t : p.RT + drafter * K + (t - K - 1);
-    const RowStats st = merge_row(p, b, r);
-    L.rk[t] = st.k;
-    L.rs[t] = st.s;
+  const int dsafe = bad_sel ? 0 : drafter;
+  // thread t < K: the drafted token of position t, its uniform and its two logits,
+  // fetched first so that these loads overlap the statistics loads
+  int n = -1;
+  float rr = 0.0f, zt = 0.0f, zd = 0.0f;
+  bool tok_ok = false;
+  if (t < K) {
+    n = p.tokens[b * K + t];
+    rr = p.r[b * K + t];
+    tok_ok = !bad_sel && n >= 0 && n < V;
+    if (tok_ok) {
+      zt = bf16_at(target_row(p, b, t), n);
+      zd = bf16_at(draft_row(p, b, drafter, t), n);
+    }
   }
-  __syncthreads();
+  // rows 0..K: target rows 0..K; rows K+1..2K: the drafter's rows 0..K-1
+  merge_rows(p, b, 2 * K + 1, [&](int i) { return i <= K ? i : p.RT + dsafe * K + (i - K - 1); }, L.m);
   if (t < K) {
     uint32_t state = ST_INVALID;
     bool acc = false;
-    const int n = p.tokens[b * K + t];
-    if (!bad_sel && n >= 0 && n < V) {
-      const RowStats st{L.rk[t], L.rs[t]};
-      const RowStats sd{L.rk[K + 1 + t], L.rs[K + 1 + t]};
+    if (tok_ok) {
+      const RowStats st{L.m.rk[t], L.m.rs[t]};
+      const RowStats sd{L.m.rk[K + 1 + t], L.m.rs[K + 1 + t]};
       // [CA] Key design 3 with the verifier's probability c of the candidate; delta = 0 is SpS.
-      const double ct = fmin(token_prob(bf16_at(target_row(p, b, t), n), p.c, st), 1.0);
-      const double cd = token_prob(bf16_at(draft_row(p, b, drafter, t), n), p.c, sd);
+      const double ct = fmin(token_prob(zt, p.c, st), 1.0);
+      const double cd = token_prob(zd, p.c, sd);
       const double gs = fmin(ct + sqrt(2.0 * p.delta * ct * (1.0 - ct)), 1.0);
       const double ratio = cd > 0.0 ? gs / cd : (gs > 0.0 ? __builtin_inf() : 0.0);
-      acc = static_cast<double>(p.r[b * K + t]) < ratio;  // [LT] §5.1: strict
+      acc = static_cast<double>(rr) < ratio;  // [LT] §5.1: strict
       state = acc ? ST_ACCEPT : ST_REJECT;
-      L.ct[t] = ct;
-      L.gs[t] = gs;
+      L.dl.ct[t] = ct;
+      L.dl.gs[t] = gs;
       if (write_outputs && p.gamma_star) p.gamma_star[b * K + t] = static_cast<float>(gs);
     }
     if (write_outputs && p.accept_mask) p.accept_mask[b * K + t] = acc ? 1 : 0;
-    L.state[t] = state;
+    L.dl.state[t] = state;
   }
   __syncthreads();
   if (t == 0) {
@@ -413,8 +593,8 @@ __device__ __forceinline__ void decide(const Params& p, int b, int drafter, bool
     int A = K;
     bool bad = bad_sel;
     for (int q = 0; q < K; ++q) {
-      bad |= (L.state[q] == ST_INVALID);
-      if (L.state[q] == ST_REJECT && A == K) A = q;
+      bad |= (L.dl.state[q] == ST_INVALID);
+      if (L.dl.state[q] == ST_REJECT && A == K) A = q;
     }
     WeightCtx w;
     w.c = p.c;
@@ -433,15 +613,15 @@ __device__ __forceinline__ void decide(const Params& p, int b, int drafter, bool
       w.inv_st = 1.0;
     } else if (A < K) {
       // [LT] §9.1: the first rejection A is resampled from the residual of its row pair
-      const double ct = L.ct[A], gs = L.gs[A];
+      const double ct = L.dl.ct[A], gs = L.dl.gs[A];
       d.A = A;
       d.draw_row = A;
       d.pair = 1;
       w.mode = W_RESID;
-      w.kt = L.rk[A];
-      w.inv_st = 1.0 / L.rs[A];
-      w.kd = L.rk[K + 1 + A];
-      w.inv_sd = 1.0 / L.rs[K + 1 + A];
+      w.kt = L.m.rk[A];
+      w.inv_st = 1.0 / L.m.rs[A];
+      w.kd = L.m.rk[K + 1 + A];
+      w.inv_sd = 1.0 / L.m.rs[K + 1 + A];
       w.s_scale = ct < 1.0 ? (1.0 - gs) / (1.0 - ct) : 0.0;  // [CA] Key design 2 (1.0 exactly at delta = 0)
       w.gstar = gs;
       w.n = p.tokens[b * K + A];
@@ -452,177 +632,135 @@ __device__ __forceinline__ void decide(const Params& p, int b, int drafter, bool
       d.draw_row = K;
       d.pair = 0;
       w.mode = W_TARGET;
-      w.kt = L.rk[K];
-      w.inv_st = 1.0 / L.rs[K];
+      w.kt = L.m.rk[K];
+      w.inv_st = 1.0 / L.m.rs[K];
     }
     d.w = w;
-    L.d = d;
+    L.dl.d = d;
   }
   __syncthreads();
-}
-
-__device__ __forceinline__ void store_decision(double* rec, const Decision& d) {
-  st_agent_d(rec + 0, static_cast<double>(d.A));
-  st_agent_d(rec + 1, static_cast<double>(d.draw_row));
-  st_agent_d(rec + 2, static_cast<double>(d.pair));
-  st_agent_d(rec + 3, static_cast<double>(d.w.kt));
-  st_agent_d(rec + 4, static_cast<double>(d.w.kd));
-  st_agent_d(rec + 5, d.w.inv_st);
-  st_agent_d(rec + 6, d.w.inv_sd);
-  st_agent_d(rec + 7, d.w.s_scale);
-  st_agent_d(rec + 8, d.w.gstar);
-  st_agent_d(rec + 9, static_cast<double>(d.w.n));
-  st_agent_d(rec + 10, static_cast<double>(d.w.special));
-  st_agent_d(rec + 11, static_cast<double>(d.w.mode));
-}
-
-__device__ __forceinline__ Decision load_decision(double* rec, float c) {
-  Decision d;
-  d.A = static_cast<int>(ld_agent_d(rec + 0));
-  d.draw_row = static_cast<int>(ld_agent_d(rec + 1));
-  d.pair = static_cast<int>(ld_agent_d(rec + 2));
-  d.w.c = c;
-  d.w.kt = static_cast<float>(ld_agent_d(rec + 3));
-  d.w.kd = static_cast<float>(ld_agent_d(rec + 4));
-  d.w.inv_st = ld_agent_d(rec + 5);
-  d.w.inv_sd = ld_agent_d(rec + 6);
-  d.w.s_scale = ld_agent_d(rec + 7);
-  d.w.gstar = ld_agent_d(rec + 8);
-  d.w.n = static_cast<int>(ld_agent_d(rec + 9));
-  d.w.special = static_cast<int>(ld_agent_d(rec + 10));
-  d.w.mode = static_cast<int>(ld_agent_d(rec + 11));
-  return d;
 }
 
 // ---------------------------------------------------------------------------
 // Units
 // ---------------------------------------------------------------------------
 
-struct Lds {
-  double subsum[kMaxSub];
-  double scratch[2 * kWaves];
-  double part[SPEC_MAX_N * kWaves];
-  float lt;
-  float ld[SPEC_MAX_N];
-  DecideLds dl;
-  int flag;
-  unsigned long long desc;
-};
-
-__device__ __forceinline__ void load_slice(const uint4* rc, int c0, int nchunks, uint4 v[kTilesPerSlice]) {
-#pragma unroll
-  for (int t = 0; t < kTilesPerSlice; ++t) {
-    const int ci = c0 + t * kThreads + static_cast<int>(threadIdx.x);
-    if (ci < nchunks) v[t] = rc[ci];
-  }
-}
-
-__device__ __forceinline__ void acc_slice(const uint4 v[kTilesPerSlice], int c0, int nchunks, int V, float c,
-                                          RowAcc& a) {
-#pragma unroll
-  for (int t = 0; t < kTilesPerSlice; ++t) {
-    const int ci = c0 + t * kThreads + static_cast<int>(threadIdx.x);
-    if (ci < nchunks) {
-      float z[8];
-      unpack8(v[t], z, V - ci * kVec);
-      row_acc_add8(a, z, c);
-    }
-  }
-}
-
-__device__ __forceinline__ int draw_drafter(const Params& p, int b) { return p.mode == MODE_VERIFY ? 0 : p.sel[b]; }
-
-__device__ __forceinline__ unsigned long long dyn_desc(int type, int b, int k, int s) {
-  return (static_cast<unsigned long long>(type) << 56) | (static_cast<unsigned long long>(b) << 32) |
-         (static_cast<unsigned long long>(k) << 16) | static_cast<unsigned long long>(s);
-}
-
-// Thread 0: append a unit to the queue.  A slot past the capacity can only come from
-// counters that did not start at zero: it is not written, and the fault flag is set.
-__device__ __forceinline__ void publish(const Params& p, int type, int b, int k, int s) {
-  const uint32_t slot = ticket(&p.work[2]);
-  if (slot < static_cast<uint32_t>(p.queue_cap))
-    st_agent_u64(&p.queue[slot], dyn_desc(type, b, k, s));
-  else
-    st_agent(&p.work[3], 3u);
-}
-
-// Thread 0 after a sequence's final step: the last one resets the sequence's counters
-// (by then every other unit of the sequence has finished).
-__device__ __forceinline__ void finish_sequence(const Params& p, int b) {
-  const uint32_t old = ticket(&p.done[b]);
-  if (old == static_cast<uint32_t>(p.U3 - 1)) {
-    for (int k = 0; k <= p.K; ++k) st_agent(&p.p1cnt[b * (p.K + 1) + k], 0u);
-    st_agent(&p.p1all[b], 0u);
-    st_agent(&p.p2cnt[b], 0u);
-    st_agent(&p.p2gcnt[b], 0u);
-    st_agent(&p.done[b], 0u);
-  }
-}
-
-// A sequence's statistics are complete: take its decisions (block-wide), record
-// them, and publish its draw units.
-__device__ __forceinline__ void start_draws(const Params& p, int b, Lds& L) {
-  decide(p, b, draw_drafter(p, b), true, L.dl);
+// A sequence's last step: clear the statistics words it published.  Fused gamma
+// calls have two last steps (estimator and draw); the second one clears.
+__device__ __forceinline__ void finish_sequence(const Params& p, int b, Lds& L) {
+  stores_complete();
+  __syncthreads();
   if (threadIdx.x == 0) {
-    store_decision(p.dec + static_cast<size_t>(b) * kDecWords, L.dl.d);
-    stores_complete();
-    for (int s = 0; s < p.S; ++s) publish(p, DYN_DRAW, b, 0, s);
-  }
-}
-
-// Statistics unit: slices [j * kSlicesPerUnit, ...) of statistic row r of sequence b,
-// double-buffered.  Thread 0 issues the next claim once the first loads are out.
-__device__ __forceinline__ void unit_stats(const Params& p, int b, int r, int j, Lds& L, uint32_t* claim) {
-  const uint4* rc = as_chunks(stat_row(p, b, r));
-  const int nchunks = (p.V + kVec - 1) / kVec;
-  const int s0 = j * kSlicesPerUnit;
-  const int cnt = min(kSlicesPerUnit, p.S - s0);
-  uint4 va[kTilesPerSlice], vb[kTilesPerSlice];
-  RowAcc a = row_acc_init();
-  load_slice(rc, s0 * kSliceChunks, nchunks, va);
-  if (threadIdx.x == 0) *claim = ticket(&p.work[0]);
-#pragma unroll 1
-  for (int q = 0; q < cnt; q += 2) {
-    if (q + 1 < cnt) load_slice(rc, (s0 + q + 1) * kSliceChunks, nchunks, vb);
-    acc_slice(va, (s0 + q) * kSliceChunks, nchunks, p.V, p.c, a);
-    if (q + 1 < cnt) {
-      if (q + 2 < cnt) load_slice(rc, (s0 + q + 2) * kSliceChunks, nchunks, va);
-      acc_slice(vb, (s0 + q + 1) * kSliceChunks, nchunks, p.V, p.c, a);
+    int last = 1;
+    if (p.P2 > 1) {
+      last = ticket(&p.done[b]) == static_cast<uint32_t>(p.P2 - 1) ? 1 : 0;
+      if (last) st_agent(&p.done[b], 0u);
     }
-  }
-  const RowStats st = block_row_stats(a, L.scratch);
-  if (threadIdx.x == 0) {
-    const size_t idx = (static_cast<size_t>(b) * p.R + r) * p.Q + j;
-    st_agent(reinterpret_cast<uint32_t*>(p.stat_k + idx), __float_as_uint(st.k));
-    st_agent_d(p.stat_s + idx, st.s);
-    stores_complete();
-    int fl = 0;
-    if (p.mode == MODE_VERIFY) {
-      if (ticket(&p.p1cnt[b * (p.K + 1)]) == static_cast<uint32_t>(p.R * p.Q - 1)) fl |= 1;
-    } else {
-      if (r < p.K || r >= p.RT) {  // a row of position k < K: target row k or a drafter row
-        const int k = counter_of(p, r);
-        if (ticket(&p.p1cnt[b * (p.K + 1) + k]) == p1_target(p, k) - 1) {
-          for (int s = 0; s < p.S; ++s) publish(p, DYN_GAMMA, b, k, s);
-        }
-      }
-      if (p.fused && ticket(&p.p1all[b]) == static_cast<uint32_t>(p.R * p.Q - 1)) fl |= 1;
-    }
-    L.flag = fl;
+    L.flag = last;
   }
   __syncthreads();
-  if (L.flag & 1) start_draws(p, b, L);
+  if (L.flag) {
+    unsigned long long* w = part_row(p, b, 0);
+    const int n = p.R * p.S * kWaves;
+    for (int q = threadIdx.x; q < n; q += kThreads) st_agent_u64(w + q, 0ull);
+  }
+  __syncthreads();
 }
 
-// Last draw unit of a sequence: the inverse-CDF crossing and the output token.
-__device__ __forceinline__ void draw_final(const Params& p, int b, const Decision& d, Lds& L) {
+// Decision record: words 1..5 hold the weight context, word 0 (written last, once
+// the others have completed) the integer fields and the published bit.
+__device__ __forceinline__ void store_decision(unsigned long long* rec, const Decision& d) {
+  st_agent_u64(rec + 1, static_cast<unsigned long long>(__double_as_longlong(d.w.inv_st)));
+  st_agent_u64(rec + 2, static_cast<unsigned long long>(__double_as_longlong(d.w.inv_sd)));
+  st_agent_u64(rec + 3, static_cast<unsigned long long>(__double_as_longlong(d.w.s_scale)));
+  st_agent_u64(rec + 4, static_cast<unsigned long long>(__double_as_longlong(d.w.gstar)));
+  st_agent_u64(rec + 5, static_cast<unsigned long long>(__float_as_uint(d.w.kt)) |
+                            (static_cast<unsigned long long>(__float_as_uint(d.w.kd)) << 32));
+  stores_complete();
+  const unsigned long long head = static_cast<unsigned long long>(d.A + 1) |
+                                  (static_cast<unsigned long long>(d.draw_row) << 8) |
+                                  (static_cast<unsigned long long>(d.pair) << 16) |
+                                  (static_cast<unsigned long long>(d.w.special) << 17) |
+                                  (static_cast<unsigned long long>(d.w.mode) << 18) |
+                                  (static_cast<unsigned long long>(static_cast<uint32_t>(d.w.n + 1)) << 32) | kValid;
+  st_agent_u64(rec, head);
+}
+
+// Thread 0: wait for a decision record and decode it.  A timed-out wait gives an
+// invalid decision (A = -1).
+__device__ __forceinline__ Decision load_decision(const Params& p, unsigned long long* rec) {
+  Decision d;
+  const unsigned long long head = poll_word(p.flags, rec);
+  d.A = static_cast<int>(head & 0xffull) - 1;
+  d.draw_row = static_cast<int>((head >> 8) & 0xffull);
+  d.pair = static_cast<int>((head >> 16) & 1ull);
+  d.w.special = static_cast<int>((head >> 17) & 1ull);
+  d.w.mode = static_cast<int>((head >> 18) & 3ull);
+  d.w.n = static_cast<int>(static_cast<uint32_t>(head >> 32)) - 1;
+  d.w.c = p.c;
+  d.w.inv_st = __longlong_as_double(static_cast<long long>(ld_agent_u64(rec + 1)));
+  d.w.inv_sd = __longlong_as_double(static_cast<long long>(ld_agent_u64(rec + 2)));
+  d.w.s_scale = __longlong_as_double(static_cast<long long>(ld_agent_u64(rec + 3)));
+  d.w.gstar = __longlong_as_double(static_cast<long long>(ld_agent_u64(rec + 4)));
+  const unsigned long long kk = ld_agent_u64(rec + 5);
+  d.w.kt = __uint_as_float(static_cast<uint32_t>(kk));
+  d.w.kd = __uint_as_float(static_cast<uint32_t>(kk >> 32));
+  if (head == 0ull || d.A > p.K || d.draw_row > p.K || (d.pair && d.draw_row >= p.K)) d.A = -1;  // timed out
+  return d;
+}
+
+// Draw unit: the sequence's decisions, then the sub-tile masses of slice x of its
+// draw row(s).  Unit x = 0 also writes the per-position outputs and the decision
+// record.  A sequence with no valid draw publishes zero masses.
+__device__ __forceinline__ void unit_draw(const Params& p, int b, int x, Lds& L) {
+  decide(p, b, x == 0, L);
+  const Decision d = L.dl.d;
+  if (x == 0 && threadIdx.x == 0) store_decision(p.dec + static_cast<size_t>(b) * kDecWords, d);
+  unsigned long long* out = p.mass + static_cast<size_t>(b) * p.nsub;
+  const int t0 = x * kTilesPerSlice;
+  if (d.A >= 0) {
+    const uint16_t* trow = target_row(p, b, d.draw_row);
+    if (d.pair)
+      weight_subtiles<true, true, kTilesPerSlice>(trow, draft_row(p, b, draw_drafter(p, b), d.draw_row), p.V, d.w,
+                                                  t0, kTilesPerSlice, nullptr, out, p.nsub);
+    else
+      weight_subtiles<false, true, kTilesPerSlice>(trow, trow, p.V, d.w, t0, kTilesPerSlice, nullptr, out, p.nsub);
+  } else {
+    const int s = t0 * kWaves + threadIdx.x;
+    if (threadIdx.x < kTilesPerSlice * kWaves && s < p.nsub) st_agent_u64(out + s, pack_f64(0.0));
+  }
+  __syncthreads();
+}
+
+// Final step of a draw: the inverse-CDF crossing and the output token.
+__device__ __forceinline__ void unit_final(const Params& p, int b, Lds& L) {
+  const int tid = threadIdx.x;
+  unsigned long long* rec = p.dec + static_cast<size_t>(b) * kDecWords;
+  unsigned long long* msrc = p.mass + static_cast<size_t>(b) * p.nsub;
+  // the record and the masses are read together
+  if (tid == 0) L.dl.d = load_decision(p, rec);
+  unsigned long long w[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int q = tid + e * kThreads;
+    w[e] = 1ull;
+    if (q < p.nsub) w[e] = ld_agent_u64(msrc + q);
+  }
+  bool missing = false;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int q = tid + e * kThreads;
+    if (q < p.nsub) L.subsum[q] = unpack_f64(w[e]);
+    missing |= w[e] == 0ull;
+  }
+  if (missing) {  // not every mass was published yet (rare): read this thread's words again, waiting
+    for (int q = tid; q < p.nsub; q += kThreads) L.subsum[q] = unpack_f64(poll_word(p.flags, msrc + q));
+  }
+  __syncthreads();
+  const Decision d = L.dl.d;
   const bool ok = d.A >= 0;
   int token = -1;
   if (ok) {
-    for (int q = threadIdx.x; q < p.nsub; q += kThreads)
-      L.subsum[q] = ld_agent_d(p.subsum + static_cast<size_t>(b) * p.nsub + q);
-    __syncthreads();
     const uint16_t* trow = target_row(p, b, d.draw_row);
     const uint16_t* drow = d.pair ? draft_row(p, b, draw_drafter(p, b), d.draw_row) : trow;
     const double uu = static_cast<double>(p.u[b * (p.K + 1) + d.draw_row]);
@@ -644,7 +782,7 @@ __device__ __forceinline__ void draw_final(const Params& p, int b, const Decisio
       WeightCtx wh = d.w;
       wh.mode = W_TARGET_H;
       const int ntiles = (p.V + kTile - 1) / kTile;
-      weight_subtiles<false, false>(trow, trow, p.V, wh, 0, ntiles, L.subsum, p.nsub);
+      weight_subtiles<false, false, 4>(trow, trow, p.V, wh, 0, ntiles, L.subsum, nullptr, p.nsub);
       __syncthreads();
       if (wave_id() == 0) {
         int s_star = -1;
@@ -658,87 +796,25 @@ __device__ __forceinline__ void draw_final(const Params& p, int b, const Decisio
       token = L.flag;
     }
   }
-  if (threadIdx.x == 0) {
+  // every draw unit has published (all masses were read above): clear the masses and the record
+  for (int q = tid; q < p.nsub; q += kThreads) st_agent_u64(msrc + q, 0ull);
+  if (tid < kDecWords) st_agent_u64(rec + tid, 0ull);
+  if (tid == 0) {
     const bool good = ok && token >= 0;
     p.accepted_len[b] = good ? d.A : -1;
     p.out_token[b] = good ? token : -1;
-    finish_sequence(p, b);
   }
+  finish_sequence(p, b, L);
 }
 
-// Draw unit: sub-tile masses of slice s of sequence b's draw row(s).
-__device__ __forceinline__ void unit_draw(const Params& p, int b, int s, Lds& L) {
-  if (threadIdx.x == 0) {
-    Decision d = load_decision(p.dec + static_cast<size_t>(b) * kDecWords, p.c);
-    // a record is used only if it describes a draw row of this call
-    if (d.A < -1 || d.A > p.K || d.draw_row < 0 || d.draw_row > p.K || (d.pair && d.draw_row >= p.K)) {
-      d.A = -1;
-      st_agent(&p.work[3], 4u);
-    }
-    L.dl.d = d;
-  }
-  __syncthreads();
-  const Decision d = L.dl.d;
-  if (d.A >= 0) {
-    const uint16_t* trow = target_row(p, b, d.draw_row);
-    double* out = p.subsum + static_cast<size_t>(b) * p.nsub;
-    const int t0 = s * kTilesPerSlice;
-    if (d.pair)
-      weight_subtiles<true, true>(trow, draft_row(p, b, draw_drafter(p, b), d.draw_row), p.V, d.w, t0,
-                                  kTilesPerSlice, out, p.nsub);
-    else
-      weight_subtiles<false, true>(trow, trow, p.V, d.w, t0, kTilesPerSlice, out, p.nsub);
-  }
-  stores_complete();
-  __syncthreads();
-  if (threadIdx.x == 0) L.flag = ticket(&p.p2cnt[b]) == static_cast<uint32_t>(p.S - 1) ? 1 : 0;
-  __syncthreads();
-  if (L.flag) draw_final(p, b, d, L);
-}
-
-// Last gamma unit of a sequence: gamma, the estimator and the loss of every drafter.
-__device__ __forceinline__ void estimate(const Params& p, int b) {
+// Gamma unit: sum_x min(pt_k, pd_{i,k}) over slice x for every drafter i ([NB] Key design 1).
+__device__ __forceinline__ void unit_gamma(const Params& p, int b, int k, int x, Lds& L) {
   const int tid = threadIdx.x;
-  if (tid < p.N) {
-    const int i = tid, K = p.K;
-    // [NB] Key design 2 (reading: L = 1 + sum_k gamma_k prod_{j<k} a_j) and Key design 3 (f = K + 1 - L)
-    double Lh = 1.0, prod = 1.0;
-    for (int k = 0; k < K; ++k) {
-      double g = 0.0;
-      const size_t gi = ((static_cast<size_t>(b) * K + k) * p.N + i) * p.S;
-      for (int s = 0; s < p.S; ++s) g += ld_agent_d(p.gpart + gi + s);
-      p.gamma[(b * K + k) * p.N + i] = static_cast<float>(g);
-      Lh += g * prod;
-      if (k < K - 1) {
-        double a;
-        const int x = p.traj[b * K + k];
-        if (x < 0 || x >= p.V) {
-          a = __builtin_nan("");
-        } else {
-          const RowStats st = merge_row(p, b, k);
-          const RowStats sd = merge_row(p, b, p.RT + i * K + k);
-          const double ptx = token_prob(bf16_at(target_row(p, b, k), x), p.c, st);
-          const double pdx = token_prob(bf16_at(draft_row(p, b, i, k), x), p.c, sd);
-          a = ptx > 0.0 ? fmin(1.0, pdx / ptx) : (pdx > 0.0 ? 1.0 : 0.0);
-        }
-        prod *= a;
-      }
-    }
-    p.est_len[b * p.N + i] = static_cast<float>(Lh);
-    p.loss[b * p.N + i] = static_cast<float>(static_cast<double>(K + 1) - Lh);
-  }
-  __syncthreads();
-  if (tid == 0) finish_sequence(p, b);
-}
-
-// Gamma unit: sum_x min(pt_k, pd_{i,k}) over slice s for every drafter i.
-__device__ __forceinline__ void unit_gamma(const Params& p, int b, int k, int s, Lds& L) {
-  const int tid = threadIdx.x;
-  // log2 normalisers L = k + log2(s) of the target row and the N drafter rows
+  // rows: 0 the target row k, 1 + i drafter i's row k
+  merge_rows(p, b, p.N + 1, [&](int i) { return i == 0 ? k : p.RT + (i - 1) * p.K + k; }, L.m);
+  // log2 normalisers l = k + log2(s)
   if (tid <= p.N) {
-    const int r = tid == 0 ? k : p.RT + (tid - 1) * p.K + k;
-    const RowStats st = merge_row(p, b, r);
-    const float lv = static_cast<float>(static_cast<double>(st.k) + log2(st.s));
+    const float lv = static_cast<float>(static_cast<double>(L.m.rk[tid]) + log2(L.m.rs[tid]));
     if (tid == 0)
       L.lt = lv;
     else
@@ -749,10 +825,11 @@ __device__ __forceinline__ void unit_gamma(const Params& p, int b, int k, int s,
   const float c = p.c, lt = L.lt;
   const int nchunks = (p.V + kVec - 1) / kVec;
   const uint4* tr = as_chunks(target_row(p, b, k));
-  constexpr int kHalf = kTilesPerSlice / 2;
+  constexpr int kParts = 4;  // the slice is streamed in quarters to bound registers
+  constexpr int kHalf = kTilesPerSlice / kParts;
 #pragma unroll 1
-  for (int h = 0; h < 2; ++h) {
-    const int c0 = s * kSliceChunks + h * kHalf * kThreads;
+  for (int h = 0; h < kParts; ++h) {
+    const int c0 = x * kSliceChunks + h * kHalf * kThreads;
     uint4 vt[kHalf], vd[kHalf], vn[kHalf];
 #pragma unroll
     for (int t = 0; t < kHalf; ++t) {
@@ -797,116 +874,155 @@ __device__ __forceinline__ void unit_gamma(const Params& p, int b, int k, int s,
   if (tid < p.N) {
     double g = 0.0;
     for (int w = 0; w < kWaves; ++w) g += L.part[tid * kWaves + w];
-    st_agent_d(p.gpart + ((static_cast<size_t>(b) * p.K + k) * p.N + tid) * p.S + s, g);
+    st_agent_u64(p.gpart + ((static_cast<size_t>(b) * p.K + k) * p.N + tid) * p.S + x, pack_f64(g));
   }
-  stores_complete();
   __syncthreads();
-  if (tid == 0) L.flag = ticket(&p.p2gcnt[b]) == static_cast<uint32_t>(p.K * p.S - 1) ? 1 : 0;
-  __syncthreads();
-  if (L.flag) estimate(p, b);
 }
 
-// ---------------------------------------------------------------------------
-// The persistent kernel
-// ---------------------------------------------------------------------------
-
-#ifdef SPEC_TRACE
-// Diagnostic build only: per-unit timestamps (start, end) and workgroup.
-__device__ unsigned long long g_trace[1 << 17][3];
-#endif
-
-// Statistics unit h: sequence-major; within a sequence, verify rows in order, gamma rows
-// grouped by position (target row k, then every drafter's row k), the bonus row last.
-__device__ __forceinline__ void run_static(const Params& p, int h, Lds& L, uint32_t* claim) {
-  const int b = h / p.U1, loc = h % p.U1;
-  const int slot = loc / p.Q, j = loc % p.Q;
-  int r;
-  if (p.mode == MODE_VERIFY) {
-    r = slot;
-  } else if (slot < p.K * (1 + p.N)) {
-    const int k = slot / (1 + p.N), t = slot % (1 + p.N);
-    r = t == 0 ? k : p.RT + (t - 1) * p.K + k;
-  } else {
-    r = p.K;  // fused: target row K (bonus)
-  }
-  unit_stats(p, b, r, j, L, claim);
-}
-
-// SPEC_FLOW_WAVES_PER_EU (compile time) caps registers for that many waves per SIMD.
-#ifdef SPEC_FLOW_WAVES_PER_EU
-__global__ __launch_bounds__(kThreads, SPEC_FLOW_WAVES_PER_EU) void flow_kernel(Params p) {
-#else
-__global__ __launch_bounds__(kThreads) void flow_kernel(Params p) {
-#endif
-  __shared__ Lds L;
-  __shared__ int sh_unit;
-  if (threadIdx.x == 0) sh_unit = static_cast<int>(ticket(&p.work[0]));
-  __syncthreads();
-  int u = sh_unit;
-  while (u < p.total_units) {
-    __syncthreads();
-#ifdef SPEC_TRACE
-    const unsigned long long t_start = wall_clock64();
-#endif
-    uint32_t nxt = 0;
-    if (u < p.n_static) {
-      run_static(p, u, L, &nxt);
-    } else {
-      if (threadIdx.x == 0) {
-        nxt = ticket(&p.work[0]);
-        // a queue slot: wait until its unit is published (only when nothing else is left)
-        unsigned long long* slot = &p.queue[u - p.n_static];
-        unsigned long long d = ld_agent_u64(slot);
-        const unsigned long long t0 = wall_clock64();
-        while (d == 0ull) {
-          if (wall_clock64() - t0 > kWaitTicks) {
-            st_agent(&p.work[3], 1u);  // fault: a published unit never arrived
-            break;
-          }
-          __builtin_amdgcn_s_sleep(2);
-          d = ld_agent_u64(slot);
-        }
-        st_agent_u64(slot, 0ull);
-        L.desc = d;
-      }
-      __syncthreads();
-      const unsigned long long d = L.desc;
-      if (d != 0ull) {
-        const int type = static_cast<int>(d >> 56);
-        const int b = static_cast<int>((d >> 32) & 0xffffffull);
-        const int k = static_cast<int>((d >> 16) & 0xffffull);
-        const int s = static_cast<int>(d & 0xffffull);
-        // a descriptor is used only if every field is in range (a corrupt slot sets the fault flag)
-        const bool ok = b < p.B && s < p.S &&
-                        ((type == DYN_DRAW && (p.mode == MODE_VERIFY || p.fused)) ||
-                         (type == DYN_GAMMA && p.mode == MODE_GAMMA && k < p.K));
-        if (!ok) {
-          if (threadIdx.x == 0) st_agent(&p.work[3], 2u);
-        } else if (type == DYN_DRAW) {
-          unit_draw(p, b, s, L);
+// Estimator step of a sequence: gamma, the estimator and the loss of every drafter,
+// positions in chunks whose rows fit the LDS arrays.
+__device__ __forceinline__ void unit_estimate(const Params& p, int b, Lds& L) {
+  const int tid = threadIdx.x, K = p.K, N = p.N;
+  const int J = max(1, min(K, kRowCap / (N + 1)));
+  // [NB] Key design 2 (reading: L = 1 + sum_k gamma_k prod_{j<k} a_j) and Key design 3 (f = K + 1 - L)
+  double Lh = 1.0, prod = 1.0;
+  for (int k0 = 0; k0 < K; k0 += J) {
+    const int nk = min(J, K - k0);
+    // gamma of the chunk's (position, drafter) pairs: one pair per thread
+    if (tid < nk * N) {
+      const int kk = k0 + tid / N, i = tid % N;
+      unsigned long long* src = p.gpart + ((static_cast<size_t>(b) * K + kk) * N + i) * p.S;
+      double g = 0.0;
+      for (int x0 = 0; x0 < p.S; x0 += 8) {
+        unsigned long long w[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = x0 + e < p.S ? ld_agent_u64(src + x0 + e) : kValid;
+        bool missing = false;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) missing |= w[e] == 0ull;
+        if (missing) {  // not yet published (rare): wait for each word of the batch in turn
+          for (int e = 0; e < 8 && x0 + e < p.S; ++e) g += unpack_f64(poll_word(p.flags, src + x0 + e));
         } else {
-          unit_gamma(p, b, k, s, L);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) g += unpack_f64(w[e]);
         }
+      }
+      L.gsum[tid] = g;
+      p.gamma[(b * K + kk) * N + i] = static_cast<float>(g);
+    }
+    // statistics of the chunk's rows: (target kk, drafter 0 kk, ..., drafter N-1 kk)
+    merge_rows(p, b, nk * (N + 1),
+               [&](int i) {
+                 const int kk = k0 + i / (N + 1), m = i % (N + 1);
+                 return m == 0 ? kk : p.RT + (m - 1) * K + kk;
+               },
+               L.m);
+    // realised-token acceptance a = min(1, pd(x)/pt(x)) at x = traj[kk]
+    if (tid < nk * N) {
+      const int kl = tid / N, i = tid % N, kk = k0 + kl;
+      double a = 1.0;
+      if (kk < K - 1) {
+        const int x = p.traj[b * K + kk];
+        if (x < 0 || x >= p.V) {
+          a = __builtin_nan("");
+        } else {
+          const RowStats st{L.m.rk[kl * (N + 1)], L.m.rs[kl * (N + 1)]};
+          const RowStats sd{L.m.rk[kl * (N + 1) + 1 + i], L.m.rs[kl * (N + 1) + 1 + i]};
+          const double ptx = token_prob(bf16_at(target_row(p, b, kk), x), p.c, st);
+          const double pdx = token_prob(bf16_at(draft_row(p, b, i, kk), x), p.c, sd);
+          a = ptx > 0.0 ? fmin(1.0, pdx / ptx) : (pdx > 0.0 ? 1.0 : 0.0);
+        }
+      }
+      L.arat[tid] = a;
+    }
+    __syncthreads();
+    if (tid < N) {
+      for (int kl = 0; kl < nk; ++kl) {
+        Lh += L.gsum[kl * N + tid] * prod;
+        prod *= L.arat[kl * N + tid];
       }
     }
     __syncthreads();
-#ifdef SPEC_TRACE
-    if (threadIdx.x == 0 && u < (1 << 17)) {
-      g_trace[u][0] = t_start;
-      g_trace[u][1] = wall_clock64();
-      g_trace[u][2] = blockIdx.x;
-    }
-#endif
-    if (threadIdx.x == 0) sh_unit = static_cast<int>(nxt);
-    __syncthreads();
-    u = sh_unit;
   }
-  if (threadIdx.x == 0) {
-    if (ticket(&p.work[1]) == gridDim.x - 1) {  // every other workgroup has left
-      st_agent(&p.work[0], 0u);
-      st_agent(&p.work[1], 0u);
-      st_agent(&p.work[2], 0u);
+  if (tid < N) {
+    p.est_len[b * N + tid] = static_cast<float>(Lh);
+    p.loss[b * N + tid] = static_cast<float>(static_cast<double>(K + 1) - Lh);
+  }
+  // every gamma unit of the sequence has published (all were read above): clear them
+  unsigned long long* gw = p.gpart + static_cast<size_t>(b) * K * N * p.S;
+  for (int q = tid; q < K * N * p.S; q += kThreads) st_agent_u64(gw + q, 0ull);
+  finish_sequence(p, b, L);
+}
+
+// ---------------------------------------------------------------------------
+// The kernel
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void run_unit1(const Params& p, int u, Lds& L) {
+  const int b = u / p.P1;
+  const int l = u - b * p.P1;
+  if (p.mode == MODE_GAMMA && l < p.K * p.S)
+    unit_gamma(p, b, l / p.S, l % p.S, L);
+  else
+    unit_draw(p, b, p.mode == MODE_GAMMA ? l - p.K * p.S : l, L);
+}
+
+__device__ __forceinline__ void run_unit2(const Params& p, int v, Lds& L) {
+  const int b = v / p.P2;
+  const int kind = v - b * p.P2;
+  if (p.mode == MODE_GAMMA && kind == 0)
+    unit_estimate(p, b, L);
+  else
+    unit_final(p, b, L);
+}
+
+// Phase 0: workgroup g streams statistics slices g, g + G, g + 2G, ... of the
+// sequence-major slice list, with the next slice's loads in flight while the
+// current one is reduced.
+__device__ __forceinline__ void static_phase(const Params& p) {
+  const int G = gridDim.x, g = blockIdx.x, T0 = p.total0;
+  uint4 va[kTilesPerSlice], vb[kTilesPerSlice];
+  int sig = g;
+  SliceLoc la{}, lb{};
+  if (sig < T0) {
+    la = slice_loc(p, sig);
+    slice_load(p, la, va);
+  }
+  while (sig < T0) {
+    const int s1 = sig + G;
+    if (s1 < T0) {
+      lb = slice_loc(p, s1);
+      slice_load(p, lb, vb);
     }
+    slice_finish(p, la, va);
+    if (s1 >= T0) break;
+    const int s2 = s1 + G;
+    if (s2 < T0) {
+      la = slice_loc(p, s2);
+      slice_load(p, la, va);
+    }
+    slice_finish(p, lb, vb);
+    sig = s2;
+  }
+}
+
+// Phase 0 (static_phase), then phase 1 and phase 2: units g, g + G, ... of each
+// list.  A phase-1 unit waits only for phase-0 words and a phase-2 unit only for
+// phase-0 and phase-1 words, and every workgroup finishes a phase before it
+// starts the next, so every wait ends.
+__global__ __launch_bounds__(kThreads) void flow_kernel(Params p) {
+  __shared__ Lds L;
+  const int G = gridDim.x, g = blockIdx.x;
+  static_phase(p);
+  const int T1 = p.B * p.P1;
+  for (int u = g; u < T1; u += G) {
+    __syncthreads();
+    run_unit1(p, u, L);
+  }
+  const int T2 = p.B * p.P2;
+  for (int v = g; v < T2; v += G) {
+    __syncthreads();
+    run_unit2(p, v, L);
   }
 }
 
@@ -986,8 +1102,8 @@ __global__ void fill_zero_kernel(uint32_t* p, size_t n) {
 
 struct Shape {
   int B, K, N, V, mode, fused;
-  int R, RT, S, Q, nsub, U1, U3;
-  int64_t n_static, n_dyn;
+  int R, RT, S, nsub, P1, P2;
+  int64_t RS, total0;  // checked below 2^31 before a launch
 };
 
 static Shape make_shape(int B, int K, int N, int V, int mode, int fused) {
@@ -1001,61 +1117,38 @@ static Shape make_shape(int B, int K, int N, int V, int mode, int fused) {
   s.RT = mode == MODE_VERIFY ? K + 1 : K + fused;
   s.R = s.RT + N * K;
   s.S = (V + kSliceTok - 1) / kSliceTok;
-  s.Q = (s.S + kSlicesPerUnit - 1) / kSlicesPerUnit;
   s.nsub = (V + kSub - 1) / kSub;
-  s.U1 = s.R * s.Q;
-  s.U3 = mode == MODE_VERIFY ? 1 : 1 + fused;
-  s.n_static = static_cast<int64_t>(B) * s.U1;
-  const int64_t dyn_per_seq = mode == MODE_VERIFY ? s.S : static_cast<int64_t>(K) * s.S + (fused ? s.S : 0);
-  s.n_dyn = static_cast<int64_t>(B) * dyn_per_seq;
+  s.P1 = mode == MODE_VERIFY ? s.S : K * s.S + (fused ? s.S : 0);
+  s.P2 = mode == MODE_VERIFY ? 1 : 1 + fused;
+  s.RS = static_cast<int64_t>(s.R) * s.S;
+  s.total0 = static_cast<int64_t>(B) * s.RS;
   return s;
 }
 
+// Byte offsets of the workspace regions.  They depend on (B, K, N, mode) only
+// (every region is sized for the longest row), so one workspace serves every V.
 struct WsLayout {
-  size_t work, p1cnt, p1all, p2cnt, p2gcnt, done, queue, zero_end, stat_k, stat_s, subsum, gpart, dec, total;
+  size_t flags, done, dec, part, mass, gpart, total;
 };
-
-// Queue slots one call can publish at most: B * (K + 1) * (slices of the longest row)
-// covers B * S draw units and B * K * S gamma units for any V.
-static size_t queue_capacity(int B, int K) {
-  return static_cast<size_t>(B) * (static_cast<size_t>(K) + 1) * kMaxSlices;
-}
 
 static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// Counters first (they must read zero at launch), scratch after them.
 static WsLayout ws_layout(const Shape& s) {
   WsLayout L;
-  const size_t B = static_cast<size_t>(s.B), K1 = static_cast<size_t>(s.K) + 1;
-  const size_t cells = B * static_cast<size_t>(s.R) * static_cast<size_t>(s.Q);
+  const size_t B = static_cast<size_t>(s.B);
   size_t o = 0;
-  L.work = o;
+  L.flags = o;
   o = align256(o + 16);
-  L.p1cnt = o;
-  o = align256(o + 4 * B * K1);
-  L.p1all = o;
-  o = align256(o + 4 * B);
-  L.p2cnt = o;
-  o = align256(o + 4 * B);
-  L.p2gcnt = o;
-  o = align256(o + 4 * B);
   L.done = o;
   o = align256(o + 4 * B);
-  L.queue = o;  // slots are zero between calls, like the counters
-  o = align256(o + 8 * queue_capacity(s.B, s.K));
-  // Everything before zero_end must read zero at launch; it depends on B and K only,
-  // so a workspace can serve any V without being cleared again.
-  L.zero_end = o;
-  L.stat_k = o;
-  o = align256(o + 4 * cells);
-  L.stat_s = o;
-  o = align256(o + 8 * cells);
-  L.subsum = o;
-  o = align256(o + 8 * B * static_cast<size_t>(s.nsub));
-  L.gpart = o;
-  o = align256(o + (s.mode == MODE_GAMMA ? 8 * B * s.K * s.N * s.S : 0));
   L.dec = o;
   o = align256(o + 8 * B * kDecWords);
+  L.part = o;
+  o = align256(o + 8 * B * static_cast<size_t>(s.R) * kMaxSlices * kWaves);
+  L.mass = o;
+  o = align256(o + 8 * B * static_cast<size_t>(kMaxSub));
+  L.gpart = o;
+  o = align256(o + (s.mode == MODE_GAMMA ? 8 * B * static_cast<size_t>(s.K) * s.N * kMaxSlices : 0));
   L.total = o;
   return L;
 }
@@ -1067,21 +1160,13 @@ static int bind_workspace(Params& p, const Shape& s, void* ws, size_t bytes) {
   if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return SPEC_ERR_WORKSPACE;
   const WsLayout L = ws_layout(s);
   if (bytes < L.total) return SPEC_ERR_WORKSPACE;
-  if (static_cast<size_t>(s.n_dyn) > queue_capacity(s.B, s.K)) return SPEC_ERR_SHAPE;
-  p.queue_cap = static_cast<int>(queue_capacity(s.B, s.K));
   char* base = static_cast<char*>(ws);
-  p.work = reinterpret_cast<uint32_t*>(base + L.work);
-  p.p1cnt = reinterpret_cast<uint32_t*>(base + L.p1cnt);
-  p.p1all = reinterpret_cast<uint32_t*>(base + L.p1all);
-  p.p2cnt = reinterpret_cast<uint32_t*>(base + L.p2cnt);
-  p.p2gcnt = reinterpret_cast<uint32_t*>(base + L.p2gcnt);
+  p.flags = reinterpret_cast<uint32_t*>(base + L.flags);
   p.done = reinterpret_cast<uint32_t*>(base + L.done);
-  p.queue = reinterpret_cast<unsigned long long*>(base + L.queue);
-  p.stat_k = reinterpret_cast<float*>(base + L.stat_k);
-  p.stat_s = reinterpret_cast<double*>(base + L.stat_s);
-  p.subsum = reinterpret_cast<double*>(base + L.subsum);
-  p.gpart = reinterpret_cast<double*>(base + L.gpart);
-  p.dec = reinterpret_cast<double*>(base + L.dec);
+  p.dec = reinterpret_cast<unsigned long long*>(base + L.dec);
+  p.part = reinterpret_cast<unsigned long long*>(base + L.part);
+  p.mass = reinterpret_cast<unsigned long long*>(base + L.mass);
+  p.gpart = reinterpret_cast<unsigned long long*>(base + L.gpart);
   return SPEC_OK;
 }
 
@@ -1099,25 +1184,25 @@ static int resident_workgroups() {
   return g;
 }
 
-// Statistics units first (in claim order), then one queue slot per published unit.
 static void plan_units(Params& p, const Shape& s) {
   p.R = s.R;
   p.RT = s.RT;
   p.S = s.S;
-  p.Q = s.Q;
   p.nsub = s.nsub;
-  p.U1 = s.U1;
-  p.U3 = s.U3;
-  p.n_static = static_cast<int>(s.n_static);
-  p.total_units = static_cast<int>(s.n_static + s.n_dyn);
+  p.P1 = s.P1;
+  p.P2 = s.P2;
+  p.RS = static_cast<int>(s.RS);
+  p.total0 = static_cast<int>(s.total0);
 }
 
 static int launch_flow(Params& p, const Shape& s, hipStream_t stream) {
-  const int64_t total = s.n_static + s.n_dyn;
-  if (total > 0x3fffffffLL) return SPEC_ERR_SHAPE;
+  // a slice is 32 KB of logits, so 2^31 slices exceed any device's memory; the
+  // limit keeps the schedule in 32-bit arithmetic (with room for j * G + g)
+  if (s.total0 > 0x3fffffffLL || static_cast<int64_t>(s.B) * s.P1 > 0x3fffffffLL) return SPEC_ERR_SHAPE;
   int grid = resident_workgroups();
   if (grid <= 0) return SPEC_ERR_HIP;
-  if (grid > total) grid = static_cast<int>(total);
+  // every workgroup is resident at once (the schedule's waits rely on it)
+  if (grid > s.total0) grid = static_cast<int>(s.total0);
   plan_units(p, s);
   hipLaunchKernelGGL(flow_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
@@ -1187,14 +1272,8 @@ const char* spec_status_str(int status) {
   }
 }
 
-size_t spec_workspace_counter_bytes(int B, int K) {
-  if (B < 1 || K < 1 || K > SPEC_MAX_K || B > SPEC_MAX_B) return 0;
-  return ws_layout(make_shape(B, K, 1, 1, MODE_VERIFY, 0)).zero_end;
-}
-
 size_t spec_workspace_bytes(int B, int K, int N) {
   if (B < 1 || K < 1 || N < 1 || K > SPEC_MAX_K || N > SPEC_MAX_N || B > SPEC_MAX_B) return 0;
-  // the layout grows with V: size it for the largest vocabulary a call may use
   const size_t v = ws_layout(make_shape(B, K, 1, SPEC_MAX_V, MODE_VERIFY, 0)).total;
   const size_t g = ws_layout(make_shape(B, K, N, SPEC_MAX_V, MODE_GAMMA, 1)).total;
   return v > g ? v : g;

@@ -1,7 +1,8 @@
 // Host-only check of the workspace layout of libspecverify (no GPU is touched):
-// for every (B, K, N, V, mode) the zero region (counters + queue) ends at the same
-// offset for a given (B, K), holds every unit one call can publish, and the whole
-// layout fits in spec_workspace_bytes(B, K, N).
+// for every (B, K, N, V, mode) the regions a call indexes with its own slice and
+// sub-tile counts stay inside their region, the regions do not overlap, the
+// fault word lies in the flags region, and the layout fits in
+// spec_workspace_bytes(B, K, N), whatever V is.
 #include "spec_verify.hip"
 #include <cstdio>
 
@@ -13,8 +14,7 @@ int main() {
   const int Vs[] = {1, 3, 7, 8, 9, 511, 513, 2048, 9000, 16384, 16385, 32000, 40000, 65536, 128256, 151936,
                     1000003, 1 << 20};
   for (int B : Bs)
-    for (int K : Ks) {
-      const size_t zero = spec_workspace_counter_bytes(B, K);
+    for (int K : Ks)
       for (int N : Ns) {
         const size_t total = spec_workspace_bytes(B, K, N);
         for (int V : Vs)
@@ -24,18 +24,21 @@ int main() {
               const Shape s = make_shape(B, K, N, V, mode, fused);
               const WsLayout L = ws_layout(s);
               ++checked;
-              const bool ok = L.zero_end == zero && L.queue + 8 * static_cast<size_t>(s.n_dyn) <= L.zero_end &&
-                              L.total <= total && L.stat_k >= L.zero_end && L.subsum >= L.stat_k &&
-                              L.dec + 8 * static_cast<size_t>(B) * kDecWords <= L.total;
+              const size_t part_words = static_cast<size_t>(B) * s.R * s.S * kWaves;
+              const size_t gpart_words = mode == MODE_GAMMA ? static_cast<size_t>(B) * K * N * s.S : 0;
+              const bool ok = L.flags == 0 && L.done >= 16 && L.done + 4 * static_cast<size_t>(B) <= L.part &&
+                              L.part + 8 * part_words <= L.mass &&
+                              L.mass + 8 * static_cast<size_t>(B) * s.nsub <= L.gpart &&
+                              L.gpart + 8 * gpart_words <= L.total && L.total <= total && s.nsub <= kMaxSub &&
+                              s.S <= kMaxSlices;
               if (!ok) {
                 ++bad;
                 if (bad < 10)
-                  printf("layout violation B=%d K=%d N=%d V=%d mode=%d fused=%d zero_end=%zu/%zu total=%zu/%zu\n", B,
-                         K, N, V, mode, fused, L.zero_end, zero, L.total, total);
+                  printf("layout violation B=%d K=%d N=%d V=%d mode=%d fused=%d total=%zu/%zu\n", B, K, N, V, mode,
+                         fused, L.total, total);
               }
             }
       }
-    }
   printf("checked %d layouts, %d violations\n", checked, bad);
   return bad ? 1 : 0;
 }

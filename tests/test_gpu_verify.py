@@ -214,6 +214,11 @@ def test_repeat_deterministic_one_workspace(B):
     y = sps_case(16, 5, 40000, seed=20)
     got = run_verify(B, y, ws=ws)
     compare_verify(oracle_verify(y), *got[:3], "same workspace, V=40000")
+    # every call leaves the workspace zero: a smaller B and K reuse it without clearing
+    z = sps_case(8, 3, 20000, seed=21)
+    got = run_verify(B, z, ws=ws)
+    compare_verify(oracle_verify(z), *got[:3], "same workspace, B=8 K=3")
+    assert int(ws.count_nonzero().item()) == 0
 
 
 # ---------------------------------------------------------------------------
