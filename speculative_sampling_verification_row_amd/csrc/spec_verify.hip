@@ -64,16 +64,18 @@ constexpr int kRowCap = 256;          // merged rows held in LDS at once
 constexpr int kNoK = INT32_MIN;       // statistics word of a share with no finite logit
 constexpr int kDecWords = 6;          // words of a decision record
 
-// Everything a lane needs to turn logits into sampling weights (fp64).
+// Everything a lane needs to turn logits into sampling weights.  Weights are kept
+// in units of 1/st (st the target row's sum): an inverse-CDF draw depends only on
+// ratios of weights, so the target normaliser never has to be applied per token.
 struct WeightCtx {
   float c;
-  float kt, kd;           // row references
-  double inv_st, inv_sd;  // 1 / row sums
-  double s_scale;         // Cactus rescale s of the non-candidate tokens (1.0 for SpS)
-  double gstar;           // Cactus gamma* (the candidate's target mass)
-  int n;                  // candidate token
-  int special;            // 1: token n carries gamma* (delta > 0)
-  int mode;               // W_RESID, W_TARGET_H, W_TARGET
+  float kt, kd;    // row references
+  double r;        // st / sd: a draft term 2^(zd c - kd) in units of 1/st
+  double s_scale;  // Cactus rescale s of the non-candidate tokens (1.0 for SpS)
+  double hn;       // Cactus gamma* * st: the candidate's h in units of 1/st
+  int n;           // candidate token
+  int special;     // 1: token n carries gamma* (delta > 0)
+  int mode;        // W_RESID, W_TARGET_H, W_TARGET
 };
 
 struct Params {
@@ -320,25 +322,29 @@ __device__ __forceinline__ void merge_rows(const Params& p, int b, int nrows, Ro
 // Sampling weights, sub-tile search and token search
 // ---------------------------------------------------------------------------
 
-// Sampling weight of one token:
+// Sampling weight of one token in units of 1/st, with MODE and SPECIAL (Cactus's
+// candidate rule, delta > 0) fixed at compile time so that a lane's tokens form
+// straight-line code the scheduler can interleave:
 //   W_RESID    (h - pd)+ with h = s * pt, h_n = gamma*   ([LT] §2.2 / [CA] Key design 2)
 //   W_TARGET_H h          (a rejection with zero residual mass)
 //   W_TARGET   pt         (bonus token)
+// Without SPECIAL, h = pt (s = 1 exactly when delta = 0).
+template <int MODE, bool SPECIAL>
 __device__ __forceinline__ double weight1(const WeightCtx& w, float zt, float zd, int tok) {
-  const double pt = static_cast<double>(fast_exp2(fmaf(zt, w.c, -w.kt))) * w.inv_st;
-  if (w.mode == W_TARGET) return pt;
-  double h = w.s_scale * pt;
-  if (w.special && tok == w.n) h = w.gstar;
-  if (w.mode == W_TARGET_H) return h;
-  const double pd = static_cast<double>(fast_exp2(fmaf(zd, w.c, -w.kd))) * w.inv_sd;
-  return fmax(h - pd, 0.0);
+  const double et = static_cast<double>(fast_exp2(fmaf(zt, w.c, -w.kt)));
+  if (MODE == W_TARGET) return et;
+  const double h = SPECIAL ? (tok == w.n ? w.hn : w.s_scale * et) : et;
+  if (MODE == W_TARGET_H) return h;
+  const double ed = static_cast<double>(fast_exp2(fmaf(zd, w.c, -w.kd)));
+  return fmax(fma(-w.r, ed, h), 0.0);
 }
 
 // Weights of eight consecutive tokens starting at `tok0`.
+template <int MODE, bool SPECIAL>
 __device__ __forceinline__ void weights8(const WeightCtx& w, const float zt[8], const float zd[8], int tok0,
                                          double out[8]) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) out[e] = weight1(w, zt[e], zd[e], tok0 + e);
+  for (int e = 0; e < 8; ++e) out[e] = weight1<MODE, SPECIAL>(w, zt[e], zd[e], tok0 + e);
 }
 
 // Wave 0: the sub-tile holding the crossing of x = u * Z, Z = sum of subsum[].
@@ -403,7 +409,7 @@ __device__ __forceinline__ bool find_subtile(const double* subsum, int nsub, dou
 // Wave 0: the token in sub-tile s_star where the running mass passes x_rel
 // (or the sub-tile's last positive-mass token when x_rel is +inf).  Recomputes
 // the sub-tile's weights and lane scan exactly as the draw pass did.
-template <bool PAIR>
+template <int MODE, bool SPECIAL>
 __device__ __forceinline__ int find_token(const uint16_t* trow, const uint16_t* drow, int V, const WeightCtx& w,
                                           int s_star, double x_rel) {
   const int lane = lane_id();
@@ -415,12 +421,12 @@ __device__ __forceinline__ int find_token(const uint16_t* trow, const uint16_t* 
     const int valid = V - ci * kVec;
     float zt[8], zd[8];
     unpack8(as_chunks(trow)[ci], zt, valid);
-    if (PAIR)
+    if (MODE == W_RESID)
       unpack8(as_chunks(drow)[ci], zd, valid);
     else
 #pragma unroll
       for (int e = 0; e < 8; ++e) zd[e] = -__builtin_inff();
-    weights8(w, zt, zd, ci * kVec, wv);
+    weights8<MODE, SPECIAL>(w, zt, zd, ci * kVec, wv);
 #pragma unroll
     for (int e = 0; e < 8; ++e) ls += wv[e];
   }
@@ -460,7 +466,7 @@ __device__ __forceinline__ int find_token(const uint16_t* trow, const uint16_t* 
 // Per-sub-tile masses of the sampling weights over tiles [t0, t0 + ntiles) of a
 // row (pair); lane 63 of each wave holds the sub-tile's inclusive scan total.
 // A draw slice publishes them (TO_GLOBAL); the whole-row fallback keeps them in LDS.
-template <bool PAIR, bool TO_GLOBAL, int kBatch>
+template <int MODE, bool SPECIAL, bool TO_GLOBAL, int kBatch>
 __device__ __forceinline__ void weight_subtiles(const uint16_t* trow, const uint16_t* drow, int V, const WeightCtx& w,
                                                 int t0, int ntiles, double* lds_sub, unsigned long long* glob_sub,
                                                 int nsub) {
@@ -476,7 +482,7 @@ __device__ __forceinline__ void weight_subtiles(const uint16_t* trow, const uint
       const int ci = (t0 + j0 + q) * kThreads + tid;
       if (j0 + q < ntiles && ci < nchunks) {
         vt[q] = tr[ci];
-        if (PAIR) vd[q] = dr[ci];
+        if (MODE == W_RESID) vd[q] = dr[ci];
       }
     }
 #pragma unroll
@@ -489,14 +495,16 @@ __device__ __forceinline__ void weight_subtiles(const uint16_t* trow, const uint
         const int valid = V - ci * kVec;
         float zt[8], zd[8];
         unpack8(vt[q], zt, valid);
-        if (PAIR)
+        if (MODE == W_RESID)
           unpack8(vd[q], zd, valid);
         else
 #pragma unroll
           for (int e = 0; e < 8; ++e) zd[e] = -__builtin_inff();
         // same element order as find_token's lane sum, so the two agree bit for bit
+        double wv[8];
+        weights8<MODE, SPECIAL>(w, zt, zd, ci * kVec, wv);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) lsum += weight1(w, zt[e], zd[e], ci * kVec + e);
+        for (int e = 0; e < 8; ++e) lsum += wv[e];
       }
       const double incl = wave_incl_scan(lsum);
       const int s = jt * kWaves + wave_id();
@@ -599,9 +607,9 @@ __device__ __forceinline__ void decide(const Params& p, int b, bool write_output
     WeightCtx w;
     w.c = p.c;
     w.kd = 0.0f;
-    w.inv_sd = 1.0;
+    w.r = 0.0;
     w.s_scale = 1.0;
-    w.gstar = 0.0;
+    w.hn = 0.0;
     w.n = -1;
     w.special = 0;
     if (bad) {
@@ -610,7 +618,6 @@ __device__ __forceinline__ void decide(const Params& p, int b, bool write_output
       d.pair = 0;
       w.mode = W_TARGET;
       w.kt = 0.0f;
-      w.inv_st = 1.0;
     } else if (A < K) {
       // [LT] §9.1: the first rejection A is resampled from the residual of its row pair
       const double ct = L.dl.ct[A], gs = L.dl.gs[A];
@@ -619,11 +626,10 @@ __device__ __forceinline__ void decide(const Params& p, int b, bool write_output
       d.pair = 1;
       w.mode = W_RESID;
       w.kt = L.m.rk[A];
-      w.inv_st = 1.0 / L.m.rs[A];
       w.kd = L.m.rk[K + 1 + A];
-      w.inv_sd = 1.0 / L.m.rs[K + 1 + A];
+      w.r = L.m.rs[A] / L.m.rs[K + 1 + A];
       w.s_scale = ct < 1.0 ? (1.0 - gs) / (1.0 - ct) : 0.0;  // [CA] Key design 2 (1.0 exactly at delta = 0)
-      w.gstar = gs;
+      w.hn = gs * L.m.rs[A];
       w.n = p.tokens[b * K + A];
       w.special = p.delta > 0.0 ? 1 : 0;
     } else {
@@ -633,7 +639,6 @@ __device__ __forceinline__ void decide(const Params& p, int b, bool write_output
       d.pair = 0;
       w.mode = W_TARGET;
       w.kt = L.m.rk[K];
-      w.inv_st = 1.0 / L.m.rs[K];
     }
     d.w = w;
     L.dl.d = d;
@@ -670,10 +675,10 @@ __device__ __forceinline__ void finish_sequence(const Params& p, int b, Lds& L) 
 // Decision record: words 1..5 hold the weight context, word 0 (written last, once
 // the others have completed) the integer fields and the published bit.
 __device__ __forceinline__ void store_decision(unsigned long long* rec, const Decision& d) {
-  st_agent_u64(rec + 1, static_cast<unsigned long long>(__double_as_longlong(d.w.inv_st)));
-  st_agent_u64(rec + 2, static_cast<unsigned long long>(__double_as_longlong(d.w.inv_sd)));
-  st_agent_u64(rec + 3, static_cast<unsigned long long>(__double_as_longlong(d.w.s_scale)));
-  st_agent_u64(rec + 4, static_cast<unsigned long long>(__double_as_longlong(d.w.gstar)));
+  st_agent_u64(rec + 1, static_cast<unsigned long long>(__double_as_longlong(d.w.r)));
+  st_agent_u64(rec + 2, static_cast<unsigned long long>(__double_as_longlong(d.w.s_scale)));
+  st_agent_u64(rec + 3, static_cast<unsigned long long>(__double_as_longlong(d.w.hn)));
+  st_agent_u64(rec + 4, 0ull);
   st_agent_u64(rec + 5, static_cast<unsigned long long>(__float_as_uint(d.w.kt)) |
                             (static_cast<unsigned long long>(__float_as_uint(d.w.kd)) << 32));
   stores_complete();
@@ -698,10 +703,9 @@ __device__ __forceinline__ Decision load_decision(const Params& p, unsigned long
   d.w.mode = static_cast<int>((head >> 18) & 3ull);
   d.w.n = static_cast<int>(static_cast<uint32_t>(head >> 32)) - 1;
   d.w.c = p.c;
-  d.w.inv_st = __longlong_as_double(static_cast<long long>(ld_agent_u64(rec + 1)));
-  d.w.inv_sd = __longlong_as_double(static_cast<long long>(ld_agent_u64(rec + 2)));
-  d.w.s_scale = __longlong_as_double(static_cast<long long>(ld_agent_u64(rec + 3)));
-  d.w.gstar = __longlong_as_double(static_cast<long long>(ld_agent_u64(rec + 4)));
+  d.w.r = __longlong_as_double(static_cast<long long>(ld_agent_u64(rec + 1)));
+  d.w.s_scale = __longlong_as_double(static_cast<long long>(ld_agent_u64(rec + 2)));
+  d.w.hn = __longlong_as_double(static_cast<long long>(ld_agent_u64(rec + 3)));
   const unsigned long long kk = ld_agent_u64(rec + 5);
   d.w.kt = __uint_as_float(static_cast<uint32_t>(kk));
   d.w.kd = __uint_as_float(static_cast<uint32_t>(kk >> 32));
@@ -720,11 +724,16 @@ __device__ __forceinline__ void unit_draw(const Params& p, int b, int x, Lds& L)
   const int t0 = x * kTilesPerSlice;
   if (d.A >= 0) {
     const uint16_t* trow = target_row(p, b, d.draw_row);
-    if (d.pair)
-      weight_subtiles<true, true, kTilesPerSlice>(trow, draft_row(p, b, draw_drafter(p, b), d.draw_row), p.V, d.w,
-                                                  t0, kTilesPerSlice, nullptr, out, p.nsub);
+    const uint16_t* drow = d.pair ? draft_row(p, b, draw_drafter(p, b), d.draw_row) : trow;
+    if (!d.pair)
+      weight_subtiles<W_TARGET, false, true, kTilesPerSlice>(trow, drow, p.V, d.w, t0, kTilesPerSlice, nullptr, out,
+                                                             p.nsub);
+    else if (d.w.special)
+      weight_subtiles<W_RESID, true, true, kTilesPerSlice>(trow, drow, p.V, d.w, t0, kTilesPerSlice, nullptr, out,
+                                                           p.nsub);
     else
-      weight_subtiles<false, true, kTilesPerSlice>(trow, trow, p.V, d.w, t0, kTilesPerSlice, nullptr, out, p.nsub);
+      weight_subtiles<W_RESID, false, true, kTilesPerSlice>(trow, drow, p.V, d.w, t0, kTilesPerSlice, nullptr, out,
+                                                            p.nsub);
   } else {
     const int s = t0 * kWaves + threadIdx.x;
     if (threadIdx.x < kTilesPerSlice * kWaves && s < p.nsub) st_agent_u64(out + s, pack_f64(0.0));
@@ -770,8 +779,9 @@ __device__ __forceinline__ void unit_final(const Params& p, int b, Lds& L) {
       const bool found = find_subtile(L.subsum, p.nsub, uu, s_star, x_rel);
       int tok = -2;  // -2: no mass (zero residual)
       if (found)
-        tok = d.pair ? find_token<true>(trow, drow, p.V, d.w, s_star, x_rel)
-                     : find_token<false>(trow, drow, p.V, d.w, s_star, x_rel);
+        tok = !d.pair        ? find_token<W_TARGET, false>(trow, drow, p.V, d.w, s_star, x_rel)
+              : d.w.special ? find_token<W_RESID, true>(trow, drow, p.V, d.w, s_star, x_rel)
+                            : find_token<W_RESID, false>(trow, drow, p.V, d.w, s_star, x_rel);
       if (lane_id() == 0) L.flag = tok;
     }
     __syncthreads();
@@ -782,14 +792,18 @@ __device__ __forceinline__ void unit_final(const Params& p, int b, Lds& L) {
       WeightCtx wh = d.w;
       wh.mode = W_TARGET_H;
       const int ntiles = (p.V + kTile - 1) / kTile;
-      weight_subtiles<false, false, 4>(trow, trow, p.V, wh, 0, ntiles, L.subsum, nullptr, p.nsub);
+      if (wh.special)
+        weight_subtiles<W_TARGET_H, true, false, 4>(trow, trow, p.V, wh, 0, ntiles, L.subsum, nullptr, p.nsub);
+      else
+        weight_subtiles<W_TARGET_H, false, false, 4>(trow, trow, p.V, wh, 0, ntiles, L.subsum, nullptr, p.nsub);
       __syncthreads();
       if (wave_id() == 0) {
         int s_star = -1;
         double x_rel = 0.0;
         int tok = -1;
         if (find_subtile(L.subsum, p.nsub, uu, s_star, x_rel))
-          tok = find_token<false>(trow, trow, p.V, wh, s_star, x_rel);
+          tok = wh.special ? find_token<W_TARGET_H, true>(trow, trow, p.V, wh, s_star, x_rel)
+                           : find_token<W_TARGET_H, false>(trow, trow, p.V, wh, s_star, x_rel);
         if (lane_id() == 0) L.flag = tok;
       }
       __syncthreads();
