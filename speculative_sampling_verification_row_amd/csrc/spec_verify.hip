@@ -62,7 +62,8 @@ constexpr unsigned long long kValid = 1ull << 63;        // published bit of an 
 constexpr int kStage = 8 * kThreads;  // statistics words staged in LDS at once
 constexpr int kRowCap = 256;          // merged rows held in LDS at once
 constexpr int kNoK = INT32_MIN;       // statistics word of a share with no finite logit
-constexpr int kDecWords = 6;          // words of a decision record
+constexpr int kDecWords = 5;          // words of a decision record
+constexpr int kNoToken = INT32_MIN;   // no preloaded drafted token
 
 // Everything a lane needs to turn logits into sampling weights.  Weights are kept
 // in units of 1/st (st the target row's sum): an inverse-CDF draw depends only on
@@ -183,8 +184,8 @@ __device__ __forceinline__ unsigned long long poll_word(uint32_t* flags, unsigne
   unsigned long long w = ld_agent_u64(a);
   if (w != 0ull) return w;
   const unsigned long long t0 = wall_clock64();
-  while (true) {
-    if (ld_agent(&flags[3]) != 0u) return 0ull;
+  for (uint32_t n = 1;; ++n) {
+    if ((n & 7u) == 0u && ld_agent(&flags[3]) != 0u) return 0ull;  // another wait timed out
     __builtin_amdgcn_s_sleep(2);
     w = ld_agent_u64(a);
     if (w != 0ull) return w;
@@ -206,10 +207,16 @@ struct SliceLoc {
   unsigned long long* out;  // the slice's kWaves statistics words
 };
 
+// Slice `sig` of the list: sequence-major, then statistic row in streaming order,
+// then slice, rotated by the row's position so that a workgroup whose list
+// entries share one residue modulo S does not always get the same (and, for the
+// last slice, shorter) slice of its rows.
 __device__ __forceinline__ SliceLoc slice_loc(const Params& p, int sig) {
   const int b = sig / p.RS;
   const int q = sig - b * p.RS;
-  const int i = q / p.S, x = q - i * p.S;
+  const int i = q / p.S;
+  int x = q - i * p.S + i % p.S;
+  if (x >= p.S) x -= p.S;
   const int r = order_row(p, i);
   SliceLoc L;
   L.row = as_chunks(stat_row(p, b, r));
@@ -553,7 +560,7 @@ __device__ __forceinline__ int draw_drafter(const Params& p, int b) { return p.m
 // Merge the statistics of target rows 0..K and drafter `drafter`'s rows 0..K-1,
 // take every accept decision, and describe the draw.  Writes accept_mask and
 // gamma_star when `write_outputs`.  The result is in L.dl.d after the call.
-__device__ __forceinline__ void decide(const Params& p, int b, bool write_outputs, Lds& L) {
+__device__ __forceinline__ void decide(const Params& p, int b, bool write_outputs, int pre_n, Lds& L) {
   const int K = p.K, V = p.V;
   const int t = threadIdx.x;
   const int drafter = draw_drafter(p, b);
@@ -565,7 +572,7 @@ __device__ __forceinline__ void decide(const Params& p, int b, bool write_output
   float rr = 0.0f, zt = 0.0f, zd = 0.0f;
   bool tok_ok = false;
   if (t < K) {
-    n = p.tokens[b * K + t];
+    n = pre_n != kNoToken ? pre_n : p.tokens[b * K + t];
     rr = p.r[b * K + t];
     tok_ok = !bad_sel && n >= 0 && n < V;
     if (tok_ok) {
@@ -653,18 +660,19 @@ __device__ __forceinline__ void decide(const Params& p, int b, bool write_output
 // A sequence's last step: clear the statistics words it published.  Fused gamma
 // calls have two last steps (estimator and draw); the second one clears.
 __device__ __forceinline__ void finish_sequence(const Params& p, int b, Lds& L) {
-  stores_complete();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int last = 1;
-    if (p.P2 > 1) {
-      last = ticket(&p.done[b]) == static_cast<uint32_t>(p.P2 - 1) ? 1 : 0;
-      if (last) st_agent(&p.done[b], 0u);
+  int last = 1;
+  if (p.P2 > 1) {
+    stores_complete();  // this step is done with the sequence's words before it takes its ticket
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int l = ticket(&p.done[b]) == static_cast<uint32_t>(p.P2 - 1) ? 1 : 0;
+      if (l) st_agent(&p.done[b], 0u);
+      L.flag = l;
     }
-    L.flag = last;
+    __syncthreads();
+    last = L.flag;
   }
-  __syncthreads();
-  if (L.flag) {
+  if (last) {
     unsigned long long* w = part_row(p, b, 0);
     const int n = p.R * p.S * kWaves;
     for (int q = threadIdx.x; q < n; q += kThreads) st_agent_u64(w + q, 0ull);
@@ -672,16 +680,21 @@ __device__ __forceinline__ void finish_sequence(const Params& p, int b, Lds& L) 
   __syncthreads();
 }
 
-// Decision record: words 1..5 hold the weight context, word 0 (written last, once
-// the others have completed) the integer fields and the published bit.
+// Decision record: kDecWords words, each non-zero once written, so that a reader
+// needs no ordering between them and waits for each word: word 0 holds the
+// integer fields and the published bit, words 1.. the bitwise complement of a
+// value (zero only for an all-ones NaN, which no step produces).
+__device__ __forceinline__ unsigned long long dec_word(double v) {
+  return ~static_cast<unsigned long long>(__double_as_longlong(v));
+}
+__device__ __forceinline__ double dec_value(unsigned long long w) { return __longlong_as_double(static_cast<long long>(~w)); }
+
 __device__ __forceinline__ void store_decision(unsigned long long* rec, const Decision& d) {
-  st_agent_u64(rec + 1, static_cast<unsigned long long>(__double_as_longlong(d.w.r)));
-  st_agent_u64(rec + 2, static_cast<unsigned long long>(__double_as_longlong(d.w.s_scale)));
-  st_agent_u64(rec + 3, static_cast<unsigned long long>(__double_as_longlong(d.w.hn)));
-  st_agent_u64(rec + 4, 0ull);
-  st_agent_u64(rec + 5, static_cast<unsigned long long>(__float_as_uint(d.w.kt)) |
-                            (static_cast<unsigned long long>(__float_as_uint(d.w.kd)) << 32));
-  stores_complete();
+  st_agent_u64(rec + 1, dec_word(d.w.r));
+  st_agent_u64(rec + 2, dec_word(d.w.s_scale));
+  st_agent_u64(rec + 3, dec_word(d.w.hn));
+  st_agent_u64(rec + 4, ~(static_cast<unsigned long long>(__float_as_uint(d.w.kt)) |
+                          (static_cast<unsigned long long>(__float_as_uint(d.w.kd)) << 32)));
   const unsigned long long head = static_cast<unsigned long long>(d.A + 1) |
                                   (static_cast<unsigned long long>(d.draw_row) << 8) |
                                   (static_cast<unsigned long long>(d.pair) << 16) |
@@ -695,7 +708,13 @@ __device__ __forceinline__ void store_decision(unsigned long long* rec, const De
 // invalid decision (A = -1).
 __device__ __forceinline__ Decision load_decision(const Params& p, unsigned long long* rec) {
   Decision d;
-  const unsigned long long head = poll_word(p.flags, rec);
+  unsigned long long w[kDecWords];
+#pragma unroll
+  for (int i = 0; i < kDecWords; ++i) w[i] = ld_agent_u64(rec + i);  // one round trip when all are written
+#pragma unroll
+  for (int i = 0; i < kDecWords; ++i)
+    if (w[i] == 0ull) w[i] = poll_word(p.flags, rec + i);
+  const unsigned long long head = w[0];
   d.A = static_cast<int>(head & 0xffull) - 1;
   d.draw_row = static_cast<int>((head >> 8) & 0xffull);
   d.pair = static_cast<int>((head >> 16) & 1ull);
@@ -703,23 +722,28 @@ __device__ __forceinline__ Decision load_decision(const Params& p, unsigned long
   d.w.mode = static_cast<int>((head >> 18) & 3ull);
   d.w.n = static_cast<int>(static_cast<uint32_t>(head >> 32)) - 1;
   d.w.c = p.c;
-  d.w.r = __longlong_as_double(static_cast<long long>(ld_agent_u64(rec + 1)));
-  d.w.s_scale = __longlong_as_double(static_cast<long long>(ld_agent_u64(rec + 2)));
-  d.w.hn = __longlong_as_double(static_cast<long long>(ld_agent_u64(rec + 3)));
-  const unsigned long long kk = ld_agent_u64(rec + 5);
+  d.w.r = dec_value(w[1]);
+  d.w.s_scale = dec_value(w[2]);
+  d.w.hn = dec_value(w[3]);
+  const unsigned long long kk = ~w[4];
   d.w.kt = __uint_as_float(static_cast<uint32_t>(kk));
   d.w.kd = __uint_as_float(static_cast<uint32_t>(kk >> 32));
-  if (head == 0ull || d.A > p.K || d.draw_row > p.K || (d.pair && d.draw_row >= p.K)) d.A = -1;  // timed out
+  bool lost = false;
+#pragma unroll
+  for (int i = 0; i < kDecWords; ++i) lost |= w[i] == 0ull;  // a wait timed out
+  if (lost || d.A > p.K || d.draw_row > p.K || (d.pair && d.draw_row >= p.K)) d.A = -1;
   return d;
 }
 
 // Draw unit: the sequence's decisions, then the sub-tile masses of slice x of its
 // draw row(s).  Unit x = 0 also writes the per-position outputs and the decision
-// record.  A sequence with no valid draw publishes zero masses.
-__device__ __forceinline__ void unit_draw(const Params& p, int b, int x, Lds& L) {
-  decide(p, b, x == 0, L);
+// record.  A sequence with no valid draw publishes zero masses.  `pre_n`: the drafted token of position threadIdx.x,
+// loaded ahead of time, or kNoToken.
+__device__ __forceinline__ void unit_draw(const Params& p, int b, int x, int pre_n, Lds& L) {
+  decide(p, b, x == 0, pre_n, L);
   const Decision d = L.dl.d;
-  if (x == 0 && threadIdx.x == 0) store_decision(p.dec + static_cast<size_t>(b) * kDecWords, d);
+  unsigned long long* rec = p.dec + static_cast<size_t>(b) * kDecWords;
+  if (x == 0 && threadIdx.x == 0) store_decision(rec, d);
   unsigned long long* out = p.mass + static_cast<size_t>(b) * p.nsub;
   const int t0 = x * kTilesPerSlice;
   if (d.A >= 0) {
@@ -746,8 +770,7 @@ __device__ __forceinline__ void unit_final(const Params& p, int b, Lds& L) {
   const int tid = threadIdx.x;
   unsigned long long* rec = p.dec + static_cast<size_t>(b) * kDecWords;
   unsigned long long* msrc = p.mass + static_cast<size_t>(b) * p.nsub;
-  // the record and the masses are read together
-  if (tid == 0) L.dl.d = load_decision(p, rec);
+  // the masses and the record are read together
   unsigned long long w[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -755,6 +778,7 @@ __device__ __forceinline__ void unit_final(const Params& p, int b, Lds& L) {
     w[e] = 1ull;
     if (q < p.nsub) w[e] = ld_agent_u64(msrc + q);
   }
+  if (tid == 0) L.dl.d = load_decision(p, rec);
   bool missing = false;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -972,13 +996,17 @@ __device__ __forceinline__ void unit_estimate(const Params& p, int b, Lds& L) {
 // The kernel
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ void run_unit1(const Params& p, int u, Lds& L) {
+__device__ __forceinline__ bool is_draw_unit(const Params& p, int u) {
+  return p.mode != MODE_GAMMA || u % p.P1 >= p.K * p.S;
+}
+
+__device__ __forceinline__ void run_unit1(const Params& p, int u, int pre_n, Lds& L) {
   const int b = u / p.P1;
   const int l = u - b * p.P1;
   if (p.mode == MODE_GAMMA && l < p.K * p.S)
     unit_gamma(p, b, l / p.S, l % p.S, L);
   else
-    unit_draw(p, b, p.mode == MODE_GAMMA ? l - p.K * p.S : l, L);
+    unit_draw(p, b, p.mode == MODE_GAMMA ? l - p.K * p.S : l, pre_n, L);
 }
 
 __device__ __forceinline__ void run_unit2(const Params& p, int v, Lds& L) {
@@ -990,33 +1018,54 @@ __device__ __forceinline__ void run_unit2(const Params& p, int v, Lds& L) {
     unit_final(p, b, L);
 }
 
-// Phase 0: workgroup g streams statistics slices g, g + G, g + 2G, ... of the
-// sequence-major slice list, with the next slice's loads in flight while the
-// current one is reduced.
+// Phase 0 share of the later-dispatched half of the workgroups, relative to an
+// even share.  Waves dispatched first win the memory arbitration, so the first
+// half of the workgroups streams about 1.4x faster than the second: with 8/11
+// of an even share for the second half and the rest for the first, both halves
+// finish phase 0 together.
+constexpr int kLateShareNum = 8, kLateShareDen = 11;
+
+// k-th statistics slice of workgroup g (T0 when it has no more): J rounds of
+// slices j * G + g for every workgroup, then the rest of the list round-robin
+// over the first H workgroups.
+__device__ __forceinline__ int static_slice(int k, int g, int G, int H, int J, int T0) {
+  if (k < J) return k * G + g;
+  if (g >= H) return T0;
+  const int64_t s = static_cast<int64_t>(J) * G + g + static_cast<int64_t>(k - J) * H;
+  return s < T0 ? static_cast<int>(s) : T0;
+}
+
+// Phase 0: workgroup g streams its statistics slices of the sequence-major slice
+// list in order, with the next slice's loads in flight while the current one is
+// reduced.
 __device__ __forceinline__ void static_phase(const Params& p) {
   const int G = gridDim.x, g = blockIdx.x, T0 = p.total0;
+  const int H = (G + 1) / 2;
+  const int J = static_cast<int>(static_cast<int64_t>(T0) * kLateShareNum / (static_cast<int64_t>(G) * kLateShareDen));
   uint4 va[kTilesPerSlice], vb[kTilesPerSlice];
-  int sig = g;
+  int k = 0;
+  int sig = static_slice(k, g, G, H, J, T0);
   SliceLoc la{}, lb{};
   if (sig < T0) {
     la = slice_loc(p, sig);
     slice_load(p, la, va);
   }
   while (sig < T0) {
-    const int s1 = sig + G;
+    const int s1 = static_slice(k + 1, g, G, H, J, T0);
     if (s1 < T0) {
       lb = slice_loc(p, s1);
       slice_load(p, lb, vb);
     }
     slice_finish(p, la, va);
     if (s1 >= T0) break;
-    const int s2 = s1 + G;
+    const int s2 = static_slice(k + 2, g, G, H, J, T0);
     if (s2 < T0) {
       la = slice_loc(p, s2);
       slice_load(p, la, va);
     }
     slice_finish(p, lb, vb);
     sig = s2;
+    k += 2;
   }
 }
 
@@ -1027,11 +1076,16 @@ __device__ __forceinline__ void static_phase(const Params& p) {
 __global__ __launch_bounds__(kThreads) void flow_kernel(Params p) {
   __shared__ Lds L;
   const int G = gridDim.x, g = blockIdx.x;
-  static_phase(p);
   const int T1 = p.B * p.P1;
+  // the drafted token of this workgroup's first draw unit, loaded now so that the
+  // unit's decisions do not wait for it (nothing waits for the load here)
+  int pre_n = kNoToken;
+  if (g < T1 && is_draw_unit(p, g) && static_cast<int>(threadIdx.x) < p.K)
+    pre_n = p.tokens[(g / p.P1) * p.K + static_cast<int>(threadIdx.x)];
+  static_phase(p);
   for (int u = g; u < T1; u += G) {
     __syncthreads();
-    run_unit1(p, u, L);
+    run_unit1(p, u, u == g ? pre_n : kNoToken, L);
   }
   const int T2 = p.B * p.P2;
   for (int v = g; v < T2; v += G) {
