@@ -241,30 +241,46 @@ __device__ __forceinline__ void slice_load(const Params& p, const SliceLoc& L, u
   }
 }
 
+// One reference per lane and slice: the maximum over the lane's 64 logits first
+// (three-input max instructions, 0.5 per logit), then 2^(z c - k) summed in fp32
+// groups of eight and in fp64 beyond.  A lane with no finite logit keeps k = kNoRef
+// and s = 0.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ void slice_finish(const Params& p, const SliceLoc& L, const uint4 v[kTilesPerSlice]) {
-  RowAcc a = row_acc_init();
+  float z[kTilesPerSlice][8];
   if (L.full) {
 #pragma unroll
-    for (int t = 0; t < kTilesPerSlice; ++t) {
-      float z[8];
-      unpack8(v[t], z, 8);
-      row_acc_add8(a, z, p.c);
-    }
+    for (int t = 0; t < kTilesPerSlice; ++t) unpack8(v[t], z[t], 8);
   } else {
     const int nchunks = (p.V + kVec - 1) / kVec;
 #pragma unroll
     for (int t = 0; t < kTilesPerSlice; ++t) {
       const int ci = L.c0 + t * kThreads + static_cast<int>(threadIdx.x);
-      if (ci < nchunks) {
-        float z[8];
-        unpack8(v[t], z, p.V - ci * kVec);
-        row_acc_add8(a, z, p.c);
-      }
+      unpack8(v[t], z[t], ci < nchunks ? p.V - ci * kVec : 0);
     }
   }
-  const float km = wave_max(a.k);
-  const double s = wave_sum(ldexp(a.s, static_cast<int>(fmaxf(a.k - km, -2000.0f))));
-  if (lane_id() == 0) st_agent_u64(L.out + wave_id(), pack_stats(km, s));
+  float m = -__builtin_inff();
+#pragma unroll
+  for (int t = 0; t < kTilesPerSlice; ++t)
+    m = max3f(max3f(z[t][0], z[t][1], z[t][2]), max3f(z[t][3], z[t][4], z[t][5]), max3f(z[t][6], z[t][7], m));
+  const float c = p.c;
+  const float k = fmaxf(kNoRef, ceilf(m * c));
+  double s = 0.0;
+#pragma unroll
+  for (int t = 0; t < kTilesPerSlice; ++t) {
+    float e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = fast_exp2(fmaf(z[t][i], c, -k));
+    s += static_cast<double>(((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7])));
+  }
+  const float km = wave_max(k);
+  const double sw = wave_sum(ldexp(s, static_cast<int>(fmaxf(k - km, -2000.0f))));
+  if (lane_id() == 0) st_agent_u64(L.out + wave_id(), pack_stats(km, sw));
 }
 
 // ---------------------------------------------------------------------------
@@ -1036,36 +1052,74 @@ __device__ __forceinline__ int static_slice(int k, int g, int G, int H, int J, i
 }
 
 // Phase 0: workgroup g streams its statistics slices of the sequence-major slice
-// list in order, with the next slice's loads in flight while the current one is
-// reduced.
+// list in order.  kStaticDepth slices are in flight: the loads of the next
+// kStaticDepth - 1 slices are outstanding while the current one is reduced.
+constexpr int kStaticDepth = 2;
+
 __device__ __forceinline__ void static_phase(const Params& p) {
   const int G = gridDim.x, g = blockIdx.x, T0 = p.total0;
   const int H = (G + 1) / 2;
   const int J = static_cast<int>(static_cast<int64_t>(T0) * kLateShareNum / (static_cast<int64_t>(G) * kLateShareDen));
+  auto slice = [&](int k) { return static_slice(k, g, G, H, J, T0); };
   uint4 va[kTilesPerSlice], vb[kTilesPerSlice];
-  int k = 0;
-  int sig = static_slice(k, g, G, H, J, T0);
   SliceLoc la{}, lb{};
-  if (sig < T0) {
-    la = slice_loc(p, sig);
+  int k = 0;
+  int sa = slice(0), sb = slice(1);
+  if (sa < T0) {
+    la = slice_loc(p, sa);
     slice_load(p, la, va);
   }
-  while (sig < T0) {
-    const int s1 = static_slice(k + 1, g, G, H, J, T0);
-    if (s1 < T0) {
-      lb = slice_loc(p, s1);
+  if constexpr (kStaticDepth == 2) {
+    while (sa < T0) {
+      if (sb < T0) {
+        lb = slice_loc(p, sb);
+        slice_load(p, lb, vb);
+      }
+      slice_finish(p, la, va);
+      if (sb >= T0) break;
+      const int sc = slice(k + 2);
+      if (sc < T0) {
+        la = slice_loc(p, sc);
+        slice_load(p, la, va);
+      }
+      slice_finish(p, lb, vb);
+      sa = sc;
+      sb = slice(k + 3);
+      k += 2;
+    }
+  } else {
+    uint4 vc[kTilesPerSlice];
+    SliceLoc lc{};
+    if (sb < T0) {
+      lb = slice_loc(p, sb);
       slice_load(p, lb, vb);
     }
-    slice_finish(p, la, va);
-    if (s1 >= T0) break;
-    const int s2 = static_slice(k + 2, g, G, H, J, T0);
-    if (s2 < T0) {
-      la = slice_loc(p, s2);
-      slice_load(p, la, va);
+    // at the top: slice k in va, slice k + 1 in vb (loads outstanding)
+    while (sa < T0) {
+      const int sc = slice(k + 2);
+      if (sc < T0) {
+        lc = slice_loc(p, sc);
+        slice_load(p, lc, vc);
+      }
+      slice_finish(p, la, va);
+      if (sb >= T0) break;
+      const int sd = slice(k + 3);
+      if (sd < T0) {
+        la = slice_loc(p, sd);
+        slice_load(p, la, va);
+      }
+      slice_finish(p, lb, vb);
+      if (sc >= T0) break;
+      const int se = slice(k + 4);
+      if (se < T0) {
+        lb = slice_loc(p, se);
+        slice_load(p, lb, vb);
+      }
+      slice_finish(p, lc, vc);
+      sa = sd;
+      sb = se;
+      k += 3;
     }
-    slice_finish(p, lb, vb);
-    sig = s2;
-    k += 2;
   }
 }
 
