@@ -553,9 +553,6 @@ struct Decision {
 };
 
 struct DecideLds {
-  uint32_t state[SPEC_MAX_K];
-  double ct[SPEC_MAX_K];
-  double gs[SPEC_MAX_K];
   Decision d;
 };
 
@@ -598,73 +595,73 @@ __device__ __forceinline__ void decide(const Params& p, int b, bool write_output
   }
   // rows 0..K: target rows 0..K; rows K+1..2K: the drafter's rows 0..K-1
   merge_rows(p, b, 2 * K + 1, [&](int i) { return i <= K ? i : p.RT + dsafe * K + (i - K - 1); }, L.m);
+  // threads t < K (all in wave 0): the accept test of position t
+  uint32_t state = ST_INVALID;
+  double ct = 0.0, gs = 0.0;
   if (t < K) {
-    uint32_t state = ST_INVALID;
     bool acc = false;
     if (tok_ok) {
       const RowStats st{L.m.rk[t], L.m.rs[t]};
       const RowStats sd{L.m.rk[K + 1 + t], L.m.rs[K + 1 + t]};
       // [CA] Key design 3 with the verifier's probability c of the candidate; delta = 0 is SpS.
-      const double ct = fmin(token_prob(zt, p.c, st), 1.0);
+      ct = fmin(token_prob(zt, p.c, st), 1.0);
       const double cd = token_prob(zd, p.c, sd);
-      const double gs = fmin(ct + sqrt(2.0 * p.delta * ct * (1.0 - ct)), 1.0);
+      gs = fmin(ct + sqrt(2.0 * p.delta * ct * (1.0 - ct)), 1.0);
       const double ratio = cd > 0.0 ? gs / cd : (gs > 0.0 ? __builtin_inf() : 0.0);
       acc = static_cast<double>(rr) < ratio;  // [LT] §5.1: strict
       state = acc ? ST_ACCEPT : ST_REJECT;
-      L.dl.ct[t] = ct;
-      L.dl.gs[t] = gs;
       if (write_outputs && p.gamma_star) p.gamma_star[b * K + t] = static_cast<float>(gs);
     }
     if (write_outputs && p.accept_mask) p.accept_mask[b * K + t] = acc ? 1 : 0;
-    L.dl.state[t] = state;
   }
-  __syncthreads();
-  if (t == 0) {
-    Decision d;
-    int A = K;
-    bool bad = bad_sel;
-    for (int q = 0; q < K; ++q) {
-      bad |= (L.dl.state[q] == ST_INVALID);
-      if (L.dl.state[q] == ST_REJECT && A == K) A = q;
+  // wave 0: the first rejection A (ballots over the positions) and the draw
+  if (wave_id() == 0) {
+    const unsigned long long rej = __ballot(t < K && state == ST_REJECT);
+    const unsigned long long inv = __ballot(t < K && state == ST_INVALID);
+    const int A = rej != 0ull ? __ffsll(static_cast<long long>(rej)) - 1 : K;
+    const double ctA = readlane_f64(ct, A < K ? A : 0);
+    const double gsA = readlane_f64(gs, A < K ? A : 0);
+    const int nA = __builtin_amdgcn_readlane(n, A < K ? A : 0);
+    if (t == 0) {
+      Decision d;
+      WeightCtx w;
+      w.c = p.c;
+      w.kd = 0.0f;
+      w.r = 0.0;
+      w.s_scale = 1.0;
+      w.hn = 0.0;
+      w.n = -1;
+      w.special = 0;
+      if (bad_sel || inv != 0ull) {
+        d.A = -1;
+        d.draw_row = 0;
+        d.pair = 0;
+        w.mode = W_TARGET;
+        w.kt = 0.0f;
+      } else if (A < K) {
+        // [LT] §9.1: the first rejection A is resampled from the residual of its row pair
+        d.A = A;
+        d.draw_row = A;
+        d.pair = 1;
+        w.mode = W_RESID;
+        w.kt = L.m.rk[A];
+        w.kd = L.m.rk[K + 1 + A];
+        w.r = L.m.rs[A] / L.m.rs[K + 1 + A];
+        w.s_scale = ctA < 1.0 ? (1.0 - gsA) / (1.0 - ctA) : 0.0;  // [CA] Key design 2 (1.0 exactly at delta = 0)
+        w.hn = gsA * L.m.rs[A];
+        w.n = nA;
+        w.special = p.delta > 0.0 ? 1 : 0;
+      } else {
+        // every draft kept: bonus token from target row K
+        d.A = K;
+        d.draw_row = K;
+        d.pair = 0;
+        w.mode = W_TARGET;
+        w.kt = L.m.rk[K];
+      }
+      d.w = w;
+      L.dl.d = d;
     }
-    WeightCtx w;
-    w.c = p.c;
-    w.kd = 0.0f;
-    w.r = 0.0;
-    w.s_scale = 1.0;
-    w.hn = 0.0;
-    w.n = -1;
-    w.special = 0;
-    if (bad) {
-      d.A = -1;
-      d.draw_row = 0;
-      d.pair = 0;
-      w.mode = W_TARGET;
-      w.kt = 0.0f;
-    } else if (A < K) {
-      // [LT] §9.1: the first rejection A is resampled from the residual of its row pair
-      const double ct = L.dl.ct[A], gs = L.dl.gs[A];
-      d.A = A;
-      d.draw_row = A;
-      d.pair = 1;
-      w.mode = W_RESID;
-      w.kt = L.m.rk[A];
-      w.kd = L.m.rk[K + 1 + A];
-      w.r = L.m.rs[A] / L.m.rs[K + 1 + A];
-      w.s_scale = ct < 1.0 ? (1.0 - gs) / (1.0 - ct) : 0.0;  // [CA] Key design 2 (1.0 exactly at delta = 0)
-      w.hn = gs * L.m.rs[A];
-      w.n = p.tokens[b * K + A];
-      w.special = p.delta > 0.0 ? 1 : 0;
-    } else {
-      // every draft kept: bonus token from target row K
-      d.A = K;
-      d.draw_row = K;
-      d.pair = 0;
-      w.mode = W_TARGET;
-      w.kt = L.m.rk[K];
-    }
-    d.w = w;
-    L.dl.d = d;
   }
   __syncthreads();
 }
