@@ -5,12 +5,14 @@
 // and every workgroup g runs three phases on a fixed schedule; nothing is
 // claimed from a shared counter.
 //
-//   phase 0 -- statistics slices g, g + G, g + 2G, ... of the call's slice
-//       list.  A slice is 16384 tokens of one row, streamed once from HBM with
-//       128-bit loads while the next slice's loads are in flight.  Each wave
-//       reduces its share to an exact base-2 softmax pair (reference k, sum s)
-//       (spec_device.hpp) and publishes it as one 64-bit word.  The list is
-//       sequence-major, so sequences finish their statistics one after another.
+//   phase 0 -- statistics slices of the call's slice list, dealt to the
+//       workgroups on a fixed schedule weighted by how fast the hardware serves
+//       each half of them (static_phase).  A slice is 16384 tokens of one row,
+//       streamed once from HBM with 128-bit loads while the next slice's loads
+//       are in flight.  Each wave reduces its share to an exact base-2 softmax
+//       pair (reference k, sum s) and publishes it as one 64-bit word.  The list
+//       is sequence-major, so sequences finish their statistics one after
+//       another.
 //   phase 1 -- units g, g + G, ... of the draw / gamma list.  A draw unit (one
 //       per slice of a sequence's rows) merges the sequence's statistics, takes
 //       every accept decision ([LT] §5.1, [CA] Key design 3), finds the first
