@@ -106,7 +106,8 @@ struct Params {
   int P1;      // phase-1 units per sequence
   int P2;      // phase-2 units per sequence
   int RS;      // statistics slices per sequence (R * S)
-  int total0;  // statistics slices of the call (B * R * S; below 2^31 since each is 32 KB of logits)
+  int total0;  // slices of the statistics list (verify: B * R * S; gamma: the fused bonus rows, B * S or 0)
+  int ngroups; // gamma groups (B * K): a position's target row and its N drafter rows
   // outputs
   int32_t* accepted_len;
   int32_t* out_token;
@@ -121,7 +122,7 @@ struct Params {
   unsigned long long* dec;    // [B][kDecWords] draw decision records
   unsigned long long* part;   // [B][R][S][kWaves] statistics words
   unsigned long long* mass;   // [B][nsub] sub-tile masses (fp64 | kValid)
-  unsigned long long* gpart;  // [B][K][N][S] gamma partial sums (fp64 | kValid)
+  unsigned long long* gpart;  // [B][K][N][S][kWaves] gamma partial sums (fp64 | kValid)
 };
 
 __device__ __forceinline__ const uint4* as_chunks(const uint16_t* row) { return reinterpret_cast<const uint4*>(row); }
@@ -214,12 +215,19 @@ struct SliceLoc {
 // entries share one residue modulo S does not always get the same (and, for the
 // last slice, shorter) slice of its rows.
 __device__ __forceinline__ SliceLoc slice_loc(const Params& p, int sig) {
-  const int b = sig / p.RS;
-  const int q = sig - b * p.RS;
-  const int i = q / p.S;
-  int x = q - i * p.S + i % p.S;
-  if (x >= p.S) x -= p.S;
-  const int r = order_row(p, i);
+  int b, x, r;
+  if (p.mode == MODE_GAMMA) {  // the list holds only the fused bonus rows (the groups do the rest)
+    b = sig / p.S;
+    x = sig - b * p.S;
+    r = p.K;
+  } else {
+    b = sig / p.RS;
+    const int q = sig - b * p.RS;
+    const int i = q / p.S;
+    x = q - i * p.S + i % p.S;
+    if (x >= p.S) x -= p.S;
+    r = order_row(p, i);
+  }
   SliceLoc L;
   L.row = as_chunks(stat_row(p, b, r));
   L.c0 = x * kSliceChunks;
@@ -562,11 +570,8 @@ struct Lds {
   MergeLds m;
   DecideLds dl;
   double subsum[kMaxSub];
-  double part[SPEC_MAX_N * kWaves];
   double gsum[kRowCap];
   double arat[kRowCap];
-  float lt;
-  float ld[SPEC_MAX_N];
   int flag;
 };
 
@@ -860,77 +865,211 @@ __device__ __forceinline__ void unit_final(const Params& p, int b, Lds& L) {
   finish_sequence(p, b, L);
 }
 
-// Gamma unit: sum_x min(pt_k, pd_{i,k}) over slice x for every drafter i ([NB] Key design 1).
-__device__ __forceinline__ void unit_gamma(const Params& p, int b, int k, int x, Lds& L) {
-  const int tid = threadIdx.x;
-  // rows: 0 the target row k, 1 + i drafter i's row k
-  merge_rows(p, b, p.N + 1, [&](int i) { return i == 0 ? k : p.RT + (i - 1) * p.K + k; }, L.m);
-  // log2 normalisers l = k + log2(s)
-  if (tid <= p.N) {
-    const float lv = static_cast<float>(static_cast<double>(L.m.rk[tid]) + log2(L.m.rs[tid]));
-    if (tid == 0)
-      L.lt = lv;
-    else
-      L.ld[tid - 1] = lv;
-  }
-  for (int i = tid; i < p.N * kWaves; i += kThreads) L.part[i] = 0.0;
-  __syncthreads();
-  const float c = p.c, lt = L.lt;
+// ---------------------------------------------------------------------------
+// Gamma groups: statistics and gamma in one pass
+// ---------------------------------------------------------------------------
+//
+// Group (b, k) is position k of sequence b: the target row k and the N drafter
+// rows k.  A slot of S workgroups takes a group at a time; member x streams slice
+// x of each of the N + 1 rows once, keeping the lane's 64 exponentials of the
+// target slice and of the current drafter slice in registers.  After publishing
+// a row slice's statistics it waits for the other members' words of that row
+// (they stream the same rows in the same order), turns the exponentials into
+// probabilities with the row's normaliser, and publishes its slice's share of
+// gamma_i = sum_x min(pt, pd_i) ([NB] Key design 1), without reading the row
+// again.  The next row's loads are in flight meanwhile.
+
+// Lane statistics of one slice: the lane's reference k (the ceiling of its
+// maximum z c) and s = sum 2^(z c - k); with STORE the 64 terms are kept in e.
+template <bool STORE, bool FULL>
+__device__ __forceinline__ float lane_exps(const Params& p, const uint4 v[kTilesPerSlice], int ci0,
+                                           float e[kTilesPerSlice][8], double& s) {
+  constexpr bool full = FULL;
   const int nchunks = (p.V + kVec - 1) / kVec;
-  const uint4* tr = as_chunks(target_row(p, b, k));
-  constexpr int kParts = 4;  // the slice is streamed in quarters to bound registers
-  constexpr int kHalf = kTilesPerSlice / kParts;
-#pragma unroll 1
-  for (int h = 0; h < kParts; ++h) {
-    const int c0 = x * kSliceChunks + h * kHalf * kThreads;
-    uint4 vt[kHalf], vd[kHalf], vn[kHalf];
+  if (!FULL) asm volatile("" : "+v"(ci0));  // tile bounds recomputed per pass, not kept live
+  float m = -__builtin_inff();
 #pragma unroll
-    for (int t = 0; t < kHalf; ++t) {
-      const int ci = c0 + t * kThreads + tid;
-      if (ci < nchunks) {
-        vt[t] = tr[ci];
-        vd[t] = as_chunks(draft_row(p, b, 0, k))[ci];
-      }
-    }
-#pragma unroll 1
-    for (int i = 0; i < p.N; ++i) {
-      if (i + 1 < p.N) {  // prefetch the next drafter's half-slice
-        const uint4* dn = as_chunks(draft_row(p, b, i + 1, k));
-#pragma unroll
-        for (int t = 0; t < kHalf; ++t) {
-          const int ci = c0 + t * kThreads + tid;
-          if (ci < nchunks) vn[t] = dn[ci];
-        }
-      }
-      const float ld = L.ld[i];
-      float acc = 0.0f;
-#pragma unroll
-      for (int t = 0; t < kHalf; ++t) {
-        const int ci = c0 + t * kThreads + tid;
-        if (ci < nchunks) {
-          const int valid = p.V - ci * kVec;
-          float zt[8], zd[8], e[8];
-          unpack8(vt[t], zt, valid);
-          unpack8(vd[t], zd, valid);
-#pragma unroll
-          for (int q = 0; q < 8; ++q) e[q] = fast_exp2(fminf(fmaf(zt[q], c, -lt), fmaf(zd[q], c, -ld)));
-          acc += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-        }
-      }
-      const double g = wave_sum(static_cast<double>(acc));
-      if (lane_id() == 0) L.part[i * kWaves + wave_id()] += g;
-#pragma unroll
-      for (int t = 0; t < kHalf; ++t) vd[t] = vn[t];
-    }
+  for (int t = 0; t < kTilesPerSlice; ++t) {
+    const int ci = ci0 + t * kThreads;
+    float z[8];
+    unpack8(v[t], z, full ? 8 : (ci < nchunks ? p.V - ci * kVec : 0));
+    m = max3f(max3f(z[0], z[1], z[2]), max3f(z[3], z[4], z[5]), max3f(z[6], z[7], m));
   }
-  __syncthreads();
-  if (tid < p.N) {
-    double g = 0.0;
-    for (int w = 0; w < kWaves; ++w) g += L.part[tid * kWaves + w];
-    st_agent_u64(p.gpart + ((static_cast<size_t>(b) * p.K + k) * p.N + tid) * p.S + x, pack_f64(g));
+  const float c = p.c;
+  const float k = fmaxf(kNoRef, ceilf(m * c));
+  s = 0.0;
+  if (!FULL) asm volatile("" : "+v"(ci0));
+#pragma unroll
+  for (int t = 0; t < kTilesPerSlice; ++t) {
+    const int ci = ci0 + t * kThreads;
+    float z[8], ev[8];
+    // unpacked again rather than kept from the first pass (64 more live registers)
+    uint4 w = v[t];
+    asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+    unpack8(w, z, full ? 8 : (ci < nchunks ? p.V - ci * kVec : 0));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ev[i] = fast_exp2(fmaf(z[i], c, -k));
+    if (STORE)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) e[t][i] = ev[i];
+    s += static_cast<double>(((ev[0] + ev[1]) + (ev[2] + ev[3])) + ((ev[4] + ev[5]) + (ev[6] + ev[7])));
   }
-  __syncthreads();
+  return k;
 }
+
+// Wave: publish its share of a slice's statistics (one word per wave).
+__device__ __forceinline__ void publish_slice_stats(unsigned long long* row_words, int x, float k, double s) {
+  const float km = wave_max(k);
+  const double sw = wave_sum(ldexp(s, static_cast<int>(fmaxf(k - km, -2000.0f))));
+  if (lane_id() == 0) st_agent_u64(row_words + static_cast<size_t>(x) * kWaves + wave_id(), pack_stats(km, sw));
+}
+
+// Wave: wait for all of a row's statistics words and merge them.
+__device__ __forceinline__ RowStats wave_row_stats(const Params& p, const unsigned long long* row_words) {
+  const int W = p.S * kWaves;
+  const int lane = lane_id();
+  int km = kNoK;
+  unsigned long long wv[kMaxSlices * kWaves / 64];
+#pragma unroll
+  for (int j = 0; j < kMaxSlices * kWaves / 64; ++j) {
+    const int q = lane + 64 * j;
+    wv[j] = 1ull;
+    if (q < W) wv[j] = ld_agent_u64(const_cast<unsigned long long*>(row_words) + q);
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxSlices * kWaves / 64; ++j) {
+    const int q = lane + 64 * j;
+    if (q < W && wv[j] == 0ull) wv[j] = poll_word(p.flags, const_cast<unsigned long long*>(row_words) + q);
+    if (q < W) km = max(km, stats_k(wv[j]));
+  }
+  km = wave_max_i(km);
+  double s = 0.0;
+#pragma unroll
+  for (int j = 0; j < kMaxSlices * kWaves / 64; ++j) {
+    const int q = lane + 64 * j;
+    if (q < W) {
+      const int kq = stats_k(wv[j]);
+      if (kq != kNoK) s += ldexp(stats_s(wv[j]), max(kq - km, -2000));
+    }
+  }
+  s = wave_sum(s);
+  return RowStats{km == kNoK ? kNoRef : static_cast<float>(km), s};
+}
+
+// Factor turning a lane's terms (reference kl) into probabilities of the row.
+__device__ __forceinline__ float lane_scale(float kl, const RowStats& r) {
+  if (kl == kNoRef || !(r.s > 0.0)) return 0.0f;
+  return static_cast<float>(ldexp(1.0 / r.s, static_cast<int>(fmaxf(kl - r.k, -2000.0f))));
+}
+
+// The target slice's 64 terms per lane, in LDS (conflict-free: consecutive lanes,
+// consecutive words), while the drafters' slices stream through registers.
+struct GammaLds {
+  float pt[kTilesPerSlice * 8][kThreads];
+};
+
+template <bool FULL>
+__device__ __forceinline__ void gamma_member(const Params& p, GammaLds& GL, int slot, int x) {
+  constexpr bool full = FULL;
+  const int S = p.S, Q = gridDim.x / S;
+  const int K = p.K, N = p.N, nG = p.ngroups;
+  const int ci0 = x * kSliceChunks + static_cast<int>(threadIdx.x);
+  const int nchunks = (p.V + kVec - 1) / kVec;
+  const int tid = threadIdx.x;
+  // row r of group q: 0 the target row k, 1 + i drafter i's row k
+  auto row_index = [&](int k, int r) { return r == 0 ? k : p.RT + (r - 1) * K + k; };
+  auto load = [&](int q, int r, uint4 (&v)[kTilesPerSlice]) {
+    const int b = q / K, k = q - b * K;
+    // the lane's chunk index, recomputed here rather than kept live (as 64-bit
+    // offsets) across the whole loop
+    int c0 = ci0;
+    asm volatile("" : "+v"(c0));
+    const uint4* row = as_chunks(stat_row(p, b, row_index(k, r))) + c0;
+#pragma unroll
+    for (int t = 0; t < kTilesPerSlice; ++t)
+      if (full || c0 + t * kThreads < nchunks) v[t] = row[t * kThreads];
+  };
+  // The terms of the previous row slice wait in `e` (registers) until its row's
+  // normaliser is known, one step later, so that the exchange between the
+  // members is off the critical path.
+  float e[kTilesPerSlice][8];
+  int pq = -1, pr = 0;
+  float pkl = 0.0f;
+  auto finish_prev = [&]() {
+    const int b = pq / K, k = pq - b * K;
+    const float sc = lane_scale(pkl, wave_row_stats(p, part_row(p, b, row_index(k, pr))));
+    if (pr == 0) {  // the target's terms become probabilities
+#pragma unroll
+      for (int j = 0; j < kTilesPerSlice * 8; ++j) GL.pt[j][tid] *= sc;
+      return;
+    }
+    double gs = 0.0;
+#pragma unroll
+    for (int t = 0; t < kTilesPerSlice; ++t) {
+      float mn[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mn[i] = fminf(GL.pt[t * 8 + i][tid], e[t][i] * sc);
+      gs += static_cast<double>(((mn[0] + mn[1]) + (mn[2] + mn[3])) + ((mn[4] + mn[5]) + (mn[6] + mn[7])));
+    }
+    gs = wave_sum(gs);
+    if (lane_id() == 0)
+      st_agent_u64(p.gpart + ((((static_cast<size_t>(b) * K + k) * N + (pr - 1)) * S + x) * kWaves + wave_id()),
+                   pack_f64(gs));
+  };
+  // job (q, r): finish the previous row slice, then reduce row r of group q from
+  // `cur` while the next job's loads go to `nxt`
+  auto step = [&](int q, int r, uint4 (&cur)[kTilesPerSlice], uint4 (&nxt)[kTilesPerSlice]) {
+    const int b = q / K, k = q - b * K;
+    if (r < N)
+      load(q, r + 1, nxt);
+    else if (q + Q < nG)
+      load(q + Q, 0, nxt);
+    if (pq >= 0) finish_prev();
+    double sl;
+    const float kl = lane_exps<true, FULL>(p, cur, ci0, e, sl);
+    publish_slice_stats(part_row(p, b, row_index(k, r)), x, kl, sl);
+    if (r == 0) {  // the target's terms wait in LDS for the row's normaliser
+#pragma unroll
+      for (int t = 0; t < kTilesPerSlice; ++t)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) GL.pt[t * 8 + i][tid] = e[t][i];
+    }
+    pq = q;
+    pr = r;
+    pkl = kl;
+  };
+  uint4 va[kTilesPerSlice], vb[kTilesPerSlice];
+  int q = slot, r = 0;
+  auto advance = [&]() {
+    if (++r > N) {
+      r = 0;
+      q += Q;
+    }
+    return q < nG;
+  };
+  load(q, 0, va);
+#pragma unroll 1
+  while (true) {
+    step(q, r, va, vb);
+    if (!advance()) break;
+    step(q, r, vb, va);
+    if (!advance()) break;
+  }
+  finish_prev();
+}
+
+// Slot g / S of the workgroups, member g % S (workgroups beyond the last full slot
+// and slots beyond the last group have no group work).
+__device__ __forceinline__ void gamma_groups(const Params& p, GammaLds& GL) {
+  const int S = p.S, Q = gridDim.x / S, g = blockIdx.x;
+  if (g >= Q * S || g / S >= p.ngroups) return;
+  const int slot = g / S, x = g - slot * S;
+  if ((x + 1) * kSliceTok <= p.V)
+    gamma_member<true>(p, GL, slot, x);
+  else
+    gamma_member<false>(p, GL, slot, x);
+}
+
 
 // Estimator step of a sequence: gamma, the estimator and the loss of every drafter,
 // positions in chunks whose rows fit the LDS arrays.
@@ -944,17 +1083,18 @@ __device__ __forceinline__ void unit_estimate(const Params& p, int b, Lds& L) {
     // gamma of the chunk's (position, drafter) pairs: one pair per thread
     if (tid < nk * N) {
       const int kk = k0 + tid / N, i = tid % N;
-      unsigned long long* src = p.gpart + ((static_cast<size_t>(b) * K + kk) * N + i) * p.S;
+      const int nw = p.S * kWaves;  // one word per (slice, wave) of the group members
+      unsigned long long* src = p.gpart + ((static_cast<size_t>(b) * K + kk) * N + i) * nw;
       double g = 0.0;
-      for (int x0 = 0; x0 < p.S; x0 += 8) {
+      for (int x0 = 0; x0 < nw; x0 += 8) {
         unsigned long long w[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] = x0 + e < p.S ? ld_agent_u64(src + x0 + e) : kValid;
+        for (int e = 0; e < 8; ++e) w[e] = x0 + e < nw ? ld_agent_u64(src + x0 + e) : kValid;
         bool missing = false;
 #pragma unroll
         for (int e = 0; e < 8; ++e) missing |= w[e] == 0ull;
         if (missing) {  // not yet published (rare): wait for each word of the batch in turn
-          for (int e = 0; e < 8 && x0 + e < p.S; ++e) g += unpack_f64(poll_word(p.flags, src + x0 + e));
+          for (int e = 0; e < 8 && x0 + e < nw; ++e) g += unpack_f64(poll_word(p.flags, src + x0 + e));
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) g += unpack_f64(w[e]);
@@ -1002,8 +1142,8 @@ __device__ __forceinline__ void unit_estimate(const Params& p, int b, Lds& L) {
     p.loss[b * N + tid] = static_cast<float>(static_cast<double>(K + 1) - Lh);
   }
   // every gamma unit of the sequence has published (all were read above): clear them
-  unsigned long long* gw = p.gpart + static_cast<size_t>(b) * K * N * p.S;
-  for (int q = tid; q < K * N * p.S; q += kThreads) st_agent_u64(gw + q, 0ull);
+  unsigned long long* gw = p.gpart + static_cast<size_t>(b) * K * N * p.S * kWaves;
+  for (int q = tid; q < K * N * p.S * kWaves; q += kThreads) st_agent_u64(gw + q, 0ull);
   finish_sequence(p, b, L);
 }
 
@@ -1011,17 +1151,11 @@ __device__ __forceinline__ void unit_estimate(const Params& p, int b, Lds& L) {
 // The kernel
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ bool is_draw_unit(const Params& p, int u) {
-  return p.mode != MODE_GAMMA || u % p.P1 >= p.K * p.S;
-}
+__device__ __forceinline__ bool is_draw_unit(const Params& p, int u) { return p.P1 > 0; }
 
 __device__ __forceinline__ void run_unit1(const Params& p, int u, int pre_n, Lds& L) {
   const int b = u / p.P1;
-  const int l = u - b * p.P1;
-  if (p.mode == MODE_GAMMA && l < p.K * p.S)
-    unit_gamma(p, b, l / p.S, l % p.S, L);
-  else
-    unit_draw(p, b, p.mode == MODE_GAMMA ? l - p.K * p.S : l, pre_n, L);
+  unit_draw(p, b, u - b * p.P1, pre_n, L);
 }
 
 __device__ __forceinline__ void run_unit2(const Params& p, int v, Lds& L) {
@@ -1126,8 +1260,15 @@ __device__ __forceinline__ void static_phase(const Params& p) {
 // list.  A phase-1 unit waits only for phase-0 words and a phase-2 unit only for
 // phase-0 and phase-1 words, and every workgroup finishes a phase before it
 // starts the next, so every wait ends.
-__global__ __launch_bounds__(kThreads) void flow_kernel(Params p) {
-  __shared__ Lds L;
+// LDS of the units, or of the gamma groups (which run before any unit)
+union KernelLds {
+  Lds units;
+  GammaLds gamma;
+};
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void flow_kernel(Params p) {
+  __shared__ KernelLds KL;
+  Lds& L = KL.units;
   const int G = gridDim.x, g = blockIdx.x;
   const int T1 = p.B * p.P1;
   // the drafted token of this workgroup's first draw unit, loaded now so that the
@@ -1135,6 +1276,7 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(Params p) {
   int pre_n = kNoToken;
   if (g < T1 && is_draw_unit(p, g) && static_cast<int>(threadIdx.x) < p.K)
     pre_n = p.tokens[(g / p.P1) * p.K + static_cast<int>(threadIdx.x)];
+  if (p.mode == MODE_GAMMA) gamma_groups(p, KL.gamma);
   static_phase(p);
   for (int u = g; u < T1; u += G) {
     __syncthreads();
@@ -1224,7 +1366,7 @@ __global__ void fill_zero_kernel(uint32_t* p, size_t n) {
 struct Shape {
   int B, K, N, V, mode, fused;
   int R, RT, S, nsub, P1, P2;
-  int64_t RS, total0;  // checked below 2^31 before a launch
+  int64_t RS, total0, ngroups;  // checked below 2^31 before a launch
 };
 
 static Shape make_shape(int B, int K, int N, int V, int mode, int fused) {
@@ -1239,10 +1381,12 @@ static Shape make_shape(int B, int K, int N, int V, int mode, int fused) {
   s.R = s.RT + N * K;
   s.S = (V + kSliceTok - 1) / kSliceTok;
   s.nsub = (V + kSub - 1) / kSub;
-  s.P1 = mode == MODE_VERIFY ? s.S : K * s.S + (fused ? s.S : 0);
+  s.P1 = mode == MODE_VERIFY || fused ? s.S : 0;
   s.P2 = mode == MODE_VERIFY ? 1 : 1 + fused;
   s.RS = static_cast<int64_t>(s.R) * s.S;
-  s.total0 = static_cast<int64_t>(B) * s.RS;
+  // gamma calls: the groups take the rows of positions 0..K-1; the list holds the bonus rows
+  s.total0 = mode == MODE_VERIFY ? static_cast<int64_t>(B) * s.RS : (fused ? static_cast<int64_t>(B) * s.S : 0);
+  s.ngroups = mode == MODE_VERIFY ? 0 : static_cast<int64_t>(B) * K;
   return s;
 }
 
@@ -1269,7 +1413,7 @@ static WsLayout ws_layout(const Shape& s) {
   L.mass = o;
   o = align256(o + 8 * B * static_cast<size_t>(kMaxSub));
   L.gpart = o;
-  o = align256(o + (s.mode == MODE_GAMMA ? 8 * B * static_cast<size_t>(s.K) * s.N * kMaxSlices : 0));
+  o = align256(o + (s.mode == MODE_GAMMA ? 8 * B * static_cast<size_t>(s.K) * s.N * kMaxSlices * kWaves : 0));
   L.total = o;
   return L;
 }
@@ -1314,16 +1458,24 @@ static void plan_units(Params& p, const Shape& s) {
   p.P2 = s.P2;
   p.RS = static_cast<int>(s.RS);
   p.total0 = static_cast<int>(s.total0);
+  p.ngroups = static_cast<int>(s.ngroups);
 }
 
 static int launch_flow(Params& p, const Shape& s, hipStream_t stream) {
   // a slice is 32 KB of logits, so 2^31 slices exceed any device's memory; the
   // limit keeps the schedule in 32-bit arithmetic (with room for j * G + g)
-  if (s.total0 > 0x3fffffffLL || static_cast<int64_t>(s.B) * s.P1 > 0x3fffffffLL) return SPEC_ERR_SHAPE;
+  if (s.total0 > 0x3fffffffLL || static_cast<int64_t>(s.B) * s.P1 > 0x3fffffffLL || s.ngroups > 0x3fffffffLL)
+    return SPEC_ERR_SHAPE;
   int grid = resident_workgroups();
   if (grid <= 0) return SPEC_ERR_HIP;
-  // every workgroup is resident at once (the schedule's waits rely on it)
-  if (grid > s.total0) grid = static_cast<int>(s.total0);
+  // every workgroup is resident at once (the schedule's waits rely on it); a gamma
+  // call needs at least one slot of S workgroups
+  if (s.mode == MODE_GAMMA && grid < s.S) return SPEC_ERR_SHAPE;
+  int64_t want = s.total0;
+  if (s.ngroups * s.S > want) want = s.ngroups * s.S;
+  if (static_cast<int64_t>(s.B) * s.P1 > want) want = static_cast<int64_t>(s.B) * s.P1;
+  if (static_cast<int64_t>(s.B) * s.P2 > want) want = static_cast<int64_t>(s.B) * s.P2;
+  if (grid > want) grid = static_cast<int>(want);
   plan_units(p, s);
   hipLaunchKernelGGL(flow_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
