@@ -924,29 +924,37 @@ __device__ __forceinline__ void publish_slice_stats(unsigned long long* row_word
   if (lane_id() == 0) st_agent_u64(row_words + static_cast<size_t>(x) * kWaves + wave_id(), pack_stats(km, sw));
 }
 
-// Wave: wait for all of a row's statistics words and merge them.
-__device__ __forceinline__ RowStats wave_row_stats(const Params& p, const unsigned long long* row_words) {
+// Wave: a row's statistics words, loaded (issue) and then, once the loads are
+// back, waited for where still missing and merged (finish).  Between the two the
+// wave can do other work while the loads fly.
+constexpr int kRowWordsPerLane = kMaxSlices * kWaves / 64;
+
+__device__ __forceinline__ void wave_row_issue(const Params& p, const unsigned long long* row_words,
+                                               unsigned long long wv[kRowWordsPerLane]) {
   const int W = p.S * kWaves;
-  const int lane = lane_id();
-  int km = kNoK;
-  unsigned long long wv[kMaxSlices * kWaves / 64];
 #pragma unroll
-  for (int j = 0; j < kMaxSlices * kWaves / 64; ++j) {
-    const int q = lane + 64 * j;
+  for (int j = 0; j < kRowWordsPerLane; ++j) {
+    const int q = lane_id() + 64 * j;
     wv[j] = 1ull;
     if (q < W) wv[j] = ld_agent_u64(const_cast<unsigned long long*>(row_words) + q);
   }
+}
+
+__device__ __forceinline__ RowStats wave_row_finish(const Params& p, const unsigned long long* row_words,
+                                                    unsigned long long wv[kRowWordsPerLane]) {
+  const int W = p.S * kWaves;
+  int km = kNoK;
 #pragma unroll
-  for (int j = 0; j < kMaxSlices * kWaves / 64; ++j) {
-    const int q = lane + 64 * j;
+  for (int j = 0; j < kRowWordsPerLane; ++j) {
+    const int q = lane_id() + 64 * j;
     if (q < W && wv[j] == 0ull) wv[j] = poll_word(p.flags, const_cast<unsigned long long*>(row_words) + q);
     if (q < W) km = max(km, stats_k(wv[j]));
   }
   km = wave_max_i(km);
   double s = 0.0;
 #pragma unroll
-  for (int j = 0; j < kMaxSlices * kWaves / 64; ++j) {
-    const int q = lane + 64 * j;
+  for (int j = 0; j < kRowWordsPerLane; ++j) {
+    const int q = lane_id() + 64 * j;
     if (q < W) {
       const int kq = stats_k(wv[j]);
       if (kq != kNoK) s += ldexp(stats_s(wv[j]), max(kq - km, -2000));
@@ -968,14 +976,41 @@ struct GammaLds {
   float pt[kTilesPerSlice * 8][kThreads];
 };
 
-template <bool FULL>
+// A slice that runs past the row's end: chunks beyond it become -inf logits and
+// the last chunk's tokens beyond it too, so that the reductions need no bounds.
+__device__ __forceinline__ void mask_tail(uint4 v[kTilesPerSlice], int ci0, int V) {
+  const int nchunks = (V + kVec - 1) / kVec;
+  constexpr uint32_t kNegInf2 = 0xff80ff80u;  // two bf16 -inf
+#pragma unroll
+  for (int t = 0; t < kTilesPerSlice; ++t) {
+    const int ci = ci0 + t * kThreads;
+    const int valid = V - ci * kVec;  // tokens of this chunk inside the row
+    if (valid <= 0) {
+      v[t] = make_uint4(kNegInf2, kNegInf2, kNegInf2, kNegInf2);
+    } else if (valid < kVec) {
+      uint32_t w[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
+#pragma unroll
+      for (int e = 0; e < kVec; ++e)
+        if (e >= valid) w[e >> 1] = (e & 1) ? ((w[e >> 1] & 0x0000ffffu) | 0xff800000u) : ((w[e >> 1] & 0xffff0000u) | 0xff80u);
+      v[t] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
 __device__ __forceinline__ void gamma_member(const Params& p, GammaLds& GL, int slot, int x) {
-  constexpr bool full = FULL;
+  const bool full = (x + 1) * kSliceTok <= p.V;
   const int S = p.S, Q = gridDim.x / S;
   const int K = p.K, N = p.N, nG = p.ngroups;
   const int ci0 = x * kSliceChunks + static_cast<int>(threadIdx.x);
   const int nchunks = (p.V + kVec - 1) / kVec;
   const int tid = threadIdx.x;
+  // the slot's n-th group, round-robin over the slots (nG when none); weighting
+  // the first-dispatched slots measured slower here (the members' exchanges,
+  // not memory arbitration, set the pace)
+  auto slot_group = [&](int n) {
+    const int64_t q = slot + static_cast<int64_t>(n) * Q;
+    return q < nG ? static_cast<int>(q) : nG;
+  };
   // row r of group q: 0 the target row k, 1 + i drafter i's row k
   auto row_index = [&](int k, int r) { return r == 0 ? k : p.RT + (r - 1) * K + k; };
   auto load = [&](int q, int r, uint4 (&v)[kTilesPerSlice]) {
@@ -989,15 +1024,16 @@ __device__ __forceinline__ void gamma_member(const Params& p, GammaLds& GL, int 
     for (int t = 0; t < kTilesPerSlice; ++t)
       if (full || c0 + t * kThreads < nchunks) v[t] = row[t * kThreads];
   };
-  // The terms of the previous row slice wait in `e` (registers) until its row's
-  // normaliser is known, one step later, so that the exchange between the
-  // members is off the critical path.
-  float e[kTilesPerSlice][8];
+  // The previous row slice's terms wait in registers until its row's normaliser
+  // is known: the other members' words of that row are loaded at the start of
+  // the next step and used after that step's own statistics pass, so the
+  // exchange between the members overlaps work.
   int pq = -1, pr = 0;
   float pkl = 0.0f;
-  auto finish_prev = [&]() {
+  // finish the previous row slice (terms in `ep`) once its row is known
+  auto finish_prev = [&](const RowStats& rs, const float (&ep)[kTilesPerSlice][8]) {
     const int b = pq / K, k = pq - b * K;
-    const float sc = lane_scale(pkl, wave_row_stats(p, part_row(p, b, row_index(k, pr))));
+    const float sc = lane_scale(pkl, rs);
     if (pr == 0) {  // the target's terms become probabilities
 #pragma unroll
       for (int j = 0; j < kTilesPerSlice * 8; ++j) GL.pt[j][tid] *= sc;
@@ -1008,7 +1044,7 @@ __device__ __forceinline__ void gamma_member(const Params& p, GammaLds& GL, int 
     for (int t = 0; t < kTilesPerSlice; ++t) {
       float mn[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) mn[i] = fminf(GL.pt[t * 8 + i][tid], e[t][i] * sc);
+      for (int i = 0; i < 8; ++i) mn[i] = fminf(GL.pt[t * 8 + i][tid], ep[t][i] * sc);
       gs += static_cast<double>(((mn[0] + mn[1]) + (mn[2] + mn[3])) + ((mn[4] + mn[5]) + (mn[6] + mn[7])));
     }
     gs = wave_sum(gs);
@@ -1016,58 +1052,83 @@ __device__ __forceinline__ void gamma_member(const Params& p, GammaLds& GL, int 
       st_agent_u64(p.gpart + ((((static_cast<size_t>(b) * K + k) * N + (pr - 1)) * S + x) * kWaves + wave_id()),
                    pack_f64(gs));
   };
-  // job (q, r): finish the previous row slice, then reduce row r of group q from
-  // `cur` while the next job's loads go to `nxt`
-  auto step = [&](int q, int r, uint4 (&cur)[kTilesPerSlice], uint4 (&nxt)[kTilesPerSlice]) {
+  // job (q, r): reduce row r of group q from `cur` into `ec` while the next job's
+  // loads go to `nxt`, then finish the previous row slice (terms in `ep`)
+  auto step = [&](int q, int r, uint4 (&cur)[kTilesPerSlice], int q1, int r1, uint4 (&nxt)[kTilesPerSlice],
+                  float (&ec)[kTilesPerSlice][8], float (&ep)[kTilesPerSlice][8]) {
     const int b = q / K, k = q - b * K;
-    if (r < N)
-      load(q, r + 1, nxt);
-    else if (q + Q < nG)
-      load(q + Q, 0, nxt);
-    if (pq >= 0) finish_prev();
+    // the previous row's words first: vmcnt retires in order, so waiting for them
+    // later must not also wait for the next slice's loads
+    unsigned long long wv[kRowWordsPerLane];
+    const unsigned long long* pw = nullptr;
+    if (pq >= 0) {
+      const int pb = pq / K, pk = pq - pb * K;
+      pw = part_row(p, pb, row_index(pk, pr));
+      wave_row_issue(p, pw, wv);
+    }
+    if (q1 < nG) load(q1, r1, nxt);
+    if (!full) mask_tail(cur, ci0, p.V);
     double sl;
-    const float kl = lane_exps<true, FULL>(p, cur, ci0, e, sl);
+    const float kl = lane_exps<true, true>(p, cur, ci0, ec, sl);
     publish_slice_stats(part_row(p, b, row_index(k, r)), x, kl, sl);
+    if (pq >= 0) finish_prev(wave_row_finish(p, pw, wv), ep);
     if (r == 0) {  // the target's terms wait in LDS for the row's normaliser
 #pragma unroll
       for (int t = 0; t < kTilesPerSlice; ++t)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) GL.pt[t * 8 + i][tid] = e[t][i];
+        for (int i = 0; i < 8; ++i) GL.pt[t * 8 + i][tid] = ec[t][i];
     }
     pq = q;
     pr = r;
     pkl = kl;
   };
+  if (slot_group(0) >= nG) return;
   uint4 va[kTilesPerSlice], vb[kTilesPerSlice];
-  int q = slot, r = 0;
-  auto advance = [&]() {
-    if (++r > N) {
-      r = 0;
-      q += Q;
+  float ea[kTilesPerSlice][8], eb[kTilesPerSlice][8];
+  int n = 0, r = 0;   // current job: the slot's group n, row r
+  int n1 = 0, r1 = 0; // next job
+  auto adv = [&](int& nn, int& rr) {
+    if (++rr > N) {
+      rr = 0;
+      ++nn;
     }
-    return q < nG;
   };
-  load(q, 0, va);
+  load(slot_group(0), 0, va);
+  adv(n1, r1);
+  bool last_in_a = true;
 #pragma unroll 1
   while (true) {
-    step(q, r, va, vb);
-    if (!advance()) break;
-    step(q, r, vb, va);
-    if (!advance()) break;
+    step(slot_group(n), r, va, slot_group(n1), r1, vb, ea, eb);
+    last_in_a = true;
+    adv(n, r);
+    adv(n1, r1);
+    if (slot_group(n) >= nG) break;
+    step(slot_group(n), r, vb, slot_group(n1), r1, va, eb, ea);
+    last_in_a = false;
+    adv(n, r);
+    adv(n1, r1);
+    if (slot_group(n) >= nG) break;
   }
-  finish_prev();
+  // the last row slice's terms are in ea or eb, whichever the last step filled
+  {
+    unsigned long long wv[kRowWordsPerLane];
+    const int pb = pq / K, pk = pq - pb * K;
+    const unsigned long long* pw = part_row(p, pb, row_index(pk, pr));
+    wave_row_issue(p, pw, wv);
+    const RowStats rs = wave_row_finish(p, pw, wv);
+    if (last_in_a)
+      finish_prev(rs, ea);
+    else
+      finish_prev(rs, eb);
+  }
 }
 
 // Slot g / S of the workgroups, member g % S (workgroups beyond the last full slot
 // and slots beyond the last group have no group work).
 __device__ __forceinline__ void gamma_groups(const Params& p, GammaLds& GL) {
   const int S = p.S, Q = gridDim.x / S, g = blockIdx.x;
-  if (g >= Q * S || g / S >= p.ngroups) return;
-  const int slot = g / S, x = g - slot * S;
-  if ((x + 1) * kSliceTok <= p.V)
-    gamma_member<true>(p, GL, slot, x);
-  else
-    gamma_member<false>(p, GL, slot, x);
+  if (g >= Q * S) return;
+  gamma_member(p, GL, g / S, g % S);
 }
 
 
