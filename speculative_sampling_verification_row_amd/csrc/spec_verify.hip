@@ -13,23 +13,23 @@
 //       pair (reference k, sum s) and publishes it as one 64-bit word.  The list
 //       is sequence-major, so sequences finish their statistics one after
 //       another.
-//   phase 1 -- units g, g + G, ... of the draw / gamma list.  A draw unit (one
-//       per slice of a sequence's rows) merges the sequence's statistics, takes
+//   phase 1 -- units g, g + G, ... of the draw list, one per slice of a
+//       sequence's rows.  A draw unit merges the sequence's statistics, takes
 //       every accept decision ([LT] §5.1, [CA] Key design 3), finds the first
-//       rejection A and publishes per-512-token sub-tile masses of the sampling
+//       rejection A and computes per-512-token sub-tile masses of the sampling
 //       weights of its slice of the row pair A ((pt - pd)+, Cactus's (h - pd)+)
-//       or of the bonus row pt; the unit of slice 0 also publishes the decision.
-//       A gamma unit publishes sum_x min(pt, pd_i) over its slice for all N
-//       drafters (the target slice stays in registers).
-//   phase 2 -- units g, g + G, ... of the final-step list: the inverse-CDF
-//       crossing, found from the sub-tile masses and a re-read of the one
-//       sub-tile that holds it ([LT] §9.1), or the HedgeSpec estimator and loss
-//       ([NB] Key designs 1-3).
+//       or of the bonus row pt.  It publishes its slice's total, reads the
+//       other slices' totals, and the unit whose slice holds the inverse-CDF
+//       crossing ([LT] §9.1) finds the token in the rows it still holds in
+//       registers.
+//   phase 2 -- (gamma calls) units g, g + G, ... of the HedgeSpec estimator and
+//       loss ([NB] Key designs 1-3).
 //
-// A phase-1 unit reads only phase-0 words and a phase-2 unit only phase-0 and
-// phase-1 words, and every workgroup finishes a phase before it starts the
-// next, so every wait ends (a wait is also bounded by the wall clock; a timeout
-// sets the workspace's fault word).
+// A draw unit reads phase-0 words and the totals of its own sequence's draw
+// units, and a phase-2 unit reads words of earlier phases; every workgroup
+// finishes a phase before it starts the next, and the draw units of a sequence
+// are at most one round of the grid apart, so every wait ends (a wait is also
+// bounded by the wall clock; a timeout sets the workspace's fault word).
 //
 // Cross-workgroup data is published with device-scope 64-bit stores of words
 // that are never zero, into a workspace that is zero before the call; a reader
@@ -64,7 +64,6 @@ constexpr unsigned long long kValid = 1ull << 63;        // published bit of an 
 constexpr int kStage = 8 * kThreads;  // statistics words staged in LDS at once
 constexpr int kRowCap = 256;          // merged rows held in LDS at once
 constexpr int kNoK = INT32_MIN;       // statistics word of a share with no finite logit
-constexpr int kDecWords = 5;          // words of a decision record
 constexpr int kNoToken = INT32_MIN;   // no preloaded drafted token
 
 // Everything a lane needs to turn logits into sampling weights.  Weights are kept
@@ -103,8 +102,9 @@ struct Params {
   int RT;      // of which target rows
   int S;       // slices per row
   int nsub;    // 512-token sub-tiles per row
-  int P1;      // phase-1 units per sequence
-  int P2;      // phase-2 units per sequence
+  int P1;      // phase-1 (draw) units per sequence
+  int P2;      // phase-2 (estimator) units per sequence
+  int nlast;   // gamma calls: steps per sequence that read its statistics (0: verify calls)
   int RS;      // statistics slices per sequence (R * S)
   int total0;  // slices of the statistics list (verify: B * R * S; gamma: the fused bonus rows, B * S or 0)
   int ngroups; // gamma groups (B * K): a position's target row and its N drafter rows
@@ -118,10 +118,9 @@ struct Params {
   float* loss;
   // workspace (all zero between calls)
   uint32_t* flags;            // [3]: fault word
-  uint32_t* done;             // [B] final steps finished (fused calls: two per sequence)
-  unsigned long long* dec;    // [B][kDecWords] draw decision records
+  uint32_t* done;             // [B] tickets of a gamma call's last steps
   unsigned long long* part;   // [B][R][S][kWaves] statistics words
-  unsigned long long* mass;   // [B][nsub] sub-tile masses (fp64 | kValid)
+  unsigned long long* tot;    // [B][kMaxSlices][kMaxSlices] draw slice totals, [reader][writer] (fp64 | kValid)
   unsigned long long* gpart;  // [B][K][N][S][kWaves] gamma partial sums (fp64 | kValid)
 };
 
@@ -439,23 +438,22 @@ __device__ __forceinline__ bool find_subtile(const double* subsum, int nsub, dou
   return s_star >= 0;
 }
 
-// Wave 0: the token in sub-tile s_star where the running mass passes x_rel
-// (or the sub-tile's last positive-mass token when x_rel is +inf).  Recomputes
-// the sub-tile's weights and lane scan exactly as the draw pass did.
+// Weights of one lane's 8-token chunk (chunk index ci; zero past the row's end)
+// and their sum in token order.  The mass pass and the token search both use it,
+// so a sub-tile's mass and its re-scan agree bit for bit.
 template <int MODE, bool SPECIAL>
-__device__ __forceinline__ int find_token(const uint16_t* trow, const uint16_t* drow, int V, const WeightCtx& w,
-                                          int s_star, double x_rel) {
-  const int lane = lane_id();
-  const int nchunks = (V + kVec - 1) / kVec;
-  const int ci = s_star * 64 + lane;
-  double wv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+__device__ __forceinline__ double chunk_weights(uint4 ct, uint4 cd, int ci, int V, const WeightCtx& w,
+                                                double wv[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) wv[e] = 0.0;
   double ls = 0.0;
+  const int nchunks = (V + kVec - 1) / kVec;
   if (ci < nchunks) {
     const int valid = V - ci * kVec;
     float zt[8], zd[8];
-    unpack8(as_chunks(trow)[ci], zt, valid);
+    unpack8(ct, zt, valid);
     if (MODE == W_RESID)
-      unpack8(as_chunks(drow)[ci], zd, valid);
+      unpack8(cd, zd, valid);
     else
 #pragma unroll
       for (int e = 0; e < 8; ++e) zd[e] = -__builtin_inff();
@@ -463,6 +461,17 @@ __device__ __forceinline__ int find_token(const uint16_t* trow, const uint16_t* 
 #pragma unroll
     for (int e = 0; e < 8; ++e) ls += wv[e];
   }
+  return ls;
+}
+
+// One wave over one sub-tile, lane l holding chunk ci (ct, cd): the token where
+// the running mass passes x_rel, or the sub-tile's last positive-mass token when
+// x_rel is +inf or rounding left no crossing; -1 when the sub-tile has no mass.
+template <int MODE, bool SPECIAL>
+__device__ __forceinline__ int subtile_token(uint4 ct, uint4 cd, int ci, int V, const WeightCtx& w, double x_rel) {
+  const int lane = lane_id();
+  double wv[8];
+  const double ls = chunk_weights<MODE, SPECIAL>(ct, cd, ci, V, w, wv);
   const double incl = wave_incl_scan(ls);
   const double excl = lane_prev(incl);
   const unsigned long long pos = __ballot(ls > 0.0);
@@ -496,13 +505,26 @@ __device__ __forceinline__ int find_token(const uint16_t* trow, const uint16_t* 
   return tok;
 }
 
-// Per-sub-tile masses of the sampling weights over tiles [t0, t0 + ntiles) of a
-// row (pair); lane 63 of each wave holds the sub-tile's inclusive scan total.
-// A draw slice publishes them (TO_GLOBAL); the whole-row fallback keeps them in LDS.
-template <int MODE, bool SPECIAL, bool TO_GLOBAL, int kBatch>
-__device__ __forceinline__ void weight_subtiles(const uint16_t* trow, const uint16_t* drow, int V, const WeightCtx& w,
-                                                int t0, int ntiles, double* lds_sub, unsigned long long* glob_sub,
-                                                int nsub) {
+// Wave 0: the token in sub-tile s_star of a row (pair), read again from memory.
+template <int MODE, bool SPECIAL>
+__device__ __forceinline__ int find_token(const uint16_t* trow, const uint16_t* drow, int V, const WeightCtx& w,
+                                          int s_star, double x_rel) {
+  const int nchunks = (V + kVec - 1) / kVec;
+  const int ci = s_star * 64 + lane_id();
+  uint4 ct = make_uint4(0u, 0u, 0u, 0u), cd = ct;
+  if (ci < nchunks) {
+    ct = as_chunks(trow)[ci];
+    if (MODE == W_RESID) cd = as_chunks(drow)[ci];
+  }
+  return subtile_token<MODE, SPECIAL>(ct, cd, ci, V, w, x_rel);
+}
+
+// Per-sub-tile masses of the sampling weights over tiles [0, ntiles) of a row
+// into LDS (the whole-row draw of a rejection whose residual has no mass).
+template <int MODE, bool SPECIAL>
+__device__ __forceinline__ void row_subtiles(const uint16_t* trow, const uint16_t* drow, int V, const WeightCtx& w,
+                                             int ntiles, double* lds_sub, int nsub) {
+  constexpr int kBatch = 4;
   const uint4* tr = as_chunks(trow);
   const uint4* dr = as_chunks(drow);
   const int nchunks = (V + kVec - 1) / kVec;
@@ -512,7 +534,9 @@ __device__ __forceinline__ void weight_subtiles(const uint16_t* trow, const uint
     uint4 vt[kBatch], vd[kBatch];
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
-      const int ci = (t0 + j0 + q) * kThreads + tid;
+      const int ci = (j0 + q) * kThreads + tid;
+      vt[q] = make_uint4(0u, 0u, 0u, 0u);
+      vd[q] = vt[q];
       if (j0 + q < ntiles && ci < nchunks) {
         vt[q] = tr[ci];
         if (MODE == W_RESID) vd[q] = dr[ci];
@@ -521,32 +545,11 @@ __device__ __forceinline__ void weight_subtiles(const uint16_t* trow, const uint
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
       if (j0 + q >= ntiles) break;  // uniform over the workgroup
-      const int jt = t0 + j0 + q;
-      const int ci = jt * kThreads + tid;
-      double lsum = 0.0;
-      if (ci < nchunks) {
-        const int valid = V - ci * kVec;
-        float zt[8], zd[8];
-        unpack8(vt[q], zt, valid);
-        if (MODE == W_RESID)
-          unpack8(vd[q], zd, valid);
-        else
-#pragma unroll
-          for (int e = 0; e < 8; ++e) zd[e] = -__builtin_inff();
-        // same element order as find_token's lane sum, so the two agree bit for bit
-        double wv[8];
-        weights8<MODE, SPECIAL>(w, zt, zd, ci * kVec, wv);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) lsum += wv[e];
-      }
+      double wv[8];
+      const double lsum = chunk_weights<MODE, SPECIAL>(vt[q], vd[q], (j0 + q) * kThreads + tid, V, w, wv);
       const double incl = wave_incl_scan(lsum);
-      const int s = jt * kWaves + wave_id();
-      if (lane_id() == 63 && s < nsub) {
-        if (TO_GLOBAL)
-          st_agent_u64(&glob_sub[s], pack_f64(incl));
-        else
-          lds_sub[s] = incl;
-      }
+      const int s = (j0 + q) * kWaves + wave_id();
+      if (lane_id() == 63 && s < nsub) lds_sub[s] = incl;
     }
   }
 }
@@ -570,6 +573,7 @@ struct Lds {
   MergeLds m;
   DecideLds dl;
   double subsum[kMaxSub];
+  double tot[kMaxSlices];
   double gsum[kRowCap];
   double arat[kRowCap];
   int flag;
@@ -677,15 +681,21 @@ __device__ __forceinline__ void decide(const Params& p, int b, bool write_output
 // Units
 // ---------------------------------------------------------------------------
 
-// A sequence's last step: clear the statistics words it published.  Fused gamma
-// calls have two last steps (estimator and draw); the second one clears.
-__device__ __forceinline__ void finish_sequence(const Params& p, int b, Lds& L) {
-  int last = 1;
-  if (p.P2 > 1) {
-    stores_complete();  // this step is done with the sequence's words before it takes its ticket
+// A sequence's last step: clear its statistics words once every step that reads
+// them is done.  In a verify call (nlast = 0) the draw unit passed as `clearer`
+// knows this, having read every draw unit's total (each unit publishes its total
+// after its last read of the words).  In a gamma call, the steps that read them
+// (nlast: the draw units of a fused call and the estimator) take a ticket and
+// the last one clears.
+__device__ __forceinline__ void finish_sequence(const Params& p, int b, bool clearer, Lds& L) {
+  int last = clearer ? 1 : 0;
+  if (p.nlast == 1) {
+    last = 1;
+  } else if (p.nlast > 1) {
+    stores_complete();  // this step's own words are out before it takes its ticket
     __syncthreads();
     if (threadIdx.x == 0) {
-      const int l = ticket(&p.done[b]) == static_cast<uint32_t>(p.P2 - 1) ? 1 : 0;
+      const int l = ticket(&p.done[b]) == static_cast<uint32_t>(p.nlast - 1) ? 1 : 0;
       if (l) st_agent(&p.done[b], 0u);
       L.flag = l;
     }
@@ -700,169 +710,169 @@ __device__ __forceinline__ void finish_sequence(const Params& p, int b, Lds& L) 
   __syncthreads();
 }
 
-// Decision record: kDecWords words, each non-zero once written, so that a reader
-// needs no ordering between them and waits for each word: word 0 holds the
-// integer fields and the published bit, words 1.. the bitwise complement of a
-// value (zero only for an all-ones NaN, which no step produces).
-__device__ __forceinline__ unsigned long long dec_word(double v) {
-  return ~static_cast<unsigned long long>(__double_as_longlong(v));
-}
-__device__ __forceinline__ double dec_value(unsigned long long w) { return __longlong_as_double(static_cast<long long>(~w)); }
-
-__device__ __forceinline__ void store_decision(unsigned long long* rec, const Decision& d) {
-  st_agent_u64(rec + 1, dec_word(d.w.r));
-  st_agent_u64(rec + 2, dec_word(d.w.s_scale));
-  st_agent_u64(rec + 3, dec_word(d.w.hn));
-  st_agent_u64(rec + 4, ~(static_cast<unsigned long long>(__float_as_uint(d.w.kt)) |
-                          (static_cast<unsigned long long>(__float_as_uint(d.w.kd)) << 32)));
-  const unsigned long long head = static_cast<unsigned long long>(d.A + 1) |
-                                  (static_cast<unsigned long long>(d.draw_row) << 8) |
-                                  (static_cast<unsigned long long>(d.pair) << 16) |
-                                  (static_cast<unsigned long long>(d.w.special) << 17) |
-                                  (static_cast<unsigned long long>(d.w.mode) << 18) |
-                                  (static_cast<unsigned long long>(static_cast<uint32_t>(d.w.n + 1)) << 32) | kValid;
-  st_agent_u64(rec, head);
+// Wave: the inverse-CDF crossing among up to 64 masses, lane i holding mass i
+// (0 past the last): the first i whose running mass (a wave scan) passes x, with
+// x made relative to the mass before it; when rounding leaves no crossing, the
+// last i with mass and x = +inf.  -1 when there is no mass.  Every wave that
+// calls it on the same masses gets the same answer.
+__device__ __forceinline__ int wave_crossing(double m, double incl, double& x) {
+  const unsigned long long hit = __ballot(incl > x);
+  if (hit != 0ull) {
+    const int i = __ffsll(static_cast<long long>(hit)) - 1;
+    x -= readlane_f64(lane_prev(incl), i);
+    return i;
+  }
+  const unsigned long long pos = __ballot(m > 0.0);
+  x = __builtin_inf();
+  return pos == 0ull ? -1 : 63 - __clzll(static_cast<long long>(pos));
 }
 
-// Thread 0: wait for a decision record and decode it.  A timed-out wait gives an
-// invalid decision (A = -1).
-__device__ __forceinline__ Decision load_decision(const Params& p, unsigned long long* rec) {
-  Decision d;
-  unsigned long long w[kDecWords];
-#pragma unroll
-  for (int i = 0; i < kDecWords; ++i) w[i] = ld_agent_u64(rec + i);  // one round trip when all are written
-#pragma unroll
-  for (int i = 0; i < kDecWords; ++i)
-    if (w[i] == 0ull) w[i] = poll_word(p.flags, rec + i);
-  const unsigned long long head = w[0];
-  d.A = static_cast<int>(head & 0xffull) - 1;
-  d.draw_row = static_cast<int>((head >> 8) & 0xffull);
-  d.pair = static_cast<int>((head >> 16) & 1ull);
-  d.w.special = static_cast<int>((head >> 17) & 1ull);
-  d.w.mode = static_cast<int>((head >> 18) & 3ull);
-  d.w.n = static_cast<int>(static_cast<uint32_t>(head >> 32)) - 1;
-  d.w.c = p.c;
-  d.w.r = dec_value(w[1]);
-  d.w.s_scale = dec_value(w[2]);
-  d.w.hn = dec_value(w[3]);
-  const unsigned long long kk = ~w[4];
-  d.w.kt = __uint_as_float(static_cast<uint32_t>(kk));
-  d.w.kd = __uint_as_float(static_cast<uint32_t>(kk >> 32));
-  bool lost = false;
-#pragma unroll
-  for (int i = 0; i < kDecWords; ++i) lost |= w[i] == 0ull;  // a wait timed out
-  if (lost || d.A > p.K || d.draw_row > p.K || (d.pair && d.draw_row >= p.K)) d.A = -1;
-  return d;
+// Wave: the crossing slice of a sequence's draw, lane i holding slice i's total:
+// x = u * Z with Z the sum of the totals.  -1 when Z is not positive.
+__device__ __forceinline__ int crossing_slice(double t, double u, double& x_rel) {
+  const double incl = wave_incl_scan(t);
+  const double Z = readlane_f64(incl, 63);
+  if (!(Z > 0.0)) return -1;
+  x_rel = u * Z;
+  return wave_crossing(t, incl, x_rel);
 }
 
-// Draw unit: the sequence's decisions, then the sub-tile masses of slice x of its
-// draw row(s).  Unit x = 0 also writes the per-position outputs and the decision
-// record.  A sequence with no valid draw publishes zero masses.  `pre_n`: the drafted token of position threadIdx.x,
-// loaded ahead of time, or kNoToken.
+constexpr int kSliceSub = kTilesPerSlice * kWaves;  // 512-token sub-tiles of a slice
+
+// Draw unit x publishes its slice total (the wave scan of its sub-tile masses
+// L.subsum[0..kSliceSub)) to each unit y of its sequence as word tot[b][y][x],
+// reads the words addressed to it (clearing them: it is their only reader), and
+// returns the crossing slice of the sequence's draw (-1 for none).
+__device__ __forceinline__ int exchange_totals(const Params& p, int b, int x, double u, double& x_rel, Lds& L) {
+  const int tid = threadIdx.x;
+  unsigned long long* tw = p.tot + static_cast<size_t>(b) * kMaxSlices * kMaxSlices;
+  if (tid < 64) {  // wave 0
+    const double T = readlane_f64(wave_incl_scan(tid < kSliceSub ? L.subsum[tid] : 0.0), 63);
+    if (tid < p.S) st_agent_u64(tw + tid * kMaxSlices + x, pack_f64(T));
+  }
+  if (tid < p.S) {
+    unsigned long long* src = tw + x * kMaxSlices + tid;
+    unsigned long long w = ld_agent_u64(src);
+    if (w == 0ull) w = poll_word(p.flags, src);
+    L.tot[tid] = unpack_f64(w);
+    st_agent_u64(src, 0ull);
+  }
+  __syncthreads();
+  const int lane = lane_id();
+  return crossing_slice(lane < p.S ? L.tot[lane] : 0.0, u, x_rel);
+}
+
+// Draw unit x of sequence b, decision d made: the sub-tile masses of slice x of
+// the draw row (pair), the totals exchanged, and, if the crossing falls in this
+// slice, the token from the rows still held in registers.  Returns the crossing
+// slice (-1: the draw has no mass).
+template <int MODE, bool SPECIAL>
+__device__ __forceinline__ int draw_slice(const Params& p, int b, int x, const Decision& d, Lds& L) {
+  const int tid = threadIdx.x, wave = wave_id();
+  const uint16_t* trow = target_row(p, b, d.draw_row);
+  const uint16_t* drow = d.pair ? draft_row(p, b, draw_drafter(p, b), d.draw_row) : trow;
+  const uint4* tr = as_chunks(trow);
+  const uint4* dr = as_chunks(drow);
+  const int nchunks = (p.V + kVec - 1) / kVec;
+  const int c0 = x * kTilesPerSlice * kThreads + tid;  // this lane's chunk of the slice's first tile
+  uint4 vt[kTilesPerSlice], vd[kTilesPerSlice];
+#pragma unroll
+  for (int q = 0; q < kTilesPerSlice; ++q) {
+    const int ci = c0 + q * kThreads;
+    vt[q] = make_uint4(0u, 0u, 0u, 0u);
+    vd[q] = vt[q];
+    if (ci < nchunks) {
+      vt[q] = tr[ci];
+      if (MODE == W_RESID) vd[q] = dr[ci];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < kTilesPerSlice; ++q) {
+    double wv[8];
+    const double ls = chunk_weights<MODE, SPECIAL>(vt[q], vd[q], c0 + q * kThreads, p.V, d.w, wv);
+    const double incl = wave_incl_scan(ls);
+    if (lane_id() == 63) L.subsum[q * kWaves + wave] = incl;
+  }
+  __syncthreads();
+  double x_rel = 0.0;
+  const int xs = exchange_totals(p, b, x, static_cast<double>(p.u[b * (p.K + 1) + d.draw_row]), x_rel, L);
+  if (xs != x) return xs;
+  // this slice's total is positive, so one of its sub-tiles has mass; the scan is
+  // the one that formed the total
+  const double m = lane_id() < kSliceSub ? L.subsum[lane_id()] : 0.0;
+  const int ss = wave_crossing(m, wave_incl_scan(m), x_rel);
+  const int qs = ss / kWaves;
+  if (wave == ss - qs * kWaves) {
+    uint4 ct = vt[0], cd = vd[0];
+#pragma unroll
+    for (int q = 1; q < kTilesPerSlice; ++q)
+      if (q == qs) {
+        ct = vt[q];
+        cd = vd[q];
+      }
+    const int tok = subtile_token<MODE, SPECIAL>(ct, cd, c0 + qs * kThreads, p.V, d.w, x_rel);
+    if (lane_id() == 0) {
+      p.accepted_len[b] = tok >= 0 ? d.A : -1;
+      p.out_token[b] = tok >= 0 ? tok : -1;
+    }
+  }
+  return xs;
+}
+
+// A rejection whose residual has no mass: the token is drawn from the position's
+// target h instead (whole row; rare).
+template <bool SPECIAL>
+__device__ __forceinline__ void target_h_draw(const Params& p, int b, const Decision& d, Lds& L) {
+  const uint16_t* trow = target_row(p, b, d.draw_row);
+  const double uu = static_cast<double>(p.u[b * (p.K + 1) + d.draw_row]);
+  WeightCtx wh = d.w;
+  wh.mode = W_TARGET_H;
+  __syncthreads();  // every thread is done with the slice's masses in LDS
+  row_subtiles<W_TARGET_H, SPECIAL>(trow, trow, p.V, wh, (p.V + kTile - 1) / kTile, L.subsum, p.nsub);
+  __syncthreads();
+  if (wave_id() == 0) {
+    int s_star = -1;
+    double x_rel = 0.0;
+    int tok = -1;
+    if (find_subtile(L.subsum, p.nsub, uu, s_star, x_rel))
+      tok = find_token<W_TARGET_H, SPECIAL>(trow, trow, p.V, wh, s_star, x_rel);
+    if (lane_id() == 0) {
+      p.accepted_len[b] = tok >= 0 ? d.A : -1;
+      p.out_token[b] = tok >= 0 ? tok : -1;
+    }
+  }
+}
+
+// Draw unit x of sequence b.  Unit 0 also writes the per-position outputs, the
+// outputs of a sequence with no valid draw, and the outputs of a draw with no
+// mass.  `pre_n`: the drafted token of position threadIdx.x, loaded ahead of
+// time, or kNoToken.
 __device__ __forceinline__ void unit_draw(const Params& p, int b, int x, int pre_n, Lds& L) {
   decide(p, b, x == 0, pre_n, L);
   const Decision d = L.dl.d;
-  unsigned long long* rec = p.dec + static_cast<size_t>(b) * kDecWords;
-  if (x == 0 && threadIdx.x == 0) store_decision(rec, d);
-  unsigned long long* out = p.mass + static_cast<size_t>(b) * p.nsub;
-  const int t0 = x * kTilesPerSlice;
-  if (d.A >= 0) {
-    const uint16_t* trow = target_row(p, b, d.draw_row);
-    const uint16_t* drow = d.pair ? draft_row(p, b, draw_drafter(p, b), d.draw_row) : trow;
-    if (!d.pair)
-      weight_subtiles<W_TARGET, false, true, kTilesPerSlice>(trow, drow, p.V, d.w, t0, kTilesPerSlice, nullptr, out,
-                                                             p.nsub);
-    else if (d.w.special)
-      weight_subtiles<W_RESID, true, true, kTilesPerSlice>(trow, drow, p.V, d.w, t0, kTilesPerSlice, nullptr, out,
-                                                           p.nsub);
-    else
-      weight_subtiles<W_RESID, false, true, kTilesPerSlice>(trow, drow, p.V, d.w, t0, kTilesPerSlice, nullptr, out,
-                                                            p.nsub);
+  int xs;
+  if (d.A < 0) {
+    // no draw: the totals are still exchanged, so that unit 0 knows when to clear
+    if (threadIdx.x < kSliceSub) L.subsum[threadIdx.x] = 0.0;
+    __syncthreads();
+    double x_rel = 0.0;
+    xs = exchange_totals(p, b, x, 0.0, x_rel, L);
+    if (x == 0 && threadIdx.x == 0) {
+      p.accepted_len[b] = -1;
+      p.out_token[b] = -1;
+    }
   } else {
-    const int s = t0 * kWaves + threadIdx.x;
-    if (threadIdx.x < kTilesPerSlice * kWaves && s < p.nsub) st_agent_u64(out + s, pack_f64(0.0));
-  }
-  __syncthreads();
-}
-
-// Final step of a draw: the inverse-CDF crossing and the output token.
-__device__ __forceinline__ void unit_final(const Params& p, int b, Lds& L) {
-  const int tid = threadIdx.x;
-  unsigned long long* rec = p.dec + static_cast<size_t>(b) * kDecWords;
-  unsigned long long* msrc = p.mass + static_cast<size_t>(b) * p.nsub;
-  // the masses and the record are read together
-  unsigned long long w[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int q = tid + e * kThreads;
-    w[e] = 1ull;
-    if (q < p.nsub) w[e] = ld_agent_u64(msrc + q);
-  }
-  if (tid == 0) L.dl.d = load_decision(p, rec);
-  bool missing = false;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int q = tid + e * kThreads;
-    if (q < p.nsub) L.subsum[q] = unpack_f64(w[e]);
-    missing |= w[e] == 0ull;
-  }
-  if (missing) {  // not every mass was published yet (rare): read this thread's words again, waiting
-    for (int q = tid; q < p.nsub; q += kThreads) L.subsum[q] = unpack_f64(poll_word(p.flags, msrc + q));
-  }
-  __syncthreads();
-  const Decision d = L.dl.d;
-  const bool ok = d.A >= 0;
-  int token = -1;
-  if (ok) {
-    const uint16_t* trow = target_row(p, b, d.draw_row);
-    const uint16_t* drow = d.pair ? draft_row(p, b, draw_drafter(p, b), d.draw_row) : trow;
-    const double uu = static_cast<double>(p.u[b * (p.K + 1) + d.draw_row]);
-    if (wave_id() == 0) {
-      int s_star = -1;
-      double x_rel = 0.0;
-      const bool found = find_subtile(L.subsum, p.nsub, uu, s_star, x_rel);
-      int tok = -2;  // -2: no mass (zero residual)
-      if (found)
-        tok = !d.pair        ? find_token<W_TARGET, false>(trow, drow, p.V, d.w, s_star, x_rel)
-              : d.w.special ? find_token<W_RESID, true>(trow, drow, p.V, d.w, s_star, x_rel)
-                            : find_token<W_RESID, false>(trow, drow, p.V, d.w, s_star, x_rel);
-      if (lane_id() == 0) L.flag = tok;
-    }
-    __syncthreads();
-    token = L.flag;
-    __syncthreads();
-    if (token == -2) {
-      // zero residual mass on a rejection: draw from the position's target h instead (whole row, rare)
-      WeightCtx wh = d.w;
-      wh.mode = W_TARGET_H;
-      const int ntiles = (p.V + kTile - 1) / kTile;
-      if (wh.special)
-        weight_subtiles<W_TARGET_H, true, false, 4>(trow, trow, p.V, wh, 0, ntiles, L.subsum, nullptr, p.nsub);
+    xs = !d.pair       ? draw_slice<W_TARGET, false>(p, b, x, d, L)
+         : d.w.special ? draw_slice<W_RESID, true>(p, b, x, d, L)
+                       : draw_slice<W_RESID, false>(p, b, x, d, L);
+    if (xs < 0 && x == 0) {
+      if (d.w.special)
+        target_h_draw<true>(p, b, d, L);
       else
-        weight_subtiles<W_TARGET_H, false, false, 4>(trow, trow, p.V, wh, 0, ntiles, L.subsum, nullptr, p.nsub);
-      __syncthreads();
-      if (wave_id() == 0) {
-        int s_star = -1;
-        double x_rel = 0.0;
-        int tok = -1;
-        if (find_subtile(L.subsum, p.nsub, uu, s_star, x_rel))
-          tok = wh.special ? find_token<W_TARGET_H, true>(trow, trow, p.V, wh, s_star, x_rel)
-                           : find_token<W_TARGET_H, false>(trow, trow, p.V, wh, s_star, x_rel);
-        if (lane_id() == 0) L.flag = tok;
-      }
-      __syncthreads();
-      token = L.flag;
+        target_h_draw<false>(p, b, d, L);
     }
   }
-  // every draw unit has published (all masses were read above): clear the masses and the record
-  for (int q = tid; q < p.nsub; q += kThreads) st_agent_u64(msrc + q, 0ull);
-  if (tid < kDecWords) st_agent_u64(rec + tid, 0ull);
-  if (tid == 0) {
-    const bool good = ok && token >= 0;
-    p.accepted_len[b] = good ? d.A : -1;
-    p.out_token[b] = good ? token : -1;
-  }
-  finish_sequence(p, b, L);
+  finish_sequence(p, b, (xs < 0 ? 0 : xs) == x, L);
 }
 
 // ---------------------------------------------------------------------------
@@ -1205,7 +1215,7 @@ __device__ __forceinline__ void unit_estimate(const Params& p, int b, Lds& L) {
   // every gamma unit of the sequence has published (all were read above): clear them
   unsigned long long* gw = p.gpart + static_cast<size_t>(b) * K * N * p.S * kWaves;
   for (int q = tid; q < K * N * p.S * kWaves; q += kThreads) st_agent_u64(gw + q, 0ull);
-  finish_sequence(p, b, L);
+  finish_sequence(p, b, false, L);
 }
 
 // ---------------------------------------------------------------------------
@@ -1219,14 +1229,7 @@ __device__ __forceinline__ void run_unit1(const Params& p, int u, int pre_n, Lds
   unit_draw(p, b, u - b * p.P1, pre_n, L);
 }
 
-__device__ __forceinline__ void run_unit2(const Params& p, int v, Lds& L) {
-  const int b = v / p.P2;
-  const int kind = v - b * p.P2;
-  if (p.mode == MODE_GAMMA && kind == 0)
-    unit_estimate(p, b, L);
-  else
-    unit_final(p, b, L);
-}
+__device__ __forceinline__ void run_unit2(const Params& p, int v, Lds& L) { unit_estimate(p, v / p.P2, L); }
 
 // Phase 0 share of the later-dispatched half of the workgroups, relative to an
 // even share.  Waves dispatched first win the memory arbitration, so the first
@@ -1317,10 +1320,10 @@ __device__ __forceinline__ void static_phase(const Params& p) {
   }
 }
 
-// Phase 0 (static_phase), then phase 1 and phase 2: units g, g + G, ... of each
-// list.  A phase-1 unit waits only for phase-0 words and a phase-2 unit only for
-// phase-0 and phase-1 words, and every workgroup finishes a phase before it
-// starts the next, so every wait ends.
+// The gamma groups (gamma calls), phase 0 (static_phase), then phase 1 and phase
+// 2: units g, g + G, ... of each list.  A draw unit waits for phase-0 words and
+// for the totals of its sequence's other draw units, which are less than one
+// round of the grid away; a phase-2 unit waits only for earlier phases' words.
 // LDS of the units, or of the gamma groups (which run before any unit)
 union KernelLds {
   Lds units;
@@ -1426,7 +1429,7 @@ __global__ void fill_zero_kernel(uint32_t* p, size_t n) {
 
 struct Shape {
   int B, K, N, V, mode, fused;
-  int R, RT, S, nsub, P1, P2;
+  int R, RT, S, nsub, P1, P2, nlast;
   int64_t RS, total0, ngroups;  // checked below 2^31 before a launch
 };
 
@@ -1443,7 +1446,8 @@ static Shape make_shape(int B, int K, int N, int V, int mode, int fused) {
   s.S = (V + kSliceTok - 1) / kSliceTok;
   s.nsub = (V + kSub - 1) / kSub;
   s.P1 = mode == MODE_VERIFY || fused ? s.S : 0;
-  s.P2 = mode == MODE_VERIFY ? 1 : 1 + fused;
+  s.P2 = mode == MODE_VERIFY ? 0 : 1;
+  s.nlast = mode == MODE_VERIFY ? 0 : s.P1 + s.P2;
   s.RS = static_cast<int64_t>(s.R) * s.S;
   // gamma calls: the groups take the rows of positions 0..K-1; the list holds the bonus rows
   s.total0 = mode == MODE_VERIFY ? static_cast<int64_t>(B) * s.RS : (fused ? static_cast<int64_t>(B) * s.S : 0);
@@ -1454,7 +1458,7 @@ static Shape make_shape(int B, int K, int N, int V, int mode, int fused) {
 // Byte offsets of the workspace regions.  They depend on (B, K, N, mode) only
 // (every region is sized for the longest row), so one workspace serves every V.
 struct WsLayout {
-  size_t flags, done, dec, part, mass, gpart, total;
+  size_t flags, done, part, tot, gpart, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -1467,12 +1471,10 @@ static WsLayout ws_layout(const Shape& s) {
   o = align256(o + 16);
   L.done = o;
   o = align256(o + 4 * B);
-  L.dec = o;
-  o = align256(o + 8 * B * kDecWords);
   L.part = o;
   o = align256(o + 8 * B * static_cast<size_t>(s.R) * kMaxSlices * kWaves);
-  L.mass = o;
-  o = align256(o + 8 * B * static_cast<size_t>(kMaxSub));
+  L.tot = o;
+  o = align256(o + 8 * B * static_cast<size_t>(kMaxSlices) * kMaxSlices);
   L.gpart = o;
   o = align256(o + (s.mode == MODE_GAMMA ? 8 * B * static_cast<size_t>(s.K) * s.N * kMaxSlices * kWaves : 0));
   L.total = o;
@@ -1489,9 +1491,8 @@ static int bind_workspace(Params& p, const Shape& s, void* ws, size_t bytes) {
   char* base = static_cast<char*>(ws);
   p.flags = reinterpret_cast<uint32_t*>(base + L.flags);
   p.done = reinterpret_cast<uint32_t*>(base + L.done);
-  p.dec = reinterpret_cast<unsigned long long*>(base + L.dec);
   p.part = reinterpret_cast<unsigned long long*>(base + L.part);
-  p.mass = reinterpret_cast<unsigned long long*>(base + L.mass);
+  p.tot = reinterpret_cast<unsigned long long*>(base + L.tot);
   p.gpart = reinterpret_cast<unsigned long long*>(base + L.gpart);
   return SPEC_OK;
 }
@@ -1517,6 +1518,7 @@ static void plan_units(Params& p, const Shape& s) {
   p.nsub = s.nsub;
   p.P1 = s.P1;
   p.P2 = s.P2;
+  p.nlast = s.nlast;
   p.RS = static_cast<int>(s.RS);
   p.total0 = static_cast<int>(s.total0);
   p.ngroups = static_cast<int>(s.ngroups);
@@ -1529,14 +1531,14 @@ static int launch_flow(Params& p, const Shape& s, hipStream_t stream) {
     return SPEC_ERR_SHAPE;
   int grid = resident_workgroups();
   if (grid <= 0) return SPEC_ERR_HIP;
-  // every workgroup is resident at once (the schedule's waits rely on it); a gamma
-  // call needs at least one slot of S workgroups
-  if (s.mode == MODE_GAMMA && grid < s.S) return SPEC_ERR_SHAPE;
   int64_t want = s.total0;
   if (s.ngroups * s.S > want) want = s.ngroups * s.S;
   if (static_cast<int64_t>(s.B) * s.P1 > want) want = static_cast<int64_t>(s.B) * s.P1;
   if (static_cast<int64_t>(s.B) * s.P2 > want) want = static_cast<int64_t>(s.B) * s.P2;
   if (grid > want) grid = static_cast<int>(want);
+  // every workgroup is resident at once (the schedule's waits rely on it); a gamma
+  // slot and a sequence's draw units need S workgroups at once
+  if ((s.mode == MODE_GAMMA || s.P1 > 0) && grid < s.S) return SPEC_ERR_SHAPE;
   plan_units(p, s);
   hipLaunchKernelGGL(flow_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;

@@ -27,8 +27,8 @@ int main() {
               const size_t part_words = static_cast<size_t>(B) * s.R * s.S * kWaves;
               const size_t gpart_words = mode == MODE_GAMMA ? static_cast<size_t>(B) * K * N * s.S * kWaves : 0;
               const bool ok = L.flags == 0 && L.done >= 16 && L.done + 4 * static_cast<size_t>(B) <= L.part &&
-                              L.part + 8 * part_words <= L.mass &&
-                              L.mass + 8 * static_cast<size_t>(B) * s.nsub <= L.gpart &&
+                              L.part + 8 * part_words <= L.tot &&
+                              L.tot + 8 * static_cast<size_t>(B) * kMaxSlices * kMaxSlices <= L.gpart &&
                               L.gpart + 8 * gpart_words <= L.total && L.total <= total && s.nsub <= kMaxSub &&
                               s.S <= kMaxSlices;
               if (!ok) {

@@ -53,10 +53,10 @@ def test_workspace_bytes_layout(lib):
     a = lib.spec_workspace_bytes(64, 5, 1)
     b = lib.spec_workspace_bytes(64, 8, 21)
     assert a % 256 == 0 and b % 256 == 0 and b > a
-    # statistics words of 2K+1 rows x 64 slices x 4 waves + sub-tile masses of the longest row
-    assert a >= 8 * 64 * 11 * 64 * 4 + 8 * 64 * 2048
-    # gamma: (K+1 + N K) rows of statistics words + gamma partial sums (K N x 64 slices)
-    assert b >= 8 * 64 * (9 + 21 * 8) * 64 * 4 + 8 * 64 * 8 * 21 * 64
+    # statistics words of 2K+1 rows x 64 slices x 4 waves + draw slice totals (64 readers x 64 slices)
+    assert a >= 8 * 64 * 11 * 64 * 4 + 8 * 64 * 64 * 64
+    # gamma: (K+1 + N K) rows of statistics words + gamma partial sums (K N x 64 slices x 4 waves)
+    assert b >= 8 * 64 * (9 + 21 * 8) * 64 * 4 + 8 * 64 * 8 * 21 * 64 * 4
 
 
 P = ctypes.c_void_p

@@ -33,6 +33,8 @@ def run_gamma(binding, x, fused=False, T=1.0):
                                             workspace=ws, **kw)
     torch.cuda.synchronize()
     assert binding.workspace_fault(ws) == 0, "kernel reported an internal consistency fault"
+    # every word the call published was cleared by its last reader
+    assert int(ws.count_nonzero().item()) == 0, "workspace not left zero"
     return {k: to_np(v) for k, v in out.items()}
 
 

@@ -40,6 +40,8 @@ def run_verify(binding, x, T=1.0, delta=None, ws=None):
         A, o, m, g = binding.spec_cactus_verify(t, d, tok, r, u, delta, T, workspace=ws)
     torch.cuda.synchronize()
     assert binding.workspace_fault(ws) == 0, "kernel reported an internal consistency fault"
+    # every word the call published was cleared by its last reader
+    assert int(ws.count_nonzero().item()) == 0, "workspace not left zero"
     return to_np(A), to_np(o), to_np(m), to_np(g)
 
 
