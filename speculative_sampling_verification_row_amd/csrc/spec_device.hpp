@@ -56,6 +56,19 @@ __device__ __forceinline__ void unpack8(const uint4 v, float z[8], int valid) {
   }
 }
 
+// Raw buffer access to a row: the descriptor covers `bytes` bytes from `base`,
+// and a load past them reads zero.  A load names its address as a per-lane byte
+// offset plus a wave-uniform one, so eight loads of a lane share one address
+// register.  Word 3 of the descriptor is the gfx9 raw-buffer format (32-bit
+// data format, no swizzle, no index stride).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_buffer(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t lane_off, uint32_t uniform_off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(lane_off), static_cast<int>(uniform_off), 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 __device__ __forceinline__ float bf16_at(const uint16_t* row, int idx) {
   return __uint_as_float(static_cast<uint32_t>(row[idx]) << 16);
 }

@@ -108,6 +108,8 @@ struct Params {
   int RS;      // statistics slices per sequence (R * S)
   int total0;  // slices of the statistics list (verify: B * R * S; gamma: the fused bonus rows, B * S or 0)
   int ngroups; // gamma groups (B * K): a position's target row and its N drafter rows
+  int ncu;     // compute units; workgroup g sits in dispatch slot g / ncu
+  int slots;   // workgroups per compute unit in this launch (1: no weighting)
   // outputs
   int32_t* accepted_len;
   int32_t* out_token;
@@ -182,13 +184,14 @@ __device__ __forceinline__ double unpack_f64(unsigned long long w) {
 
 // Re-read a word until it is published.  After the wait bound (or once another
 // wait has timed out) the fault word is set and 0 is returned.
+template <int kSleep = 2>
 __device__ __forceinline__ unsigned long long poll_word(uint32_t* flags, unsigned long long* a) {
   unsigned long long w = ld_agent_u64(a);
   if (w != 0ull) return w;
   const unsigned long long t0 = wall_clock64();
   for (uint32_t n = 1;; ++n) {
     if ((n & 7u) == 0u && ld_agent(&flags[3]) != 0u) return 0ull;  // another wait timed out
-    __builtin_amdgcn_s_sleep(2);
+    __builtin_amdgcn_s_sleep(kSleep);
     w = ld_agent_u64(a);
     if (w != 0ull) return w;
     if (wall_clock64() - t0 > kWaitTicks) {
@@ -203,7 +206,7 @@ __device__ __forceinline__ unsigned long long poll_word(uint32_t* flags, unsigne
 // ---------------------------------------------------------------------------
 
 struct SliceLoc {
-  const uint4* row;
+  __amdgpu_buffer_rsrc_t row;  // the row's chunks (loads past its last chunk read zero)
   int c0;                   // first chunk of the slice
   int full;                 // every chunk of the slice lies inside the row and holds 8 tokens
   unsigned long long* out;  // the slice's kWaves statistics words
@@ -228,65 +231,70 @@ __device__ __forceinline__ SliceLoc slice_loc(const Params& p, int sig) {
     r = order_row(p, i);
   }
   SliceLoc L;
-  L.row = as_chunks(stat_row(p, b, r));
+  L.row = row_buffer(stat_row(p, b, r), static_cast<uint32_t>((p.V + kVec - 1) / kVec) * 16u);
   L.c0 = x * kSliceChunks;
   L.full = (x + 1) * kSliceTok <= p.V;
   L.out = part_row(p, b, r) + static_cast<size_t>(x) * kWaves;
   return L;
 }
 
+// A slice's chunks past the row's end read zero; slice_finish masks their tokens.
 __device__ __forceinline__ void slice_load(const Params& p, const SliceLoc& L, uint4 v[kTilesPerSlice]) {
-  const int tid = threadIdx.x;
-  if (L.full) {
+  const uint32_t lane_off = threadIdx.x * 16u;
 #pragma unroll
-    for (int t = 0; t < kTilesPerSlice; ++t) v[t] = L.row[L.c0 + t * kThreads + tid];
-  } else {
-    const int nchunks = (p.V + kVec - 1) / kVec;
-#pragma unroll
-    for (int t = 0; t < kTilesPerSlice; ++t) {
-      const int ci = L.c0 + t * kThreads + tid;
-      if (ci < nchunks) v[t] = L.row[ci];
-    }
-  }
+  for (int t = 0; t < kTilesPerSlice; ++t)
+    v[t] = buffer_load16(L.row, lane_off, static_cast<uint32_t>(L.c0 + t * kThreads) * 16u);
 }
 
-// One reference per lane and slice: the maximum over the lane's 64 logits first
-// (three-input max instructions, 0.5 per logit), then 2^(z c - k) summed in fp32
-// groups of eight and in fp64 beyond.  A lane with no finite logit keeps k = kNoRef
-// and s = 0.
+// One reference per lane and half slice: the maximum over the lane's 32 logits
+// first (three-input max instructions, 0.5 per logit), then 2^(z c - k) summed in
+// fp32 groups of eight and in fp64 beyond.  A lane with no finite logit keeps
+// k = kNoRef and s = 0.  The halves then meet at the larger reference.
 __device__ __forceinline__ float max3f(float a, float b, float c) {
   float r;
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
 }
 
-__device__ __forceinline__ void slice_finish(const Params& p, const SliceLoc& L, const uint4 v[kTilesPerSlice]) {
-  float z[kTilesPerSlice][8];
+constexpr int kHalfTiles = kTilesPerSlice / 2;
+
+__device__ __forceinline__ void half_stats(const Params& p, const SliceLoc& L, const uint4 v[kTilesPerSlice], int t0,
+                                           float& k, double& s) {
+  float z[kHalfTiles][8];
   if (L.full) {
 #pragma unroll
-    for (int t = 0; t < kTilesPerSlice; ++t) unpack8(v[t], z[t], 8);
+    for (int t = 0; t < kHalfTiles; ++t) unpack8(v[t0 + t], z[t], 8);
   } else {
     const int nchunks = (p.V + kVec - 1) / kVec;
 #pragma unroll
-    for (int t = 0; t < kTilesPerSlice; ++t) {
-      const int ci = L.c0 + t * kThreads + static_cast<int>(threadIdx.x);
-      unpack8(v[t], z[t], ci < nchunks ? p.V - ci * kVec : 0);
+    for (int t = 0; t < kHalfTiles; ++t) {
+      const int ci = L.c0 + (t0 + t) * kThreads + static_cast<int>(threadIdx.x);
+      unpack8(v[t0 + t], z[t], ci < nchunks ? p.V - ci * kVec : 0);
     }
   }
   float m = -__builtin_inff();
 #pragma unroll
-  for (int t = 0; t < kTilesPerSlice; ++t)
+  for (int t = 0; t < kHalfTiles; ++t)
     m = max3f(max3f(z[t][0], z[t][1], z[t][2]), max3f(z[t][3], z[t][4], z[t][5]), max3f(z[t][6], z[t][7], m));
   const float c = p.c;
-  const float k = fmaxf(kNoRef, ceilf(m * c));
-  double s = 0.0;
+  k = fmaxf(kNoRef, ceilf(m * c));
+  s = 0.0;
 #pragma unroll
-  for (int t = 0; t < kTilesPerSlice; ++t) {
+  for (int t = 0; t < kHalfTiles; ++t) {
     float e[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) e[i] = fast_exp2(fmaf(z[t][i], c, -k));
     s += static_cast<double>(((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7])));
   }
+}
+
+__device__ __forceinline__ void slice_finish(const Params& p, const SliceLoc& L, const uint4 v[kTilesPerSlice]) {
+  float k1, k2;
+  double s1, s2;
+  half_stats(p, L, v, 0, k1, s1);
+  half_stats(p, L, v, kHalfTiles, k2, s2);
+  const float k = fmaxf(k1, k2);
+  const double s = ldexp(s1, static_cast<int>(fmaxf(k1 - k, -2000.0f))) + ldexp(s2, static_cast<int>(fmaxf(k2 - k, -2000.0f)));
   const float km = wave_max(k);
   const double sw = wave_sum(ldexp(s, static_cast<int>(fmaxf(k - km, -2000.0f))));
   if (lane_id() == 0) st_agent_u64(L.out + wave_id(), pack_stats(km, sw));
@@ -771,20 +779,17 @@ __device__ __forceinline__ int draw_slice(const Params& p, int b, int x, const D
   const int tid = threadIdx.x, wave = wave_id();
   const uint16_t* trow = target_row(p, b, d.draw_row);
   const uint16_t* drow = d.pair ? draft_row(p, b, draw_drafter(p, b), d.draw_row) : trow;
-  const uint4* tr = as_chunks(trow);
-  const uint4* dr = as_chunks(drow);
-  const int nchunks = (p.V + kVec - 1) / kVec;
+  const uint32_t row_bytes = static_cast<uint32_t>((p.V + kVec - 1) / kVec) * 16u;
+  const __amdgpu_buffer_rsrc_t tr = row_buffer(trow, row_bytes);
+  const __amdgpu_buffer_rsrc_t dr = row_buffer(drow, row_bytes);
   const int c0 = x * kTilesPerSlice * kThreads + tid;  // this lane's chunk of the slice's first tile
+  // chunks past the row's end read zero and weigh nothing (chunk_weights)
   uint4 vt[kTilesPerSlice], vd[kTilesPerSlice];
 #pragma unroll
   for (int q = 0; q < kTilesPerSlice; ++q) {
-    const int ci = c0 + q * kThreads;
-    vt[q] = make_uint4(0u, 0u, 0u, 0u);
-    vd[q] = vt[q];
-    if (ci < nchunks) {
-      vt[q] = tr[ci];
-      if (MODE == W_RESID) vd[q] = dr[ci];
-    }
+    const uint32_t uo = static_cast<uint32_t>((x * kTilesPerSlice + q) * kThreads) * 16u;
+    vt[q] = buffer_load16(tr, tid * 16u, uo);
+    vd[q] = MODE == W_RESID ? buffer_load16(dr, tid * 16u, uo) : make_uint4(0u, 0u, 0u, 0u);
   }
 #pragma unroll
   for (int q = 0; q < kTilesPerSlice; ++q) {
@@ -1231,21 +1236,68 @@ __device__ __forceinline__ void run_unit1(const Params& p, int u, int pre_n, Lds
 
 __device__ __forceinline__ void run_unit2(const Params& p, int v, Lds& L) { unit_estimate(p, v / p.P2, L); }
 
-// Phase 0 share of the later-dispatched half of the workgroups, relative to an
-// even share.  Waves dispatched first win the memory arbitration, so the first
-// half of the workgroups streams about 1.4x faster than the second: with 8/11
-// of an even share for the second half and the rest for the first, both halves
-// finish phase 0 together.
-constexpr int kLateShareNum = 8, kLateShareDen = 11;
+// Phase-0 shares of the workgroups by dispatch slot.  A compute unit holds
+// `slots` workgroups, dispatched in slot order (workgroup g in slot g / ncu), and
+// waves dispatched first win the memory arbitration, so slot 0 streams fastest.
+// Slot c >= 1 takes slot_share(slots, c) / 11 of an even share of the list and
+// slot 0 the rest, so that the slots finish phase 0 together.  Both kernels run
+// two slots (measured: the second takes 9/11); the shares of three and four
+// slots are rougher measurements, kept for devices where more fit.
+constexpr int kMaxSlots = 4;
+constexpr int kShareDen = 11;
+__host__ __device__ constexpr int slot_share(int P, int c) {
+  return P == 2 ? (c == 1 ? 9 : 11) : P == 3 ? (c == 1 ? 11 : c == 2 ? 9 : 11) : P == 4 ? 11 - c : 11;
+}
 
-// k-th statistics slice of workgroup g (T0 when it has no more): J rounds of
-// slices j * G + g for every workgroup, then the rest of the list round-robin
-// over the first H workgroups.
-__device__ __forceinline__ int static_slice(int k, int g, int G, int H, int J, int T0) {
-  if (k < J) return k * G + g;
-  if (g >= H) return T0;
-  const int64_t s = static_cast<int64_t>(J) * G + g + static_cast<int64_t>(k - J) * H;
-  return s < T0 ? static_cast<int>(s) : T0;
+// The list is dealt in levels, the slowest slot first.  Level l covers slots
+// 0..P-1-l for rounds[l] rounds of slices (one per workgroup of those slots and
+// round, in workgroup order); after the last level, slot 0 takes the rest of the
+// list round-robin.  A slot c >= 1 thus takes the rounds of levels 0..P-1-c.
+struct Split {
+  int P, C, T0;
+  int rounds[kMaxSlots];
+};
+
+__host__ __device__ inline Split make_split(int T0, int ncu, int slots, int G) {
+  Split sp;
+  sp.T0 = T0;
+  sp.P = (slots >= 1 && slots <= kMaxSlots && ncu * slots == G) ? slots : 1;
+  sp.C = sp.P > 1 ? ncu : G;
+  // n[c]: slices of a slot-c workgroup, c >= 1
+  // loops over the constant kMaxSlots, fully unrolled: the arrays stay in registers
+  int n[kMaxSlots + 1];
+#pragma unroll
+  for (int c = 0; c <= kMaxSlots; ++c)
+    n[c] = c >= 1 && c < sp.P
+               ? static_cast<int>(static_cast<int64_t>(sp.T0) * slot_share(sp.P, c) / (static_cast<int64_t>(G) * kShareDen))
+               : 0;
+#pragma unroll
+  for (int l = 0; l < kMaxSlots; ++l) {
+    int r = 0;
+#pragma unroll
+    for (int hi = 1; hi < kMaxSlots; ++hi)
+      if (hi == sp.P - 1 - l) r = n[hi] - n[hi + 1];  // the slowest slot of level l is hi
+    sp.rounds[l] = r > 0 ? r : 0;
+  }
+  return sp;
+}
+
+// k-th statistics slice of workgroup g (T0 when it has no more).
+__host__ __device__ inline int static_slice(const Split& sp, int k, int g) {
+  const int c = g / sp.C;
+  int64_t base = 0;
+#pragma unroll
+  for (int l = 0; l + 1 < kMaxSlots; ++l) {
+    if (l + 1 >= sp.P) break;
+    if (c > sp.P - 1 - l) return sp.T0;
+    const int width = (sp.P - l) * sp.C;
+    if (k < sp.rounds[l]) return static_cast<int>(base + static_cast<int64_t>(k) * width + g);
+    k -= sp.rounds[l];
+    base += static_cast<int64_t>(sp.rounds[l]) * width;
+  }
+  if (c > 0) return sp.T0;
+  const int64_t s = base + static_cast<int64_t>(k) * sp.C + g;
+  return s < sp.T0 ? static_cast<int>(s) : sp.T0;
 }
 
 // Phase 0: workgroup g streams its statistics slices of the sequence-major slice
@@ -1253,11 +1305,10 @@ __device__ __forceinline__ int static_slice(int k, int g, int G, int H, int J, i
 // kStaticDepth - 1 slices are outstanding while the current one is reduced.
 constexpr int kStaticDepth = 2;
 
-__device__ __forceinline__ void static_phase(const Params& p) {
-  const int G = gridDim.x, g = blockIdx.x, T0 = p.total0;
-  const int H = (G + 1) / 2;
-  const int J = static_cast<int>(static_cast<int64_t>(T0) * kLateShareNum / (static_cast<int64_t>(G) * kLateShareDen));
-  auto slice = [&](int k) { return static_slice(k, g, G, H, J, T0); };
+__device__ __forceinline__ void static_phase(const Params& p, int G, int g) {
+  const int T0 = p.total0;
+  const Split sp = make_split(p.total0, p.ncu, p.slots, G);
+  auto slice = [&](int k) { return static_slice(sp, k, g); };
   uint4 va[kTilesPerSlice], vb[kTilesPerSlice];
   SliceLoc la{}, lb{};
   int k = 0;
@@ -1341,7 +1392,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   if (g < T1 && is_draw_unit(p, g) && static_cast<int>(threadIdx.x) < p.K)
     pre_n = p.tokens[(g / p.P1) * p.K + static_cast<int>(threadIdx.x)];
   if (p.mode == MODE_GAMMA) gamma_groups(p, KL.gamma);
-  static_phase(p);
+  static_phase(p, G, g);
   for (int u = g; u < T1; u += G) {
     __syncthreads();
     run_unit1(p, u, u == g ? pre_n : kNoToken, L);
@@ -1350,6 +1401,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int v = g; v < T2; v += G) {
     __syncthreads();
     run_unit2(p, v, L);
+  }
+}
+
+// Verify calls (spec_verify, spec_cactus_verify): phase 0, then the draw units
+// g, g + G, ...  It is the gamma kernel without the groups and the estimator, so
+// it holds less LDS and fewer registers.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void verify_kernel(Params p) {
+  __shared__ Lds L;
+  const int G = gridDim.x, g = blockIdx.x;
+  const int T1 = p.B * p.P1;
+  // the drafted token of this workgroup's first draw unit, loaded now so that the
+  // unit's decisions do not wait for it (nothing waits for the load here)
+  int pre_n = kNoToken;
+  if (g < T1 && static_cast<int>(threadIdx.x) < p.K) pre_n = p.tokens[(g / p.P1) * p.K + static_cast<int>(threadIdx.x)];
+  static_phase(p, G, g);
+  for (int u = g; u < T1; u += G) {
+    __syncthreads();
+    const int b = u / p.P1;
+    unit_draw(p, b, u - b * p.P1, u == g ? pre_n : kNoToken, L);
   }
 }
 
@@ -1498,16 +1568,29 @@ static int bind_workspace(Params& p, const Shape& s, void* ws, size_t bytes) {
 }
 
 // Resident workgroups the device holds (memoised per device: a device property, not call state).
-static int resident_workgroups() {
+// Compute units of the current device (memoised per device).
+static int compute_units() {
   static int cache[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+  int ncu = 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) cache[dev] = ncu;
+  return ncu;
+}
+
+template <class Kernel>
+static int resident_workgroups(Kernel kernel, int which) {
+  static int cache[2][64] = {{0}};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64 && cache[which][dev] > 0) return cache[which][dev];
   int ncu = 0, per = 0;
   if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, flow_kernel, kThreads, 0) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, kThreads, 0) != hipSuccess) return 0;
   const int g = ncu * (per > 0 ? per : 1);
-  if (dev >= 0 && dev < 64) cache[dev] = g;
+  if (dev >= 0 && dev < 64) cache[which][dev] = g;
   return g;
 }
 
@@ -1529,8 +1612,11 @@ static int launch_flow(Params& p, const Shape& s, hipStream_t stream) {
   // limit keeps the schedule in 32-bit arithmetic (with room for j * G + g)
   if (s.total0 > 0x3fffffffLL || static_cast<int64_t>(s.B) * s.P1 > 0x3fffffffLL || s.ngroups > 0x3fffffffLL)
     return SPEC_ERR_SHAPE;
-  int grid = resident_workgroups();
+  const bool verify = s.mode == MODE_VERIFY;
+  int grid = verify ? resident_workgroups(verify_kernel, 0) : resident_workgroups(flow_kernel, 1);
   if (grid <= 0) return SPEC_ERR_HIP;
+  const int ncu = compute_units();
+  const int slots = ncu > 0 && grid % ncu == 0 ? grid / ncu : 1;
   int64_t want = s.total0;
   if (s.ngroups * s.S > want) want = s.ngroups * s.S;
   if (static_cast<int64_t>(s.B) * s.P1 > want) want = static_cast<int64_t>(s.B) * s.P1;
@@ -1540,7 +1626,12 @@ static int launch_flow(Params& p, const Shape& s, hipStream_t stream) {
   // slot and a sequence's draw units need S workgroups at once
   if ((s.mode == MODE_GAMMA || s.P1 > 0) && grid < s.S) return SPEC_ERR_SHAPE;
   plan_units(p, s);
-  hipLaunchKernelGGL(flow_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
+  p.ncu = ncu;
+  p.slots = slots;  // make_split weights the slots only when the grid is all of them
+  if (verify)
+    hipLaunchKernelGGL(verify_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(flow_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 

@@ -5,6 +5,7 @@
 // spec_workspace_bytes(B, K, N), whatever V is.
 #include "spec_verify.hip"
 #include <cstdio>
+#include <vector>
 
 int main() {
   int bad = 0, checked = 0;
@@ -40,5 +41,37 @@ int main() {
             }
       }
   printf("checked %d layouts, %d violations\n", checked, bad);
-  return bad ? 1 : 0;
+  // phase-0 schedule: every slice of the list is dealt exactly once, and a
+  // workgroup's list ends for good at its first T0 (static_phase stops there)
+  int sched_bad = 0, sched_checked = 0;
+  const int Cs[] = {1, 3, 8, 256};
+  const int T0s[] = {1, 2, 7, 100, 511, 512, 513, 5632, 24320, 100003};
+  std::vector<int> seen;
+  for (int P = 1; P <= kMaxSlots; ++P)
+    for (int C : Cs)
+      for (int dG = 0; dG < 2; ++dG)
+        for (int T0 : T0s) {
+          const int G = P * C - dG;  // dG = 1: a grid that is not all of the slots (no weighting)
+          if (G < 1) continue;
+          const Split sp = make_split(T0, C, P, G);
+          seen.assign(T0, 0);
+          bool ok = true;
+          for (int g = 0; g < G && ok; ++g) {
+            bool ended = false;
+            for (int k = 0; k < T0 + 2; ++k) {
+              const int s = static_slice(sp, k, g);
+              if (s == T0) { ended = true; continue; }
+              if (ended || s < 0 || s > T0) { ok = false; break; }
+              ++seen[s];
+            }
+          }
+          for (int i = 0; i < T0 && ok; ++i) ok = seen[i] == 1;
+          ++sched_checked;
+          if (!ok) {
+            ++sched_bad;
+            if (sched_bad < 10) printf("schedule violation P=%d C=%d G=%d T0=%d\n", P, C, G, T0);
+          }
+        }
+  printf("checked %d schedules, %d violations\n", sched_checked, sched_bad);
+  return (bad || sched_bad) ? 1 : 0;
 }

@@ -25,4 +25,5 @@ def test_workspace_regions_fit_every_shape(tmp_path):
     assert res.returncode == 0, res.stderr[-2000:]
     out = subprocess.run([exe], capture_output=True, text=True)
     assert out.returncode == 0, out.stdout + out.stderr
-    assert "0 violations" in out.stdout
+    assert "layouts, 0 violations" in out.stdout
+    assert "schedules, 0 violations" in out.stdout
