@@ -39,7 +39,12 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-KERNEL = "flow_kernel"
+GAMMA_WORKLOADS = ("hedge_eval", "pool21", "small_mixed")
+
+
+def kernel_of(key: str) -> str:
+    """The library's kernel that a workload's step launches."""
+    return "gamma_kernel" if key in GAMMA_WORKLOADS else "verify_kernel"
 
 
 def log(msg: str) -> None:
@@ -212,7 +217,7 @@ def workloads():
 
 def load_traffic(key: str, per_launch_algo: int):
     """HBM traffic per launch from the committed PMC summary, if taken on these sources."""
-    path = os.path.join(ROOT, "profiles", f"{KERNEL}_{key}_pmc.json")
+    path = os.path.join(ROOT, "profiles", f"{kernel_of(key)}_{key}_pmc.json")
     if not os.path.exists(path):
         return None
     try:
@@ -225,10 +230,11 @@ def load_traffic(key: str, per_launch_algo: int):
 
 
 def summarize_pmc(key: str, fetch_csv: str, write_csv: str, calib_mib: int, command: str) -> dict:
-    """Per-launch HBM traffic of KERNEL from two rocprofv3 --pmc counter_collection CSVs
+    """Per-launch HBM traffic of the workload's kernel from two rocprofv3 --pmc counter_collection CSVs
     (FETCH_SIZE, WRITE_SIZE, both KiB per dispatch).  Each counter is scaled by what it reads
     for the plain device copy of `calib_mib` MiB that the same run made (--copy-calib-mib)."""
     import csv
+    kernel = kernel_of(key)
 
     def per_kernel(path, counter):
         mine, calib = [], []
@@ -236,12 +242,12 @@ def summarize_pmc(key: str, fetch_csv: str, write_csv: str, calib_mib: int, comm
             if r["Counter_Name"] != counter:
                 continue
             v = float(r["Counter_Value"])
-            if r["Kernel_Name"].startswith(f"specv::{KERNEL}("):
+            if r["Kernel_Name"].startswith(f"specv::{kernel}("):
                 mine.append(v)
             elif "copyBuffer" in r["Kernel_Name"] and v > 0.4 * calib_mib * 1024:
                 calib.append(v)
         if not mine or not calib:
-            raise SystemExit(f"{path}: no {KERNEL} dispatches or no calibration copy for {counter}")
+            raise SystemExit(f"{path}: no {kernel} dispatches or no calibration copy for {counter}")
         return float(np.mean(mine)), float(np.mean(calib[-3:])), len(mine)
 
     f_k, f_c, nf = per_kernel(fetch_csv, "FETCH_SIZE")
@@ -249,7 +255,7 @@ def summarize_pmc(key: str, fetch_csv: str, write_csv: str, calib_mib: int, comm
     expect = calib_mib * 1024.0
     f_scale, w_scale = expect / f_c, expect / w_c
     traffic = (f_k * f_scale + w_k * w_scale) * 1024.0
-    return {"kernel": KERNEL, "workload": key, "source_hash": source_hash(),
+    return {"kernel": kernel, "workload": key, "source_hash": source_hash(),
             "fetch_kib_raw": f_k, "write_kib_raw": w_k, "dispatches": [nf, nw],
             "calib_copy_mib": calib_mib, "calib_fetch_kib_raw": f_c, "calib_write_kib_raw": w_c,
             "fetch_scale": f_scale, "write_scale": w_scale,
@@ -274,7 +280,7 @@ def main(argv=None):
 
     if args.pmc_summary:
         d = summarize_pmc(args.workload, *args.pmc_summary, args.copy_calib_mib or 256, args.pmc_command)
-        path = os.path.join(ROOT, "profiles", f"{KERNEL}_{args.workload}_pmc.json")
+        path = os.path.join(ROOT, "profiles", f"{kernel_of(args.workload)}_{args.workload}_pmc.json")
         with open(path, "w") as f:
             json.dump(d, f, indent=1)
             f.write("\n")
@@ -358,7 +364,7 @@ def main(argv=None):
                    "algorithmic_bytes_per_step": wl.algo_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": KERNEL, "mean_launch_ms": mean_launch_s * 1e3},
+                     "kernel": kernel_of(args.workload), "mean_launch_ms": mean_launch_s * 1e3},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -1,13 +1,15 @@
 // libspecverify: batched speculative-sampling verification on gfx950.
 //
-// One persistent kernel, `flow_kernel`, serves the three verification entry
-// points.  Its grid is the number of workgroups the device holds at once (G),
-// and every workgroup g runs three phases on a fixed schedule; nothing is
-// claimed from a shared counter.
+// Two persistent kernels: `verify_kernel` serves spec_verify and
+// spec_cactus_verify, `gamma_kernel` serves spec_counterfactual_gamma.  A grid is
+// the number of workgroups the device holds at once (G), and every workgroup g
+// runs its phases on a fixed schedule; nothing is claimed from a shared counter.
 //
+//   gamma groups -- (gamma calls) slots of S workgroups stream a position's
+//       target row and its N drafter rows once (gamma_groups).
 //   phase 0 -- statistics slices of the call's slice list, dealt to the
 //       workgroups on a fixed schedule weighted by how fast the hardware serves
-//       each half of them (static_phase).  A slice is 16384 tokens of one row,
+//       each dispatch slot of them (static_phase).  A slice is 16384 tokens of one row,
 //       streamed once from HBM with 128-bit loads while the next slice's loads
 //       are in flight.  Each wave reduces its share to an exact base-2 softmax
 //       pair (reference k, sum s) and publishes it as one 64-bit word.  The list
@@ -34,9 +36,9 @@
 // Cross-workgroup data is published with device-scope 64-bit stores of words
 // that are never zero, into a workspace that is zero before the call; a reader
 // polls a word with device-scope loads until it is non-zero.  No counter, queue
-// or fence sits on the streaming path.  The last step of each sequence clears
-// every word the sequence published, so the workspace is zero again when the
-// kernel ends.
+// or fence sits on the streaming path.  Every word is cleared once all its
+// readers are done with it (by its only reader, or by the step that knows the
+// others are done), so the workspace is zero again when the kernel ends.
 //
 // [LT] "Speculative Decoding 为什么是 Lossless 的 -- 详细证明教程";
 // [NB] HedgeSpec note "Not-a-Bandit: Provably No-Regret Drafter Selection ...";
@@ -1381,7 +1383,7 @@ union KernelLds {
   GammaLds gamma;
 };
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void flow_kernel(Params p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gamma_kernel(Params p) {
   __shared__ KernelLds KL;
   Lds& L = KL.units;
   const int G = gridDim.x, g = blockIdx.x;
@@ -1613,7 +1615,7 @@ static int launch_flow(Params& p, const Shape& s, hipStream_t stream) {
   if (s.total0 > 0x3fffffffLL || static_cast<int64_t>(s.B) * s.P1 > 0x3fffffffLL || s.ngroups > 0x3fffffffLL)
     return SPEC_ERR_SHAPE;
   const bool verify = s.mode == MODE_VERIFY;
-  int grid = verify ? resident_workgroups(verify_kernel, 0) : resident_workgroups(flow_kernel, 1);
+  int grid = verify ? resident_workgroups(verify_kernel, 0) : resident_workgroups(gamma_kernel, 1);
   if (grid <= 0) return SPEC_ERR_HIP;
   const int ncu = compute_units();
   const int slots = ncu > 0 && grid % ncu == 0 ? grid / ncu : 1;
@@ -1631,7 +1633,7 @@ static int launch_flow(Params& p, const Shape& s, hipStream_t stream) {
   if (verify)
     hipLaunchKernelGGL(verify_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(flow_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(gamma_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 
