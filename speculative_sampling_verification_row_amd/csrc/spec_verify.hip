@@ -955,6 +955,9 @@ __device__ __forceinline__ void wave_row_issue(const Params& p, const unsigned l
     wv[j] = 1ull;
     if (q < W) wv[j] = ld_agent_u64(const_cast<unsigned long long*>(row_words) + q);
   }
+  // keep the loads here: the compiler would otherwise sink them to their use,
+  // behind loads that a wait for them would then also wait for
+  asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ RowStats wave_row_finish(const Params& p, const unsigned long long* row_words,
@@ -1030,16 +1033,16 @@ __device__ __forceinline__ void gamma_member(const Params& p, GammaLds& GL, int 
   };
   // row r of group q: 0 the target row k, 1 + i drafter i's row k
   auto row_index = [&](int k, int r) { return r == 0 ? k : p.RT + (r - 1) * K + k; };
+  // Unconditional buffer loads: chunks past the row's end read zero (mask_tail
+  // then masks their tokens), so no load sits behind a branch whose join would
+  // copy, and therefore wait for, the registers it fills.
+  const uint32_t row_bytes = static_cast<uint32_t>(nchunks) * 16u;
   auto load = [&](int q, int r, uint4 (&v)[kTilesPerSlice]) {
     const int b = q / K, k = q - b * K;
-    // the lane's chunk index, recomputed here rather than kept live (as 64-bit
-    // offsets) across the whole loop
-    int c0 = ci0;
-    asm volatile("" : "+v"(c0));
-    const uint4* row = as_chunks(stat_row(p, b, row_index(k, r))) + c0;
+    const __amdgpu_buffer_rsrc_t rs = row_buffer(stat_row(p, b, row_index(k, r)), row_bytes);
 #pragma unroll
     for (int t = 0; t < kTilesPerSlice; ++t)
-      if (full || c0 + t * kThreads < nchunks) v[t] = row[t * kThreads];
+      v[t] = buffer_load16(rs, tid * 16u, static_cast<uint32_t>(x * kSliceChunks + t * kThreads) * 16u);
   };
   // The previous row slice's terms wait in registers until its row's normaliser
   // is known: the other members' words of that row are loaded at the start of
