@@ -219,6 +219,15 @@ struct SliceLoc {
 // entries share one residue modulo S does not always get the same (and, for the
 // last slice, shorter) slice of its rows.
 __device__ __forceinline__ SliceLoc slice_loc(const Params& p, int sig) {
+  if (sig >= p.total0) {
+    // no slice: a buffer of no bytes, whose loads read zero without touching memory
+    SliceLoc none;
+    none.row = row_buffer(p.target, 0u);
+    none.c0 = 0;
+    none.full = 1;
+    none.out = nullptr;
+    return none;
+  }
   int b, x, r;
   if (p.mode == MODE_GAMMA) {  // the list holds only the fused bonus rows (the groups do the rest)
     b = sig / p.S;
@@ -949,11 +958,13 @@ constexpr int kRowWordsPerLane = kMaxSlices * kWaves / 64;
 __device__ __forceinline__ void wave_row_issue(const Params& p, const unsigned long long* row_words,
                                                unsigned long long wv[kRowWordsPerLane]) {
   const int W = p.S * kWaves;
+  // every lane loads (lanes past the row's words reload word 0, and
+  // wave_row_finish ignores them): loads behind a branch would blur the count of
+  // loads in flight that the waits for the slice loads rely on
 #pragma unroll
   for (int j = 0; j < kRowWordsPerLane; ++j) {
     const int q = lane_id() + 64 * j;
-    wv[j] = 1ull;
-    if (q < W) wv[j] = ld_agent_u64(const_cast<unsigned long long*>(row_words) + q);
+    wv[j] = ld_agent_u64(const_cast<unsigned long long*>(row_words) + (q < W ? q : 0));
   }
   // keep the loads here: the compiler would otherwise sink them to their use,
   // behind loads that a wait for them would then also wait for
@@ -1001,19 +1012,20 @@ struct GammaLds {
 __device__ __forceinline__ void mask_tail(uint4 v[kTilesPerSlice], int ci0, int V) {
   const int nchunks = (V + kVec - 1) / kVec;
   constexpr uint32_t kNegInf2 = 0xff80ff80u;  // two bf16 -inf
+  // selects, not branches: a branch would join into copies of the load registers,
+  // and the copies would wait for loads issued after these
 #pragma unroll
   for (int t = 0; t < kTilesPerSlice; ++t) {
     const int ci = ci0 + t * kThreads;
     const int valid = V - ci * kVec;  // tokens of this chunk inside the row
-    if (valid <= 0) {
-      v[t] = make_uint4(kNegInf2, kNegInf2, kNegInf2, kNegInf2);
-    } else if (valid < kVec) {
-      uint32_t w[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
+    uint32_t w[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
 #pragma unroll
-      for (int e = 0; e < kVec; ++e)
-        if (e >= valid) w[e >> 1] = (e & 1) ? ((w[e >> 1] & 0x0000ffffu) | 0xff800000u) : ((w[e >> 1] & 0xffff0000u) | 0xff80u);
-      v[t] = make_uint4(w[0], w[1], w[2], w[3]);
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t lo = 2 * d < valid ? (w[d] & 0x0000ffffu) : (kNegInf2 & 0x0000ffffu);
+      const uint32_t hi = 2 * d + 1 < valid ? (w[d] & 0xffff0000u) : (kNegInf2 & 0xffff0000u);
+      w[d] = lo | hi;
     }
+    v[t] = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -1038,8 +1050,9 @@ __device__ __forceinline__ void gamma_member(const Params& p, GammaLds& GL, int 
   // copy, and therefore wait for, the registers it fills.
   const uint32_t row_bytes = static_cast<uint32_t>(nchunks) * 16u;
   auto load = [&](int q, int r, uint4 (&v)[kTilesPerSlice]) {
-    const int b = q / K, k = q - b * K;
-    const __amdgpu_buffer_rsrc_t rs = row_buffer(stat_row(p, b, row_index(k, r)), row_bytes);
+    const bool none = q >= nG;
+    const int b = none ? 0 : q / K, k = none ? 0 : q - b * K;
+    const __amdgpu_buffer_rsrc_t rs = row_buffer(stat_row(p, b, row_index(k, none ? 0 : r)), none ? 0u : row_bytes);
 #pragma unroll
     for (int t = 0; t < kTilesPerSlice; ++t)
       v[t] = buffer_load16(rs, tid * 16u, static_cast<uint32_t>(x * kSliceChunks + t * kThreads) * 16u);
@@ -1086,7 +1099,7 @@ __device__ __forceinline__ void gamma_member(const Params& p, GammaLds& GL, int 
       pw = part_row(p, pb, row_index(pk, pr));
       wave_row_issue(p, pw, wv);
     }
-    if (q1 < nG) load(q1, r1, nxt);
+    load(q1, r1, nxt);  // unconditional (no group: a buffer of no bytes), as in static_phase
     if (!full) mask_tail(cur, ci0, p.V);
     double sl;
     const float kl = lane_exps<true, true>(p, cur, ci0, ec, sl);
@@ -1315,64 +1328,26 @@ __device__ __forceinline__ void static_phase(const Params& p, int G, int g) {
   const Split sp = make_split(p.total0, p.ncu, p.slots, G);
   auto slice = [&](int k) { return static_slice(sp, k, g); };
   uint4 va[kTilesPerSlice], vb[kTilesPerSlice];
-  SliceLoc la{}, lb{};
+  // Every load is issued unconditionally (a missing slice's loads read a buffer of
+  // no bytes): a load behind a branch leaves the join with two possible counts of
+  // loads in flight, and the wait for the current slice then also waits for the
+  // first loads of the next one.
   int k = 0;
   int sa = slice(0), sb = slice(1);
-  if (sa < T0) {
-    la = slice_loc(p, sa);
+  SliceLoc la = slice_loc(p, sa), lb{};
+  slice_load(p, la, va);
+  while (sa < T0) {
+    lb = slice_loc(p, sb);
+    slice_load(p, lb, vb);
+    slice_finish(p, la, va);
+    if (sb >= T0) break;
+    const int sc = slice(k + 2);
+    la = slice_loc(p, sc);
     slice_load(p, la, va);
-  }
-  if constexpr (kStaticDepth == 2) {
-    while (sa < T0) {
-      if (sb < T0) {
-        lb = slice_loc(p, sb);
-        slice_load(p, lb, vb);
-      }
-      slice_finish(p, la, va);
-      if (sb >= T0) break;
-      const int sc = slice(k + 2);
-      if (sc < T0) {
-        la = slice_loc(p, sc);
-        slice_load(p, la, va);
-      }
-      slice_finish(p, lb, vb);
-      sa = sc;
-      sb = slice(k + 3);
-      k += 2;
-    }
-  } else {
-    uint4 vc[kTilesPerSlice];
-    SliceLoc lc{};
-    if (sb < T0) {
-      lb = slice_loc(p, sb);
-      slice_load(p, lb, vb);
-    }
-    // at the top: slice k in va, slice k + 1 in vb (loads outstanding)
-    while (sa < T0) {
-      const int sc = slice(k + 2);
-      if (sc < T0) {
-        lc = slice_loc(p, sc);
-        slice_load(p, lc, vc);
-      }
-      slice_finish(p, la, va);
-      if (sb >= T0) break;
-      const int sd = slice(k + 3);
-      if (sd < T0) {
-        la = slice_loc(p, sd);
-        slice_load(p, la, va);
-      }
-      slice_finish(p, lb, vb);
-      if (sc >= T0) break;
-      const int se = slice(k + 4);
-      if (se < T0) {
-        lb = slice_loc(p, se);
-        slice_load(p, lb, vb);
-      }
-      slice_finish(p, lc, vc);
-      sa = sd;
-      sb = se;
-      k += 3;
-    }
+    slice_finish(p, lb, vb);
+    sa = sc;
+    sb = slice(k + 3);
+    k += 2;
   }
 }
 
