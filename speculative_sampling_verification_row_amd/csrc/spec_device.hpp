@@ -69,12 +69,6 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-// Workgroup barrier for hand-offs through LDS: it waits for this wave's LDS
-// operations, not for its global stores (__syncthreads() also waits for those, so
-// a barrier after a store to a published word would wait out the store's trip).
-// Nothing here hands data between threads of a workgroup through global memory.
-__device__ __forceinline__ void block_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 __device__ __forceinline__ float bf16_at(const uint16_t* row, int idx) {
   return __uint_as_float(static_cast<uint32_t>(row[idx]) << 16);
 }
@@ -193,19 +187,19 @@ __device__ __forceinline__ RowStats block_row_stats(const RowAcc a, double* scra
   float km = wave_max(a.k);
   float* kf = reinterpret_cast<float*>(scratch);
   if (lane_id() == 0) kf[wave_id()] = km;
-  block_sync();
+  __syncthreads();
   km = kf[0];
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) km = fmaxf(km, kf[w]);
-  block_sync();
+  __syncthreads();
   double s = ldexp(a.s, static_cast<int>(fmaxf(a.k - km, -2000.0f)));
   s = wave_sum(s);
   if (lane_id() == 0) scratch[wave_id()] = s;
-  block_sync();
+  __syncthreads();
   double tot = 0.0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) tot += scratch[w];
-  block_sync();
+  __syncthreads();
   return RowStats{km, tot};
 }
 

@@ -66,6 +66,7 @@ constexpr unsigned long long kValid = 1ull << 63;        // published bit of an 
 constexpr int kStage = 8 * kThreads;  // statistics words staged in LDS at once
 constexpr int kRowCap = 256;          // merged rows held in LDS at once
 constexpr int kNoK = INT32_MIN;       // statistics word of a share with no finite logit
+constexpr int kNoToken = INT32_MIN;   // no preloaded drafted token
 
 // Everything a lane needs to turn logits into sampling weights.  Weights are kept
 // in units of 1/st (st the target row's sum): an inverse-CDF draw depends only on
@@ -320,30 +321,9 @@ struct MergeLds {
   double rs[kRowCap];  // merged sum of row i
 };
 
-// The statistics words of the batch of rows that starts at row i0: thread tid
-// holds words tid + e * kThreads.  Every thread loads (past the batch, word 0 of
-// its first row again, ignored): loads behind a branch would blur the count of
-// loads in flight that later waits rely on.
+// Rows row_of(0..nrows) of sequence b (nrows <= kRowCap) -> M.rk / M.rs.
 template <class RowFn>
-__device__ __forceinline__ void merge_issue(const Params& p, int b, int nrows, int i0, RowFn row_of,
-                                            unsigned long long w[8]) {
-  const int W = p.S * kWaves;
-  const int per = kStage / W > 0 ? kStage / W : 1;
-  const int nw = min(per, nrows - i0) * W;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int q0 = tid + e * kThreads;
-    const int q = q0 < nw ? q0 : 0;
-    w[e] = ld_agent_u64(part_row(p, b, row_of(i0 + q / W)) + q % W);
-  }
-}
-
-// Rows row_of(0..nrows) of sequence b (nrows <= kRowCap) -> M.rk / M.rs.  `first`:
-// the first batch's words, issued earlier with merge_issue, or nullptr.
-template <class RowFn>
-__device__ __forceinline__ void merge_rows(const Params& p, int b, int nrows, RowFn row_of, MergeLds& M,
-                                           const unsigned long long* first = nullptr) {
+__device__ __forceinline__ void merge_rows(const Params& p, int b, int nrows, RowFn row_of, MergeLds& M) {
   const int W = p.S * kWaves;
   const int per = kStage / W > 0 ? kStage / W : 1;
   const int tid = threadIdx.x;
@@ -351,15 +331,12 @@ __device__ __forceinline__ void merge_rows(const Params& p, int b, int nrows, Ro
     const int nb = min(per, nrows - i0);
     const int nw = nb * W;
     unsigned long long w[8];
-    if (i0 == 0 && first != nullptr) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w[e] = first[e];
-    } else {
-      merge_issue(p, b, nrows, i0, row_of, w);
+    for (int e = 0; e < 8; ++e) {
+      const int q = tid + e * kThreads;
+      w[e] = 1ull;
+      if (q < nw) w[e] = ld_agent_u64(part_row(p, b, row_of(i0 + q / W)) + q % W);
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (tid + e * kThreads >= nw) w[e] = 1ull;
     bool missing = false;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -371,7 +348,7 @@ __device__ __forceinline__ void merge_rows(const Params& p, int b, int nrows, Ro
       for (int q = tid; q < nw; q += kThreads)
         if (M.stage[q] == 0ull) M.stage[q] = poll_word(p.flags, part_row(p, b, row_of(i0 + q / W)) + q % W);
     }
-    block_sync();
+    __syncthreads();
     for (int i = wave_id(); i < nb; i += kWaves) {
       const unsigned long long* st = M.stage + i * W;
       int km = kNoK;
@@ -388,7 +365,7 @@ __device__ __forceinline__ void merge_rows(const Params& p, int b, int nrows, Ro
         M.rs[i0 + i] = s;
       }
     }
-    block_sync();
+    __syncthreads();
   }
 }
 
@@ -602,7 +579,6 @@ __device__ __forceinline__ void row_subtiles(const uint16_t* trow, const uint16_
 
 struct Decision {
   WeightCtx w;
-  int drafter;   // the drafter whose row pairs the draw
   int A;         // accepted length; -1 invalid
   int draw_row;  // position of the draw row (A, or K for the bonus)
   int pair;      // 1: residual over (target A, draft A); 0: pt of target row K
@@ -622,38 +598,33 @@ struct Lds {
   int flag;
 };
 
-// The drafter whose rows a sequence's draw uses: 0 in verify calls, sel[b] in a
-// fused gamma call.  The call kind is a template parameter, so that a verify
-// call has no load (and no branch around one) here.
-template <int KMODE>
-__device__ __forceinline__ int draw_drafter(const Params& p, int b) { return KMODE == MODE_VERIFY ? 0 : p.sel[b]; }
+__device__ __forceinline__ int draw_drafter(const Params& p, int b) { return p.mode == MODE_VERIFY ? 0 : p.sel[b]; }
 
 // Merge the statistics of target rows 0..K and drafter `drafter`'s rows 0..K-1,
 // take every accept decision, and describe the draw.  Writes accept_mask and
 // gamma_star when `write_outputs`.  The result is in L.dl.d after the call.
-template <int KMODE>
 __device__ __forceinline__ void decide(const Params& p, int b, bool write_outputs, int pre_n, Lds& L) {
   const int K = p.K, V = p.V;
   const int t = threadIdx.x;
-  const int drafter = draw_drafter<KMODE>(p, b);
+  const int drafter = draw_drafter(p, b);
   const bool bad_sel = drafter < 0 || drafter >= p.N;
   const int dsafe = bad_sel ? 0 : drafter;
-  // Thread t < K: the drafted token of position t, its uniform and its two logits,
-  // loaded with the statistics words.  All loads are unconditional (indices
-  // clamped, results of other threads ignored), the token first: the logits
-  // wait only for it, not for the words behind it.
-  const int tc = t < K ? t : 0;
-  const int n = pre_n;  // loaded by the caller ahead of time: nothing here waits for it
-  const float rr = p.r[b * K + tc];
+  // thread t < K: the drafted token of position t, its uniform and its two logits,
+  // fetched first so that these loads overlap the statistics loads
+  int n = -1;
+  float rr = 0.0f, zt = 0.0f, zd = 0.0f;
+  bool tok_ok = false;
+  if (t < K) {
+    n = pre_n != kNoToken ? pre_n : p.tokens[b * K + t];
+    rr = p.r[b * K + t];
+    tok_ok = !bad_sel && n >= 0 && n < V;
+    if (tok_ok) {
+      zt = bf16_at(target_row(p, b, t), n);
+      zd = bf16_at(draft_row(p, b, drafter, t), n);
+    }
+  }
   // rows 0..K: target rows 0..K; rows K+1..2K: the drafter's rows 0..K-1
-  auto row_of = [&](int i) { return i <= K ? i : p.RT + dsafe * K + (i - K - 1); };
-  unsigned long long w0[8];
-  merge_issue(p, b, 2 * K + 1, 0, row_of, w0);
-  const bool tok_ok = t < K && !bad_sel && n >= 0 && n < V;
-  const int nc = tok_ok ? n : 0;
-  const float zt = bf16_at(target_row(p, b, tc), nc);
-  const float zd = bf16_at(draft_row(p, b, dsafe, tc), nc);
-  merge_rows(p, b, 2 * K + 1, row_of, L.m, w0);
+  merge_rows(p, b, 2 * K + 1, [&](int i) { return i <= K ? i : p.RT + dsafe * K + (i - K - 1); }, L.m);
   // threads t < K (all in wave 0): the accept test of position t
   uint32_t state = ST_INVALID;
   double ct = 0.0, gs = 0.0;
@@ -719,11 +690,10 @@ __device__ __forceinline__ void decide(const Params& p, int b, bool write_output
         w.kt = L.m.rk[K];
       }
       d.w = w;
-      d.drafter = dsafe;
       L.dl.d = d;
     }
   }
-  block_sync();
+  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -742,13 +712,13 @@ __device__ __forceinline__ void finish_sequence(const Params& p, int b, bool cle
     last = 1;
   } else if (p.nlast > 1) {
     stores_complete();  // this step's own words are out before it takes its ticket
-    block_sync();
+    __syncthreads();
     if (threadIdx.x == 0) {
       const int l = ticket(&p.done[b]) == static_cast<uint32_t>(p.nlast - 1) ? 1 : 0;
       if (l) st_agent(&p.done[b], 0u);
       L.flag = l;
     }
-    block_sync();
+    __syncthreads();
     last = L.flag;
   }
   if (last) {
@@ -756,7 +726,7 @@ __device__ __forceinline__ void finish_sequence(const Params& p, int b, bool cle
     const int n = p.R * p.S * kWaves;
     for (int q = threadIdx.x; q < n; q += kThreads) st_agent_u64(w + q, 0ull);
   }
-  block_sync();
+  __syncthreads();
 }
 
 // Wave: the inverse-CDF crossing among up to 64 masses, lane i holding mass i
@@ -806,7 +776,7 @@ __device__ __forceinline__ int exchange_totals(const Params& p, int b, int x, do
     L.tot[tid] = unpack_f64(w);
     st_agent_u64(src, 0ull);
   }
-  block_sync();
+  __syncthreads();
   const int lane = lane_id();
   return crossing_slice(lane < p.S ? L.tot[lane] : 0.0, u, x_rel);
 }
@@ -819,13 +789,11 @@ template <int MODE, bool SPECIAL>
 __device__ __forceinline__ int draw_slice(const Params& p, int b, int x, const Decision& d, Lds& L) {
   const int tid = threadIdx.x, wave = wave_id();
   const uint16_t* trow = target_row(p, b, d.draw_row);
-  const uint16_t* drow = d.pair ? draft_row(p, b, d.drafter, d.draw_row) : trow;
+  const uint16_t* drow = d.pair ? draft_row(p, b, draw_drafter(p, b), d.draw_row) : trow;
   const uint32_t row_bytes = static_cast<uint32_t>((p.V + kVec - 1) / kVec) * 16u;
   const __amdgpu_buffer_rsrc_t tr = row_buffer(trow, row_bytes);
   const __amdgpu_buffer_rsrc_t dr = row_buffer(drow, row_bytes);
   const int c0 = x * kTilesPerSlice * kThreads + tid;  // this lane's chunk of the slice's first tile
-  // the draw's uniform, loaded first: it is used only after the weights and the exchange
-  const float u_draw = p.u[b * (p.K + 1) + d.draw_row];
   // chunks past the row's end read zero and weigh nothing (chunk_weights)
   uint4 vt[kTilesPerSlice], vd[kTilesPerSlice];
 #pragma unroll
@@ -841,9 +809,9 @@ __device__ __forceinline__ int draw_slice(const Params& p, int b, int x, const D
     const double incl = wave_incl_scan(ls);
     if (lane_id() == 63) L.subsum[q * kWaves + wave] = incl;
   }
-  block_sync();
+  __syncthreads();
   double x_rel = 0.0;
-  const int xs = exchange_totals(p, b, x, static_cast<double>(u_draw), x_rel, L);
+  const int xs = exchange_totals(p, b, x, static_cast<double>(p.u[b * (p.K + 1) + d.draw_row]), x_rel, L);
   if (xs != x) return xs;
   // this slice's total is positive, so one of its sub-tiles has mass; the scan is
   // the one that formed the total
@@ -875,9 +843,9 @@ __device__ __forceinline__ void target_h_draw(const Params& p, int b, const Deci
   const double uu = static_cast<double>(p.u[b * (p.K + 1) + d.draw_row]);
   WeightCtx wh = d.w;
   wh.mode = W_TARGET_H;
-  block_sync();  // every thread is done with the slice's masses in LDS
+  __syncthreads();  // every thread is done with the slice's masses in LDS
   row_subtiles<W_TARGET_H, SPECIAL>(trow, trow, p.V, wh, (p.V + kTile - 1) / kTile, L.subsum, p.nsub);
-  block_sync();
+  __syncthreads();
   if (wave_id() == 0) {
     int s_star = -1;
     double x_rel = 0.0;
@@ -893,17 +861,16 @@ __device__ __forceinline__ void target_h_draw(const Params& p, int b, const Deci
 
 // Draw unit x of sequence b.  Unit 0 also writes the per-position outputs, the
 // outputs of a sequence with no valid draw, and the outputs of a draw with no
-// mass.  `pre_n`: the drafted token of position min(threadIdx.x, K - 1), which
-// the caller loads ahead of time.
-template <int KMODE>
+// mass.  `pre_n`: the drafted token of position threadIdx.x, loaded ahead of
+// time, or kNoToken.
 __device__ __forceinline__ void unit_draw(const Params& p, int b, int x, int pre_n, Lds& L) {
-  decide<KMODE>(p, b, x == 0, pre_n, L);
+  decide(p, b, x == 0, pre_n, L);
   const Decision d = L.dl.d;
   int xs;
   if (d.A < 0) {
     // no draw: the totals are still exchanged, so that unit 0 knows when to clear
     if (threadIdx.x < kSliceSub) L.subsum[threadIdx.x] = 0.0;
-    block_sync();
+    __syncthreads();
     double x_rel = 0.0;
     xs = exchange_totals(p, b, x, 0.0, x_rel, L);
     if (x == 0 && threadIdx.x == 0) {
@@ -1255,14 +1222,14 @@ __device__ __forceinline__ void unit_estimate(const Params& p, int b, Lds& L) {
       }
       L.arat[tid] = a;
     }
-    block_sync();
+    __syncthreads();
     if (tid < N) {
       for (int kl = 0; kl < nk; ++kl) {
         Lh += L.gsum[kl * N + tid] * prod;
         prod *= L.arat[kl * N + tid];
       }
     }
-    block_sync();
+    __syncthreads();
   }
   if (tid < N) {
     p.est_len[b * N + tid] = static_cast<float>(Lh);
@@ -1278,10 +1245,11 @@ __device__ __forceinline__ void unit_estimate(const Params& p, int b, Lds& L) {
 // The kernel
 // ---------------------------------------------------------------------------
 
+__device__ __forceinline__ bool is_draw_unit(const Params& p, int u) { return p.P1 > 0; }
 
 __device__ __forceinline__ void run_unit1(const Params& p, int u, int pre_n, Lds& L) {
   const int b = u / p.P1;
-  unit_draw<MODE_GAMMA>(p, b, u - b * p.P1, pre_n, L);
+  unit_draw(p, b, u - b * p.P1, pre_n, L);
 }
 
 __device__ __forceinline__ void run_unit2(const Params& p, int v, Lds& L) { unit_estimate(p, v / p.P2, L); }
@@ -1400,20 +1368,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int T1 = p.B * p.P1;
   // the drafted token of this workgroup's first draw unit, loaded now so that the
   // unit's decisions do not wait for it (nothing waits for the load here)
-  const int tk = min(static_cast<int>(threadIdx.x), p.K - 1);
-  auto token_of = [&](int u) { return T1 > 0 ? p.tokens[(min(u, T1 - 1) / p.P1) * p.K + tk] : 0; };
-  int pre_n = token_of(g);
+  int pre_n = kNoToken;
+  if (g < T1 && is_draw_unit(p, g) && static_cast<int>(threadIdx.x) < p.K)
+    pre_n = p.tokens[(g / p.P1) * p.K + static_cast<int>(threadIdx.x)];
   if (p.mode == MODE_GAMMA) gamma_groups(p, KL.gamma);
   static_phase(p, G, g);
   for (int u = g; u < T1; u += G) {
-    block_sync();
-    const int next_n = token_of(u + G);  // the next unit's tokens, loaded during this unit
-    run_unit1(p, u, pre_n, L);
-    pre_n = next_n;
+    __syncthreads();
+    run_unit1(p, u, u == g ? pre_n : kNoToken, L);
   }
   const int T2 = p.B * p.P2;
   for (int v = g; v < T2; v += G) {
-    block_sync();
+    __syncthreads();
     run_unit2(p, v, L);
   }
 }
@@ -1427,16 +1393,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int T1 = p.B * p.P1;
   // the drafted token of this workgroup's first draw unit, loaded now so that the
   // unit's decisions do not wait for it (nothing waits for the load here)
-  const int tk = min(static_cast<int>(threadIdx.x), p.K - 1);
-  auto token_of = [&](int u) { return p.tokens[(min(u, T1 - 1) / p.P1) * p.K + tk]; };
-  int pre_n = token_of(g);
+  int pre_n = kNoToken;
+  if (g < T1 && static_cast<int>(threadIdx.x) < p.K) pre_n = p.tokens[(g / p.P1) * p.K + static_cast<int>(threadIdx.x)];
   static_phase(p, G, g);
-  // no barrier at the top of a unit: phase 0 uses no LDS, and a unit ends with one
   for (int u = g; u < T1; u += G) {
+    __syncthreads();
     const int b = u / p.P1;
-    const int next_n = token_of(u + G);  // the next unit's tokens, loaded during this unit
-    unit_draw<MODE_VERIFY>(p, b, u - b * p.P1, pre_n, L);
-    pre_n = next_n;
+    unit_draw(p, b, u - b * p.P1, u == g ? pre_n : kNoToken, L);
   }
 }
 
