@@ -69,6 +69,13 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// min of two floats known to be >= +0 (not NaN): their bit patterns order as
+// unsigned integers, so one integer min does it (fminf would first quiet each
+// operand read from memory, one more instruction per operand).
+__device__ __forceinline__ float min_nonneg(float a, float b) {
+  return __uint_as_float(min(__float_as_uint(a), __float_as_uint(b)));
+}
+
 __device__ __forceinline__ float bf16_at(const uint16_t* row, int idx) {
   return __uint_as_float(static_cast<uint32_t>(row[idx]) << 16);
 }

@@ -1077,7 +1077,7 @@ __device__ __forceinline__ void gamma_member(const Params& p, GammaLds& GL, int 
     for (int t = 0; t < kTilesPerSlice; ++t) {
       float mn[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) mn[i] = fminf(GL.pt[t * 8 + i][tid], ep[t][i] * sc);
+      for (int i = 0; i < 8; ++i) mn[i] = min_nonneg(GL.pt[t * 8 + i][tid], ep[t][i] * sc);
       gs += static_cast<double>(((mn[0] + mn[1]) + (mn[2] + mn[3])) + ((mn[4] + mn[5]) + (mn[6] + mn[7])));
     }
     gs = wave_sum(gs);
