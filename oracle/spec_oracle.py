@@ -49,6 +49,10 @@ R15 Cactus acceptance phi(n) = min(1, h_n / pd(n)) and recovery
 R16 Cactus: c = 1 gives gamma* = 1 and s := 0; delta = 0 gives s = 1.0
     exactly, so h == pt bit for bit and the position is plain SpS.
 R17 Cactus bonus is drawn from pt at row m (h is defined per candidate only).
+R23 Exact-KL Cactus: gamma* is the largest g in [c, 1] whose target h keeps
+    KL(h || pt) <= delta ([CA] Key design 1's optimisation, Key design 2's
+    root), 1 when even the one-hot target fits the budget (-log c <= delta),
+    and c when delta = 0 or c = 0.
 """
 
 from __future__ import annotations
@@ -68,6 +72,8 @@ __all__ = [
     "sps_sequence",
     "spec_verify",
     "cactus_gamma_star",
+    "cactus_kl",
+    "cactus_gamma_star_kl",
     "cactus_target",
     "cactus_sequence",
     "spec_cactus_verify",
@@ -250,22 +256,67 @@ def cactus_gamma_star(c: float, delta: float) -> float:
     return min(c + math.sqrt(2.0 * delta * c * (1.0 - c)), 1.0)
 
 
-def cactus_target(pt, n: int, delta: float):
+def cactus_kl(g: float, c: float) -> float:
+    """KL(h || pt) in nats of the Theorem-2 target h with h_n = g ([CA] Key design 2).
+
+    The tokens other than n keep pt's proportions, so the divergence over the
+    vocabulary collapses to the two-outcome one:
+    g log(g / c) + (1 - g) log((1 - g) / (1 - c)), with 0 log 0 = 0 and
+    +inf where g > 0 meets c = 0.
+    """
+    if g > 0.0 and c <= 0.0:
+        return math.inf
+    t1 = g * (math.log(g) - math.log(c)) if g > 0.0 else 0.0
+    if g < 1.0:
+        t2 = (1.0 - g) * (math.log1p(-g) - math.log1p(-c)) if c < 1.0 else math.inf
+    else:
+        t2 = 0.0
+    return t1 + t2
+
+
+def cactus_gamma_star_kl(c: float, delta: float) -> float:
+    """gamma* as the exact root of the KL constraint, without the Taylor step.
+
+    [CA] Key design 2: gamma* is the root in [c, +inf) of D_KL(h || q) = delta,
+    clipped to [c, 1]; Key design 3 notes that this equation (x log x terms)
+    has no closed form.  Read as the optimisation of Key design 1: the largest
+    g in [c, 1] with cactus_kl(g, c) <= delta.  The divergence grows with g on
+    [c, 1], so bisection in float64 finds it, down to adjacent doubles; the
+    lower end (inside the budget) is returned.  Reading R23.
+    """
+    if delta <= 0.0 or c <= 0.0:
+        return c            # only g = c keeps the divergence at 0 (or finite, at c = 0)
+    if c >= 1.0 or cactus_kl(1.0, c) <= delta:
+        return 1.0          # the budget reaches the one-hot target: clipped to 1
+    lo, hi = c, 1.0         # cactus_kl(lo) <= delta < cactus_kl(hi)
+    while True:
+        mid = 0.5 * (lo + hi)
+        if mid <= lo or mid >= hi:
+            return lo
+        if cactus_kl(mid, c) <= delta:
+            lo = mid
+        else:
+            hi = mid
+
+
+def cactus_target(pt, n: int, delta: float, exact_kl: bool = False):
     """The per-candidate target h of [CA] Key design 2 (Theorem 2 closed form).
 
     h_n = gamma*, h_i = (1 - gamma*) / (1 - c) * pt_i for i != n.  Reading R16:
-    c == 1 forces gamma* = 1 and s := 0.  Returns (h, gamma*).
+    c == 1 forces gamma* = 1 and s := 0.  gamma* is the Taylor form of Key
+    design 3, or with ``exact_kl`` the exact root (cactus_gamma_star_kl).
+    Returns (h, gamma*).
     """
     pt = np.asarray(pt, dtype=np.float64)
     c = float(pt[n])
-    g = cactus_gamma_star(c, delta)
+    g = cactus_gamma_star_kl(c, delta) if exact_kl else cactus_gamma_star(c, delta)
     s = (1.0 - g) / (1.0 - c) if c < 1.0 else 0.0
     h = s * pt
     h[n] = g
     return h, g
 
 
-def cactus_sequence(pt_rows, pd_rows, tokens, r, u, delta: float):
+def cactus_sequence(pt_rows, pd_rows, tokens, r, u, delta: float, exact_kl: bool = False):
     """One sequence of Cactus draft-and-verify over m positions.
 
     Position k accepts its candidate n iff r < gamma*/pd(n) (reading R15: the
@@ -283,12 +334,12 @@ def cactus_sequence(pt_rows, pd_rows, tokens, r, u, delta: float):
         if not 0 <= n < V:
             raise ValueError("drafted token id out of range")
         c = float(pt_rows[k, n])
-        gstar[k] = cactus_gamma_star(c, delta)
+        gstar[k] = cactus_gamma_star_kl(c, delta) if exact_kl else cactus_gamma_star(c, delta)
         accept[k], margin_r[k] = accept_test(gstar[k], pd_rows[k, n], float(r[k]))
     rejected = np.flatnonzero(~accept)
     A = int(rejected[0]) if rejected.size else m
     if A < m:
-        h, _ = cactus_target(pt_rows[A], int(tokens[A]), delta)
+        h, _ = cactus_target(pt_rows[A], int(tokens[A]), delta, exact_kl)
         w = residual_weights(h, pd_rows[A])
         if not np.sum(w) > 0.0:  # R10, with h as the position's target
             w = h
@@ -300,8 +351,11 @@ def cactus_sequence(pt_rows, pd_rows, tokens, r, u, delta: float):
 
 
 def spec_cactus_verify(verifier_bits, draft_bits, draft_tokens, r_accept, u_resample,
-                       delta: float, temperature=1.0):
-    """Batched Cactus verification; same layout as :func:`spec_verify` plus gamma_star [B, m]."""
+                       delta: float, temperature=1.0, exact_kl: bool = False):
+    """Batched Cactus verification; same layout as :func:`spec_verify` plus gamma_star [B, m].
+
+    ``exact_kl`` takes gamma* as the exact root of the KL constraint instead of
+    its Taylor form."""
     if not (delta >= 0.0 and math.isfinite(delta)):
         raise ValueError("delta must be finite and >= 0")
     B, m1, V = np.shape(verifier_bits)
@@ -317,7 +371,7 @@ def spec_cactus_verify(verifier_bits, draft_bits, draft_tokens, r_accept, u_resa
     for b in range(B):
         pt = softmax_t(widen_bf16(verifier_bits[b]), temperature)
         pd = softmax_t(widen_bf16(draft_bits[b]), temperature)
-        res = cactus_sequence(pt, pd, draft_tokens[b], r_accept[b], u_resample[b], delta)
+        res = cactus_sequence(pt, pd, draft_tokens[b], r_accept[b], u_resample[b], delta, exact_kl)
         out["accepted_len"][b] = res["A"]
         out["out_token"][b] = res["token"]
         out["accept_mask"][b] = res["accept"]

@@ -172,3 +172,143 @@ def test_always_reject_when_candidate_has_no_verifier_mass():
     pd = oracle.softmax_t(np.array([0.0, -1.0, -1.0]), 1.0)
     res = oracle.cactus_sequence(np.stack([pt, pt]), pd[None, :], [0], [0.0], [0.5, 0.5], 1.0)
     assert res["A"] == 0 and res["gamma_star"][0] == 0.0 and res["token"] in (1, 2)
+
+
+# ---------------------------------------------------------------------------
+# Exact-KL gamma* (Key design 2's root, without Key design 3's Taylor step)
+# ---------------------------------------------------------------------------
+
+def _binary_kl_scipy(g, c):
+    """The divergence of the two-outcome law (g, 1-g) from (c, 1-c), by scipy's rel_entr."""
+    from scipy.special import rel_entr
+    return float(rel_entr(g, c) + rel_entr(1.0 - g, 1.0 - c))
+
+
+def test_exact_kl_inverts_the_divergence():
+    """For a chosen gamma in (c, 1), delta := KL((g,1-g) || (c,1-c)) must give gamma back."""
+    rng = np.random.default_rng(10)
+    for _ in range(3000):
+        c = float(10 ** rng.uniform(-8, 0)) * 0.999
+        g = c + (1.0 - c) * float(rng.uniform(0.001, 0.999))
+        delta = _binary_kl_scipy(g, c)
+        got = oracle.cactus_gamma_star_kl(c, delta)
+        assert abs(got - g) <= 1e-9 * (g - c) + 4e-16, (c, g, delta, got)
+
+
+def test_exact_kl_full_vocab_divergence_equals_budget():
+    """KL(h || pt) over the whole vocabulary, by scipy, is delta when gamma* < 1 and at most
+    delta when clipped to 1."""
+    from scipy.special import rel_entr
+    rng = np.random.default_rng(11)
+    clipped = tight = 0
+    for _ in range(800):
+        V = int(rng.integers(2, 50))
+        pt = oracle.softmax_t(rng.normal(0, 2.5, V), 1.0)
+        n = int(rng.integers(V))
+        delta = float(10 ** rng.uniform(-5, 0.7))
+        h, g = oracle.cactus_target(pt, n, delta, exact_kl=True)
+        assert abs(h.sum() - 1.0) < 1e-12 and h[n] == g and g >= pt[n]
+        d = float(np.sum(rel_entr(h, pt)))
+        if g < 1.0:
+            tight += 1
+            assert abs(d - delta) <= 1e-9 * delta, (pt[n], delta, d)
+        else:
+            clipped += 1
+            assert d <= delta * (1 + 1e-12) and -math.log(pt[n]) <= delta * (1 + 1e-12)
+    assert tight > 300 and clipped > 10
+
+
+def test_exact_kl_is_the_constrained_optimum_brute_force():
+    """Key design 1 on a 3-token vocabulary: the largest h_n over a grid of distributions h with
+    KL(h || q) <= delta matches gamma* (the grid also tries the splits Theorem 2 rules out)."""
+    from scipy.special import rel_entr
+    q = np.array([0.25, 0.15, 0.6])
+    step = 1.0 / 1500
+    grid = np.arange(0.0, 1.0 + step / 2, step)
+    hn, ha = np.meshgrid(grid, grid, indexing="ij")
+    hb = 1.0 - hn - ha
+    ok = hb >= -1e-12
+    for n in range(3):
+        others = [i for i in range(3) if i != n]
+        H = np.zeros(hn.shape + (3,))
+        H[..., n], H[..., others[0]], H[..., others[1]] = hn, ha, np.maximum(hb, 0.0)
+        D = np.sum(rel_entr(H, q), axis=-1)
+        for delta in [0.01, 0.1, 0.4]:
+            best = float(hn[ok & (D <= delta)].max())
+            g = oracle.cactus_gamma_star_kl(float(q[n]), delta)
+            assert g - 2 * step <= best <= g + 1e-12, (n, delta, best, g)
+
+
+def test_exact_kl_edges_monotone_and_corollary6():
+    """delta = 0 and c = 0 give c; -log c <= delta gives 1; gamma* grows with delta; Corollary 6
+    (Taylor gamma* <= 0.5 keeps KL <= delta) makes the Taylor value a lower bound there; the
+    Taylor step is exact to first order as delta -> 0."""
+    assert oracle.cactus_gamma_star_kl(0.3, 0.0) == 0.3
+    assert oracle.cactus_gamma_star_kl(0.0, 2.0) == 0.0
+    assert oracle.cactus_gamma_star_kl(1.0, 0.5) == 1.0
+    assert oracle.cactus_gamma_star_kl(0.7, -math.log(0.7)) == 1.0
+    assert oracle.cactus_gamma_star_kl(0.7, 0.999 * -math.log(0.7)) < 1.0
+    rng = np.random.default_rng(12)
+    below = 0
+    for _ in range(2000):
+        c = float(rng.uniform(1e-6, 1.0))
+        ds = np.sort(10 ** rng.uniform(-6, 0.5, 6))
+        gs = [oracle.cactus_gamma_star_kl(c, float(d)) for d in ds]
+        assert all(c <= g <= 1.0 for g in gs) and np.all(np.diff(gs) >= 0.0)
+        for d, g in zip(ds, gs):
+            gt = oracle.cactus_gamma_star(c, float(d))
+            if gt <= 0.5:
+                below += 1
+                assert gt <= g * (1 + 1e-15), (c, d, gt, g)
+    assert below > 1000
+    for c in [0.05, 0.3, 0.5, 0.8]:
+        ratio = (oracle.cactus_gamma_star_kl(c, 1e-10) - c) / (oracle.cactus_gamma_star(c, 1e-10) - c)
+        assert abs(ratio - 1.0) < 1e-3
+
+
+def test_exact_kl_delta_zero_is_sps():
+    rng = np.random.default_rng(13)
+    for _ in range(100):
+        V, K = int(rng.integers(2, 40)), int(rng.integers(1, 6))
+        pt, pd = rand_rows(rng, V, K)
+        toks = np.array([rng.choice(V, p=pd[k]) for k in range(K)])
+        r = rng.random(K, dtype=np.float32)
+        u = rng.random(K + 1, dtype=np.float32)
+        a = oracle.sps_sequence(pt, pd, toks, r, u)
+        c = oracle.cactus_sequence(pt, pd, toks, r, u, 0.0, exact_kl=True)
+        assert a["A"] == c["A"] and a["token"] == c["token"] and a["margin_u"] == c["margin_u"]
+        np.testing.assert_array_equal(a["accept"], c["accept"])
+
+
+def test_exact_kl_law_brute_force():
+    """Monte-Carlo frequencies of an exact-KL Cactus position match its mixture law, and its
+    acceptance is at least the Taylor one's where Corollary 6 applies."""
+    rng = np.random.default_rng(14)
+    V, n_mc, delta = 4, 30000, 0.3
+    pt = oracle.softmax_t(rng.normal(0, 1.2, V), 1.0)
+    pd = oracle.softmax_t(rng.normal(0, 1.2, V), 1.0)
+    law = np.zeros(V)
+    for n in range(V):
+        h, g = oracle.cactus_target(pt, n, delta, exact_kl=True)
+        phi = min(1.0, g / pd[n])
+        w = np.maximum(h - pd, 0.0)
+        law[n] += pd[n] * phi
+        if phi < 1.0:
+            law += pd[n] * (1.0 - phi) * w / w.sum()
+    assert abs(law.sum() - 1.0) < 1e-12
+    counts = np.zeros(V)
+    rows_t = np.stack([pt, pt])
+    for _ in range(n_mc):
+        n = int(rng.choice(V, p=pd))
+        res = oracle.cactus_sequence(rows_t, pd[None, :], [n], rng.random(1, dtype=np.float32),
+                                     rng.random(2, dtype=np.float32), delta, exact_kl=True)
+        counts[n if res["A"] == 1 else res["token"]] += 1
+    assert stats.chisquare(counts, n_mc * law).pvalue > 1e-4
+
+
+def test_planted_kl_mistake_is_caught(monkeypatch):
+    """Dropping the (1 - g) term of the divergence fails the inversion pin."""
+    monkeypatch.setattr(so, "cactus_kl", lambda g, c: g * (math.log(g) - math.log(c)) if g > 0 else 0.0)
+    c, g = 0.2, 0.45
+    got = so.cactus_gamma_star_kl(c, _binary_kl_scipy(g, c))
+    assert abs(got - g) > 1e-3
