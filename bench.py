@@ -29,6 +29,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -87,12 +88,13 @@ def _dev(torch, bits):
 
 
 class SpsLike(Workload):
-    """spec_verify (delta None) or spec_cactus_verify over one SpsWorkload."""
+    """spec_verify (delta None) or spec_cactus_verify (spec_cactus_kl_verify with
+    exact_kl) over one SpsWorkload."""
 
-    def __init__(self, key, w, delta=None):
-        self.key, self.w, self.delta = key, w, delta
+    def __init__(self, key, w, delta=None, exact_kl=False):
+        self.key, self.w, self.delta, self.exact_kl = key, w, delta, exact_kl
         B, K, V = w.B, w.K, w.V
-        self.desc = w.name + ("" if delta is None else f" delta={delta}")
+        self.desc = w.name + ("" if delta is None else f" delta={delta}") + (" exact-KL gamma*" if exact_kl else "")
         self.positions = B * K
         rows = B * (K + 1) + B * K
         small = B * K * 4 * 2 + B * (K + 1) * 4 + B * 4 * 2 + B * K + (B * K * 4 if delta is not None else 0)
@@ -119,7 +121,8 @@ class SpsLike(Workload):
                           for t, d in self.copies]
         else:
             self.calls = [binding.prepare_cactus_verify(t, d, self.tok, self.r, self.u, self.delta,
-                                                        self.w.temperature, workspace=self.ws)
+                                                        self.w.temperature, workspace=self.ws,
+                                                        exact_kl=self.exact_kl)
                           for t, d in self.copies]
         log(f"{len(self.copies)} input copies of {2 * (t.numel() + d.numel()) / 1e6:.1f} MB")
 
@@ -137,7 +140,7 @@ class SpsLike(Workload):
                 oracle.spec_verify(x["target"][sl], x["draft"][sl], x["draft_tokens"][sl], x["r"][sl], x["u"][sl])
             else:
                 oracle.spec_cactus_verify(x["target"][sl], x["draft"][sl], x["draft_tokens"][sl], x["r"][sl],
-                                          x["u"][sl], self.delta)
+                                          x["u"][sl], self.delta, exact_kl=self.exact_kl)
             done += 1
             pos += self.w.K
             if time.perf_counter() - t0 >= budget_s:
@@ -209,6 +212,7 @@ def workloads():
         "qwen_cactus": lambda: SpsLike("qwen_cactus", gen.QWEN_CACTUS, delta=1.0),
         "qwen_cactus_d0": lambda: SpsLike("qwen_cactus_d0", gen.QWEN_CACTUS, delta=0.0),
         "qwen_cactus_d05": lambda: SpsLike("qwen_cactus_d05", gen.QWEN_CACTUS, delta=0.5),
+        "qwen_cactus_kl": lambda: SpsLike("qwen_cactus_kl", gen.QWEN_CACTUS, delta=1.0, exact_kl=True),
         "hedge_eval": lambda: GammaLike("hedge_eval", gen.HEDGE_EVAL),
         "pool21": lambda: GammaLike("pool21", gen.POOL21),
         "small_mixed": lambda: GammaLike("small_mixed", gen.SMALL_MIXED),
@@ -242,7 +246,8 @@ def summarize_pmc(key: str, fetch_csv: str, write_csv: str, calib_mib: int, comm
             if r["Counter_Name"] != counter:
                 continue
             v = float(r["Counter_Value"])
-            if r["Kernel_Name"].startswith(f"specv::{kernel}("):
+            # plain or template instance, with or without the demangled return type
+            if re.match(rf"(void )?specv::{kernel}(<[^>]*>)?\(", r["Kernel_Name"]):
                 mine.append(v)
             elif "copyBuffer" in r["Kernel_Name"] and v > 0.4 * calib_mib * 1024:
                 calib.append(v)

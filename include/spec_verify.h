@@ -153,6 +153,30 @@ int spec_cactus_verify(const spec_bf16* verifier, int64_t verifier_row_stride,
                        void* workspace, size_t workspace_bytes, spec_stream_t stream);
 
 /*
+ * spec_cactus_kl_verify -- Cactus with gamma* the exact root of the KL budget.
+ *
+ * [CA] Key designs 1-2 with the KL divergence, without the second-order Taylor
+ * step of Key design 3 (which the note derives because the equation has no
+ * closed form).  gamma* is the largest g in [c, 1] whose target h (h_n = g,
+ * h_x = (1 - g) / (1 - c) * pt(x) otherwise) keeps KL(h || pt) <= delta; for
+ * that h the divergence is g ln(g / c) + (1 - g) ln((1 - g) / (1 - c)).
+ * gamma* = 1 when -ln c <= delta, and c when delta = 0 or c = 0.  It is found
+ * in float64 (bracketed Newton steps, at most 100, to a few ulps).  Everything
+ * else -- the acceptance test, the recovery draw, the bonus, the layout, the
+ * outputs, the workspace and the status codes -- is spec_cactus_verify's, and
+ * delta = 0 again returns exactly the spec_verify results.  The Taylor value
+ * never exceeds this gamma* where it is <= 0.5 (Corollary 6), so this call
+ * accepts at least as often there.
+ */
+int spec_cactus_kl_verify(const spec_bf16* verifier, int64_t verifier_row_stride,
+                          const spec_bf16* draft, int64_t draft_row_stride,
+                          const int32_t* draft_tokens, const float* r_accept, const float* u_resample,
+                          int B, int m, int V, float delta, float temperature,
+                          int32_t* accepted_len, int32_t* out_token, uint8_t* accept_mask,
+                          float* gamma_star,
+                          void* workspace, size_t workspace_bytes, spec_stream_t stream);
+
+/*
  * spec_counterfactual_gamma -- HedgeSpec full-information evaluation of N drafters.
  *
  * For every sequence b, position k < K and drafter i ([NB] Key design 1, and

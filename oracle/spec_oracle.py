@@ -256,22 +256,39 @@ def cactus_gamma_star(c: float, delta: float) -> float:
     return min(c + math.sqrt(2.0 * delta * c * (1.0 - c)), 1.0)
 
 
+def _kl_share(g: float, c: float, d: float) -> float:
+    """c * phi(g / c) with phi(t) = t ln t - t + 1 >= 0, and d = g - c given exactly.
+
+    Written as g ln(1 + d / c) - d; when d / c is small the two parts cancel,
+    so phi(1 + x) = sum_{k>=2} (-1)^k x^k / (k (k - 1)) is summed instead
+    (x^2 / 2 - x^3 / 6 + ..., through x^8: below 1e-15 of it for |x| < 0.01).
+    """
+    if g <= 0.0:
+        return c                    # phi(0) = 1
+    x = d / c if c > 0.0 else math.inf
+    if abs(x) < 0.01:
+        return c * sum((-1.0) ** k * x ** k / (k * (k - 1)) for k in range(2, 9))
+    lr = math.log1p(x) if x < 1e10 else math.log(g) - math.log(c)
+    return g * lr - d
+
+
 def cactus_kl(g: float, c: float) -> float:
     """KL(h || pt) in nats of the Theorem-2 target h with h_n = g ([CA] Key design 2).
 
     The tokens other than n keep pt's proportions, so the divergence over the
-    vocabulary collapses to the two-outcome one:
-    g log(g / c) + (1 - g) log((1 - g) / (1 - c)), with 0 log 0 = 0 and
-    +inf where g > 0 meets c = 0.
+    vocabulary collapses to the two-outcome one,
+    g ln(g / c) + (1 - g) ln((1 - g) / (1 - c)), with 0 ln 0 = 0 and +inf where
+    g > 0 meets c = 0.  It is evaluated as c phi(g / c) + (1 - c) phi((1 - g) / (1 - c)),
+    phi(t) = t ln t - t + 1: the same sum (the added -t + 1 terms cancel
+    between the two outcomes), but as two non-negative parts that do not
+    cancel each other.
     """
     if g > 0.0 and c <= 0.0:
         return math.inf
-    t1 = g * (math.log(g) - math.log(c)) if g > 0.0 else 0.0
-    if g < 1.0:
-        t2 = (1.0 - g) * (math.log1p(-g) - math.log1p(-c)) if c < 1.0 else math.inf
-    else:
-        t2 = 0.0
-    return t1 + t2
+    if g < 1.0 and c >= 1.0:
+        return math.inf
+    d = g - c
+    return _kl_share(g, c, d) + _kl_share(1.0 - g, 1.0 - c, -d)
 
 
 def cactus_gamma_star_kl(c: float, delta: float) -> float:

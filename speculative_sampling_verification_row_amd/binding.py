@@ -41,6 +41,7 @@ _SIGNATURES = {
     "spec_workspace_init": (_I, [_P, _SZ, _P]),
     "spec_verify": (_I, [_P, _I64, _P, _I64, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P]),
     "spec_cactus_verify": (_I, [_P, _I64, _P, _I64, _P, _P, _P, _I, _I, _I, _F, _F, _P, _P, _P, _P, _P, _SZ, _P]),
+    "spec_cactus_kl_verify": (_I, [_P, _I64, _P, _I64, _P, _P, _P, _I, _I, _I, _F, _F, _P, _P, _P, _P, _P, _SZ, _P]),
     "spec_counterfactual_gamma": (_I, [_P, _I64, _I, _P, _I64, _I64, _P, _I, _I, _I, _I, _F, _P, _P, _P,
                                        _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "hedge_update": (_I, [_P, _P, _P, _P, _F, _P, _P, _I, _I, _P]),
@@ -174,6 +175,16 @@ def spec_cactus_verify(verifier, draft, draft_tokens, r_accept, u_resample, delt
                                  with_gamma_star=with_gamma_star).launch(stream)
 
 
+def spec_cactus_kl_verify(verifier, draft, draft_tokens, r_accept, u_resample, delta: float,
+                          temperature: float = 1.0, *, workspace=None, with_mask: bool = True,
+                          with_gamma_star: bool = True, stream=None):
+    """Cactus verification with gamma* the exact root of the KL budget; returns
+    (accepted_len, out_token, accept_mask, gamma_star)."""
+    return prepare_cactus_verify(verifier, draft, draft_tokens, r_accept, u_resample, delta, temperature,
+                                 workspace=workspace, with_mask=with_mask, with_gamma_star=with_gamma_star,
+                                 exact_kl=True).launch(stream)
+
+
 def prepare_verify(target, draft, draft_tokens, r_accept, u_resample, temperature: float = 1.0, *,
                    workspace: Optional[torch.Tensor] = None, with_mask: bool = True) -> Launcher:
     """spec_verify with its tensors fixed (see Launcher)."""
@@ -183,9 +194,10 @@ def prepare_verify(target, draft, draft_tokens, r_accept, u_resample, temperatur
 
 def prepare_cactus_verify(verifier, draft, draft_tokens, r_accept, u_resample, delta: float,
                           temperature: float = 1.0, *, workspace=None, with_mask: bool = True,
-                          with_gamma_star: bool = True) -> Launcher:
-    """spec_cactus_verify with its tensors fixed (see Launcher)."""
-    return _prepare_verify("spec_cactus_verify", verifier, draft, draft_tokens, r_accept, u_resample, delta,
+                          with_gamma_star: bool = True, exact_kl: bool = False) -> Launcher:
+    """spec_cactus_verify (spec_cactus_kl_verify with exact_kl) with its tensors fixed (see Launcher)."""
+    name = "spec_cactus_kl_verify" if exact_kl else "spec_cactus_verify"
+    return _prepare_verify(name, verifier, draft, draft_tokens, r_accept, u_resample, delta,
                            temperature, workspace, with_mask, with_gamma_star)
 
 

@@ -1,7 +1,8 @@
 // libspecverify: batched speculative-sampling verification on gfx950.
 //
-// Two persistent kernels: `verify_kernel` serves spec_verify and
-// spec_cactus_verify, `gamma_kernel` serves spec_counterfactual_gamma.  A grid is
+// Two persistent kernels: `verify_kernel` serves spec_verify, spec_cactus_verify
+// and (an instance of its own) spec_cactus_kl_verify, `gamma_kernel` serves
+// spec_counterfactual_gamma.  A grid is
 // the number of workgroups the device holds at once (G), and every workgroup g
 // runs its phases on a fixed schedule; nothing is claimed from a shared counter.
 //
@@ -97,6 +98,7 @@ struct Params {
   int B, K, N, V;
   float c;  // log2(e) / T
   double delta;
+  int kl_exact;  // Cactus gamma*: 0 the Taylor form, 1 the exact root of the KL budget (verify_kernel<true>)
   int mode;
   int fused;
   // schedule
@@ -586,6 +588,7 @@ struct Decision {
 
 struct DecideLds {
   Decision d;
+  double ct[SPEC_MAX_K];  // exact-KL Cactus: pt(n) of every position (-1: no valid token)
 };
 
 struct Lds {
@@ -600,9 +603,80 @@ struct Lds {
 
 __device__ __forceinline__ int draw_drafter(const Params& p, int b) { return p.mode == MODE_VERIFY ? 0 : p.sel[b]; }
 
+// One outcome's part of a two-outcome KL divergence, c * phi(1 + x) with
+// phi(t) = t ln t - t + 1 >= 0 and x = (g - c) / c: `plain` is its direct form
+// g ln(1 + x) - (g - c), whose two parts cancel when x is small; there phi(1 + x)
+// is the series x^2 / 2 - x^3 / 6 + x^4 / 12 - ... (the k-th term
+// (-1)^k x^k / (k (k - 1))), through x^8: below 1e-15 of the sum for |x| < 0.01.
+__host__ __device__ inline double kl_share(double c, double x, double plain) {
+  if (!(fabs(x) < 0.01)) return plain;
+  const double q = 1.0 / 30 + x * (-1.0 / 42 + x * (1.0 / 56));
+  return c * (x * x * (0.5 + x * (-1.0 / 6 + x * (1.0 / 12 + x * (-1.0 / 20 + x * q)))));
+}
+
+// [CA] Key designs 1-2 with the KL divergence, before Key design 3's Taylor
+// step: the largest g in [c, 1] whose target h (h_n = g, the other tokens pt
+// scaled by (1 - g) / (1 - c)) keeps KL(h || pt) <= delta.  For that h the
+// divergence is the two-outcome f(g) = g ln(g / c) + (1 - g) ln((1 - g) / (1 - c)),
+// evaluated as c phi(g / c) + (1 - c) phi((1 - g) / (1 - c)) (kl_share: the same
+// sum as two non-negative parts), with f'(g) = ln(g / c) - ln((1 - g) / (1 - c)).
+// f is increasing and convex on [c, 1], so Newton steps from above the root
+// descend to it, and one from below lands above it; a step that leaves the
+// bracket [lo, hi] (f(lo) <= delta < f(hi)) is replaced by the bracket's
+// geometric midpoint (the root can sit many decades below 1).  The Taylor value
+// starts it, its product taken as two square roots so that it does not underflow.
+// It stops once a step is below 1e-8 of min(g - c, 1 - g): Newton's error after
+// such a step is of the order of its square over that distance (f' vanishes at
+// c and f'' grows near 1), so g - c, g and 1 - g (the scale s of the other tokens)
+// are then exact to about 1e-16 relative.  `iters` (host checks) receives the
+// number of steps taken.
+constexpr int kKlMaxSteps = 100;
+__host__ __device__ inline double gamma_star_kl(double c, double delta, int* iters = nullptr) {
+  if (iters) *iters = 0;
+  if (!(delta > 0.0) || !(c > 0.0)) return c;
+  if (c >= 1.0) return 1.0;
+  const double lc = log(c);
+  if (-lc <= delta) return 1.0;  // the one-hot target fits the budget
+  const double c1 = 1.0 - c, rc = 1.0 / c, rc1 = 1.0 / c1;
+  double lo = c, hi = 1.0;
+  // a point strictly inside the bracket, or lo when none is left (adjacent doubles)
+  auto mid = [&] {
+    const double m = sqrt(lo) * sqrt(hi), a = 0.5 * (lo + hi);
+    return m > lo && m < hi ? m : a > lo && a < hi ? a : lo;
+  };
+  double g = c + sqrt(2.0 * delta) * sqrt(c * c1);
+  if (g == c) return c;  // the Taylor step is below half an ulp of c: so is the root's
+  if (!(g < hi)) g = mid();
+  for (int it = 0; it < kKlMaxSteps; ++it) {
+    if (iters) *iters = it + 1;
+    const double d = g - c, x = d * rc, y = -d * rc1;
+    const double l1 = x < 1e300 ? log1p(x) : log(g) - lc;  // ln(g / c)
+    const double l2 = log1p(y);                            // ln((1 - g) / (1 - c))
+    const double f = kl_share(c, x, g * l1 - d) + kl_share(c1, y, (1.0 - g) * l2 + d) - delta;
+    if (f <= 0.0)
+      lo = g;
+    else
+      hi = g;
+    const double gn = g - f / (l1 - l2);
+    // converged: the step is within the tolerance (g may itself be lo or hi)
+    if (fabs(gn - g) <= 1e-8 * fmin(d, 1.0 - g)) return gn >= lo && gn <= hi ? gn : g;
+    g = gn > lo && gn < hi ? gn : mid();
+    if (g == lo) return lo;  // the bracket is down to adjacent doubles
+  }
+  return lo;
+}
+
+// The divergence f(g) of gamma_star_kl itself, for 0 < c < 1 and c <= g < 1.
+__host__ __device__ inline double kl_divergence(double g, double c) {
+  const double c1 = 1.0 - c, d = g - c, x = d / c, y = -d / c1;
+  const double l1 = x < 1e300 ? log1p(x) : log(g) - log(c);
+  return kl_share(c, x, g * l1 - d) + kl_share(c1, y, (1.0 - g) * log1p(y) + d);
+}
+
 // Merge the statistics of target rows 0..K and drafter `drafter`'s rows 0..K-1,
 // take every accept decision, and describe the draw.  Writes accept_mask and
 // gamma_star when `write_outputs`.  The result is in L.dl.d after the call.
+template <bool KL = false>
 __device__ __forceinline__ void decide(const Params& p, int b, bool write_outputs, int pre_n, Lds& L) {
   const int K = p.K, V = p.V;
   const int t = threadIdx.x;
@@ -636,12 +710,22 @@ __device__ __forceinline__ void decide(const Params& p, int b, bool write_output
       // [CA] Key design 3 with the verifier's probability c of the candidate; delta = 0 is SpS.
       ct = fmin(token_prob(zt, p.c, st), 1.0);
       const double cd = token_prob(zd, p.c, sd);
-      gs = fmin(ct + sqrt(2.0 * p.delta * ct * (1.0 - ct)), 1.0);
-      const double ratio = cd > 0.0 ? gs / cd : (gs > 0.0 ? __builtin_inf() : 0.0);
-      acc = static_cast<double>(rr) < ratio;  // [LT] §5.1: strict
+      if (KL && p.delta > 0.0) {
+        // accept iff r pd(n) < gamma*, decided without the root: gamma* >= c,
+        // gamma* <= 1, and the divergence grows on [c, 1], so x = r pd(n) in [c, 1)
+        // lies below gamma* exactly when its divergence is below delta (c = 0
+        // leaves gamma* = 0, which nothing lies below).  The draw finds gamma*.
+        const double xr = static_cast<double>(rr) * cd;
+        acc = ct > 0.0 && (xr < ct || (xr < 1.0 && kl_divergence(xr, ct) < p.delta));
+      } else {
+        gs = fmin(ct + sqrt(2.0 * p.delta * ct * (1.0 - ct)), 1.0);
+        const double ratio = cd > 0.0 ? gs / cd : (gs > 0.0 ? __builtin_inf() : 0.0);
+        acc = static_cast<double>(rr) < ratio;  // [LT] §5.1: strict
+        if (write_outputs && p.gamma_star) p.gamma_star[b * K + t] = static_cast<float>(gs);
+      }
       state = acc ? ST_ACCEPT : ST_REJECT;
-      if (write_outputs && p.gamma_star) p.gamma_star[b * K + t] = static_cast<float>(gs);
     }
+    if (KL) L.dl.ct[t] = tok_ok ? ct : -1.0;
     if (write_outputs && p.accept_mask) p.accept_mask[b * K + t] = acc ? 1 : 0;
   }
   // wave 0: the first rejection A (ballots over the positions) and the draw
@@ -677,7 +761,9 @@ __device__ __forceinline__ void decide(const Params& p, int b, bool write_output
         w.kt = L.m.rk[A];
         w.kd = L.m.rk[K + 1 + A];
         w.r = L.m.rs[A] / L.m.rs[K + 1 + A];
-        w.s_scale = ctA < 1.0 ? (1.0 - gsA) / (1.0 - ctA) : 0.0;  // [CA] Key design 2 (1.0 exactly at delta = 0)
+        // [CA] Key design 2 (1.0 exactly at delta = 0); with the exact-KL gamma*
+        // the draw sets both once it has gamma* (kl_positions)
+        w.s_scale = ctA < 1.0 ? (1.0 - gsA) / (1.0 - ctA) : 0.0;
         w.hn = gsA * L.m.rs[A];
         w.n = nA;
         w.special = p.delta > 0.0 ? 1 : 0;
@@ -785,8 +871,22 @@ __device__ __forceinline__ int exchange_totals(const Params& p, int b, int x, do
 // the draw row (pair), the totals exchanged, and, if the crossing falls in this
 // slice, the token from the rows still held in registers.  Returns the crossing
 // slice (-1: the draw has no mass).
-template <int MODE, bool SPECIAL>
-__device__ __forceinline__ int draw_slice(const Params& p, int b, int x, const Decision& d, Lds& L) {
+// Exact-KL Cactus: gamma* of every position, lane t < K solving position t (K <=
+// 64; every wave does the same work, so none waits for another).  Unit 0 writes
+// them out (`write`); the result is gamma* of position A (0 if A is none).
+__device__ __forceinline__ double kl_positions(const Params& p, int b, bool write, int A, const Lds& L) {
+  const int t = lane_id();
+  const double ct = t < p.K ? L.dl.ct[t] : -1.0;
+  double gsv = 0.0;
+  if (ct >= 0.0) gsv = gamma_star_kl(ct, p.delta);
+  if (write && wave_id() == 0 && ct >= 0.0 && p.gamma_star) p.gamma_star[b * p.K + t] = static_cast<float>(gsv);
+  return A >= 0 && A < p.K ? readlane_f64(gsv, A) : 0.0;
+}
+
+// With KL (exact-KL Cactus, delta > 0), the residual's gamma* is found here, while
+// the slice's loads are in flight, and completes d.w.
+template <int MODE, bool SPECIAL, bool KL = false>
+__device__ __forceinline__ int draw_slice(const Params& p, int b, int x, Decision& d, Lds& L) {
   const int tid = threadIdx.x, wave = wave_id();
   const uint16_t* trow = target_row(p, b, d.draw_row);
   const uint16_t* drow = d.pair ? draft_row(p, b, draw_drafter(p, b), d.draw_row) : trow;
@@ -801,6 +901,12 @@ __device__ __forceinline__ int draw_slice(const Params& p, int b, int x, const D
     const uint32_t uo = static_cast<uint32_t>((x * kTilesPerSlice + q) * kThreads) * 16u;
     vt[q] = buffer_load16(tr, tid * 16u, uo);
     vd[q] = MODE == W_RESID ? buffer_load16(dr, tid * 16u, uo) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  if (KL && MODE == W_RESID && SPECIAL) {
+    const double gsA = kl_positions(p, b, x == 0, d.A, L);
+    const double ctA = L.dl.ct[d.A];
+    d.w.s_scale = ctA < 1.0 ? (1.0 - gsA) / (1.0 - ctA) : 0.0;
+    d.w.hn = gsA * L.m.rs[d.A];
   }
 #pragma unroll
   for (int q = 0; q < kTilesPerSlice; ++q) {
@@ -863,9 +969,12 @@ __device__ __forceinline__ void target_h_draw(const Params& p, int b, const Deci
 // outputs of a sequence with no valid draw, and the outputs of a draw with no
 // mass.  `pre_n`: the drafted token of position threadIdx.x, loaded ahead of
 // time, or kNoToken.
+template <bool KL = false>
 __device__ __forceinline__ void unit_draw(const Params& p, int b, int x, int pre_n, Lds& L) {
-  decide(p, b, x == 0, pre_n, L);
-  const Decision d = L.dl.d;
+  decide<KL>(p, b, x == 0, pre_n, L);
+  Decision d = L.dl.d;
+  // exact-KL gamma* outputs where the draw does not find them (no residual draw)
+  if (KL && x == 0 && p.delta > 0.0 && p.gamma_star && !(d.A >= 0 && d.pair)) kl_positions(p, b, true, -1, L);
   int xs;
   if (d.A < 0) {
     // no draw: the totals are still exchanged, so that unit 0 knows when to clear
@@ -879,7 +988,7 @@ __device__ __forceinline__ void unit_draw(const Params& p, int b, int x, int pre
     }
   } else {
     xs = !d.pair       ? draw_slice<W_TARGET, false>(p, b, x, d, L)
-         : d.w.special ? draw_slice<W_RESID, true>(p, b, x, d, L)
+         : d.w.special ? draw_slice<W_RESID, true, KL>(p, b, x, d, L)
                        : draw_slice<W_RESID, false>(p, b, x, d, L);
     if (xs < 0 && x == 0) {
       if (d.w.special)
@@ -1387,6 +1496,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // Verify calls (spec_verify, spec_cactus_verify): phase 0, then the draw units
 // g, g + G, ...  It is the gamma kernel without the groups and the estimator, so
 // it holds less LDS and fewer registers.
+// KL: Cactus gamma* as the exact root of the KL budget (spec_cactus_kl_verify), a
+// separate instance so that the other calls keep the leaner code.
+template <bool KL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void verify_kernel(Params p) {
   __shared__ Lds L;
   const int G = gridDim.x, g = blockIdx.x;
@@ -1399,7 +1511,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int u = g; u < T1; u += G) {
     __syncthreads();
     const int b = u / p.P1;
-    unit_draw(p, b, u - b * p.P1, u == g ? pre_n : kNoToken, L);
+    unit_draw<KL>(p, b, u - b * p.P1, u == g ? pre_n : kNoToken, L);
   }
 }
 
@@ -1562,7 +1674,7 @@ static int compute_units() {
 
 template <class Kernel>
 static int resident_workgroups(Kernel kernel, int which) {
-  static int cache[2][64] = {{0}};
+  static int cache[3][64] = {{0}};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (dev >= 0 && dev < 64 && cache[which][dev] > 0) return cache[which][dev];
@@ -1593,7 +1705,8 @@ static int launch_flow(Params& p, const Shape& s, hipStream_t stream) {
   if (s.total0 > 0x3fffffffLL || static_cast<int64_t>(s.B) * s.P1 > 0x3fffffffLL || s.ngroups > 0x3fffffffLL)
     return SPEC_ERR_SHAPE;
   const bool verify = s.mode == MODE_VERIFY;
-  int grid = verify ? resident_workgroups(verify_kernel, 0) : resident_workgroups(gamma_kernel, 1);
+  int grid = verify ? (p.kl_exact ? resident_workgroups(verify_kernel<true>, 2) : resident_workgroups(verify_kernel<false>, 0))
+                    : resident_workgroups(gamma_kernel, 1);
   if (grid <= 0) return SPEC_ERR_HIP;
   const int ncu = compute_units();
   const int slots = ncu > 0 && grid % ncu == 0 ? grid / ncu : 1;
@@ -1608,8 +1721,10 @@ static int launch_flow(Params& p, const Shape& s, hipStream_t stream) {
   plan_units(p, s);
   p.ncu = ncu;
   p.slots = slots;  // make_split weights the slots only when the grid is all of them
-  if (verify)
-    hipLaunchKernelGGL(verify_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
+  if (verify && p.kl_exact)
+    hipLaunchKernelGGL(verify_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, p);
+  else if (verify)
+    hipLaunchKernelGGL(verify_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, p);
   else
     hipLaunchKernelGGL(gamma_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
@@ -1626,8 +1741,8 @@ static float log2e_over(float T) { return static_cast<float>(1.44269504088896340
 
 static int verify_common(const spec_bf16* target, int64_t ts, const spec_bf16* draft, int64_t ds,
                          const int32_t* tokens, const float* r, const float* u, int B, int K, int V, double delta,
-                         float T, int32_t* A, int32_t* tok, uint8_t* mask, float* gstar, void* ws, size_t wsb,
-                         hipStream_t stream) {
+                         int kl_exact, float T, int32_t* A, int32_t* tok, uint8_t* mask, float* gstar, void* ws,
+                         size_t wsb, hipStream_t stream) {
   int st = check_common(B, K, V, T);
   if (st != SPEC_OK) return st;
   if (!target || !draft || !tokens || !r || !u || !A || !tok) return SPEC_ERR_NULL;
@@ -1652,6 +1767,7 @@ static int verify_common(const spec_bf16* target, int64_t ts, const spec_bf16* d
   p.V = V;
   p.c = log2e_over(T);
   p.delta = delta;
+  p.kl_exact = kl_exact;
   p.mode = MODE_VERIFY;
   p.accepted_len = A;
   p.out_token = tok;
@@ -1700,7 +1816,7 @@ int spec_verify(const spec_bf16* target, int64_t target_row_stride, const spec_b
                 float temperature, int32_t* accepted_len, int32_t* out_token, uint8_t* accept_mask, void* workspace,
                 size_t workspace_bytes, spec_stream_t stream) {
   return verify_common(target, target_row_stride, draft, draft_row_stride, draft_tokens, r_accept, u_resample, B, K,
-                       V, 0.0, temperature, accepted_len, out_token, accept_mask, nullptr, workspace,
+                       V, 0.0, 0, temperature, accepted_len, out_token, accept_mask, nullptr, workspace,
                        workspace_bytes, stream);
 }
 
@@ -1711,7 +1827,18 @@ int spec_cactus_verify(const spec_bf16* verifier, int64_t verifier_row_stride, c
                        void* workspace, size_t workspace_bytes, spec_stream_t stream) {
   if (!(delta >= 0.0f) || !isfinite(delta)) return SPEC_ERR_PARAM;
   return verify_common(verifier, verifier_row_stride, draft, draft_row_stride, draft_tokens, r_accept, u_resample, B,
-                       m, V, static_cast<double>(delta), temperature, accepted_len, out_token, accept_mask,
+                       m, V, static_cast<double>(delta), 0, temperature, accepted_len, out_token, accept_mask,
+                       gamma_star, workspace, workspace_bytes, stream);
+}
+
+int spec_cactus_kl_verify(const spec_bf16* verifier, int64_t verifier_row_stride, const spec_bf16* draft,
+                          int64_t draft_row_stride, const int32_t* draft_tokens, const float* r_accept,
+                          const float* u_resample, int B, int m, int V, float delta, float temperature,
+                          int32_t* accepted_len, int32_t* out_token, uint8_t* accept_mask, float* gamma_star,
+                          void* workspace, size_t workspace_bytes, spec_stream_t stream) {
+  if (!(delta >= 0.0f) || !isfinite(delta)) return SPEC_ERR_PARAM;
+  return verify_common(verifier, verifier_row_stride, draft, draft_row_stride, draft_tokens, r_accept, u_resample, B,
+                       m, V, static_cast<double>(delta), 1, temperature, accepted_len, out_token, accept_mask,
                        gamma_star, workspace, workspace_bytes, stream);
 }
 

@@ -32,7 +32,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ["spec_verify", "spec_cactus_verify", "spec_counterfactual_gamma", "hedge_update",
+    for n in ["spec_verify", "spec_cactus_verify", "spec_cactus_kl_verify", "spec_counterfactual_gamma", "hedge_update",
               "spec_workspace_bytes", "spec_workspace_init", "spec_status_str"]:
         assert n in names, names
 
@@ -100,6 +100,9 @@ def test_cactus_validation(lib):
     assert lib.spec_cactus_verify(*args, -0.5, 1.0, *tail) == -3
     assert lib.spec_cactus_verify(*args, float("nan"), 1.0, *tail) == -3
     assert lib.spec_cactus_verify(*args, 0.5, 0.0, *tail) == -3
+    for delta, T, code in [(-0.5, 1.0, -3), (float("nan"), 1.0, -3), (float("inf"), 1.0, -3), (0.5, 0.0, -3),
+                           (0.5, 1.0, -5)]:   # the last: valid, rejected only by the tiny workspace
+        assert lib.spec_cactus_kl_verify(*args, delta, T, *tail) == code
 
 
 def test_gamma_validation(lib):

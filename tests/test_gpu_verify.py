@@ -1,4 +1,5 @@
-"""GPU parity: spec_verify and spec_cactus_verify against the float64 oracle.
+"""GPU parity: spec_verify, spec_cactus_verify and spec_cactus_kl_verify against the
+float64 oracle.
 
 Every case feeds the same seeded bf16 rows, tokens and uniforms to the HIP path
 (through the C ABI) and to the oracle, and compares element by element under
@@ -27,7 +28,7 @@ def B():
     return binding
 
 
-def run_verify(binding, x, T=1.0, delta=None, ws=None):
+def run_verify(binding, x, T=1.0, delta=None, ws=None, kl=False):
     t, d = dev_bf16(x["target"]), dev_bf16(x["draft"])
     tok, r, u = dev_i32(x["draft_tokens"]), dev_f32(x["r"]), dev_f32(x["u"])
     B_, K1 = x["target"].shape[:2]
@@ -37,7 +38,8 @@ def run_verify(binding, x, T=1.0, delta=None, ws=None):
         A, o, m = binding.spec_verify(t, d, tok, r, u, T, workspace=ws)
         g = None
     else:
-        A, o, m, g = binding.spec_cactus_verify(t, d, tok, r, u, delta, T, workspace=ws)
+        fn = binding.spec_cactus_kl_verify if kl else binding.spec_cactus_verify
+        A, o, m, g = fn(t, d, tok, r, u, delta, T, workspace=ws)
     torch.cuda.synchronize()
     assert binding.workspace_fault(ws) == 0, "kernel reported an internal consistency fault"
     # every word the call published was cleared by its last reader
@@ -45,10 +47,11 @@ def run_verify(binding, x, T=1.0, delta=None, ws=None):
     return to_np(A), to_np(o), to_np(m), to_np(g)
 
 
-def oracle_verify(x, T=1.0, delta=None):
+def oracle_verify(x, T=1.0, delta=None, kl=False):
     if delta is None:
         return oracle.spec_verify(x["target"], x["draft"], x["draft_tokens"], x["r"], x["u"], T)
-    return oracle.spec_cactus_verify(x["target"], x["draft"], x["draft_tokens"], x["r"], x["u"], delta, T)
+    return oracle.spec_cactus_verify(x["target"], x["draft"], x["draft_tokens"], x["r"], x["u"], delta, T,
+                                     exact_kl=kl)
 
 
 def sps_case(B_, K, V, seed=0, T=1.0, sigma_t=2.5, sigma_d=0.8, peak=0.01):
@@ -257,3 +260,62 @@ def test_cactus_full_qwen_vocab_sampled(B):
     ref = oracle_verify(sub, delta=1.0)
     print(compare_verify(ref, A[pick], o[pick], m[pick], "cactus full"))
     assert_rel(g[pick], ref["gamma_star"], label="gamma* full")
+
+
+# ---------------------------------------------------------------------------
+# Cactus with gamma* the exact root of the KL budget
+# ---------------------------------------------------------------------------
+
+def test_cactus_kl_delta0_bit_identical_to_sps(B):
+    banner("cactus-kl delta=0 == spec_verify")
+    x = sps_case(32, 6, 6000, seed=31, sigma_t=3.0, sigma_d=1.0, peak=0.0)
+    a = run_verify(B, x)
+    c = run_verify(B, x, delta=0.0, kl=True)
+    for u, v in zip(a[:3], c[:3]):
+        np.testing.assert_array_equal(u, v)
+
+
+@pytest.mark.parametrize("delta", [0.02, 0.5, 1.0, 3.0])
+def test_cactus_kl_parity(B, delta):
+    """delta = 3 clips gamma* to 1 wherever c >= e^-3, delta = 0.02 keeps it near c."""
+    banner(f"cactus-kl delta={delta} B=16 m=20 V=4000")
+    x = sps_case(16, 20, 4000, seed=33, sigma_t=3.0, sigma_d=1.0, peak=0.0)
+    A, o, m, g = run_verify(B, x, delta=delta, kl=True)
+    ref = oracle_verify(x, delta=delta, kl=True)
+    compare_verify(ref, A, o, m, f"cactus-kl {delta}")
+    valid = x["draft_tokens"] >= 0
+    assert_rel(g[valid], ref["gamma_star"][valid], label="gamma* kl")
+
+
+def test_cactus_kl_ragged_and_peaked(B):
+    """A ragged vocabulary over several slices, peaked rows (c near 1 and near 0)."""
+    banner("cactus-kl B=8 m=7 V=20001 peaked delta=0.3")
+    x = sps_case(8, 7, 20001, seed=35, sigma_t=2.5, sigma_d=0.8, peak=0.2)
+    A, o, m, g = run_verify(B, x, delta=0.3, kl=True)
+    ref = oracle_verify(x, delta=0.3, kl=True)
+    compare_verify(ref, A, o, m, "cactus-kl ragged")
+    assert_rel(g, ref["gamma_star"], label="gamma* kl ragged")
+
+
+def test_cactus_kl_not_below_taylor_where_corollary6_applies(B):
+    """Corollary 6: where the Taylor gamma* is <= 0.5 it keeps the budget, so the exact root is
+    at least as large there, position by position, on the same launch inputs."""
+    banner("cactus-kl >= taylor where taylor <= 0.5")
+    x = sps_case(16, 20, 4000, seed=37, sigma_t=3.0, sigma_d=1.0, peak=0.0)
+    _, _, _, gt = run_verify(B, x, delta=0.5)
+    _, _, _, gk = run_verify(B, x, delta=0.5, kl=True)
+    sel = gt <= 0.5
+    assert sel.sum() > 100
+    assert np.all(gk[sel] >= gt[sel] * (1 - 1e-6))
+
+
+def test_cactus_kl_full_qwen_vocab_sampled(B):
+    """Full launch B=64, m=20, V=151936 at delta=1.0; the oracle checks 8 sequences."""
+    banner("cactus-kl full B=64 m=20 V=151936 delta=1")
+    x = gen.make_sps_inputs(gen.QWEN_CACTUS)
+    A, o, m, g = run_verify(B, x, delta=1.0, kl=True)
+    pick = np.array([0, 7, 19, 28, 36, 44, 55, 62])
+    sub = {k: (v[pick] if isinstance(v, np.ndarray) else v) for k, v in x.items()}
+    ref = oracle_verify(sub, delta=1.0, kl=True)
+    print(compare_verify(ref, A[pick], o[pick], m[pick], "cactus-kl full"))
+    assert_rel(g[pick], ref["gamma_star"], label="gamma* kl full")

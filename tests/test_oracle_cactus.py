@@ -312,3 +312,49 @@ def test_planted_kl_mistake_is_caught(monkeypatch):
     c, g = 0.2, 0.45
     got = so.cactus_gamma_star_kl(c, _binary_kl_scipy(g, c))
     assert abs(got - g) > 1e-3
+
+
+def _kl_mp(g, c):
+    """The two-outcome divergence at 700 significant digits (enough for 1 - g with g ~ 1e-300)."""
+    import mpmath
+    with mpmath.workdps(700):
+        g, c = mpmath.mpf(g), mpmath.mpf(c)
+        t1 = g * mpmath.log(g / c) if g > 0 else mpmath.mpf(0)
+        t2 = (1 - g) * mpmath.log((1 - g) / (1 - c)) if g < 1 else mpmath.mpf(0)
+        return t1 + t2
+
+
+def _extreme_pairs(rng, n):
+    out = []
+    for _ in range(n):
+        c = float(10 ** rng.uniform(-300, 0)) * 0.9999
+        if rng.random() < 0.5:
+            g = c * (1.0 + float(10 ** rng.uniform(-12, 3)))   # g near c, or decades above it
+        else:
+            g = c + (1.0 - c) * float(rng.random())
+        out.append((min(g, 1.0), c))
+    return out
+
+
+def test_kl_divergence_matches_high_precision():
+    """cactus_kl against 700-digit arithmetic, from c = 1e-300 up, g from c (1 + 1e-12) to 1."""
+    rng = np.random.default_rng(15)
+    for g, c in _extreme_pairs(rng, 1500):
+        ref = float(_kl_mp(g, c))
+        if ref == 0.0:
+            continue
+        assert abs(so.cactus_kl(g, c) - ref) <= 1e-13 * ref, (g, c, so.cactus_kl(g, c), ref)
+
+
+def test_exact_kl_root_matches_high_precision():
+    """delta := the 700-digit divergence of a chosen g gives g back, to a few ulps (or to 1e-12
+    of g - c), from c = 1e-300 up."""
+    rng = np.random.default_rng(16)
+    for g, c in _extreme_pairs(rng, 300):
+        if not g < 1.0:
+            continue
+        delta = float(_kl_mp(g, c))
+        if delta == 0.0:
+            continue
+        got = oracle.cactus_gamma_star_kl(c, delta)
+        assert abs(got - g) <= 4 * np.spacing(g) + 1e-12 * (g - c), (g, c, delta, got)
