@@ -49,6 +49,9 @@ R15 Cactus acceptance phi(n) = min(1, h_n / pd(n)) and recovery
 R16 Cactus: c = 1 gives gamma* = 1 and s := 0; delta = 0 gives s = 1.0
     exactly, so h == pt bit for bit and the position is plain SpS.
 R17 Cactus bonus is drawn from pt at row m (h is defined per candidate only).
+R24 Draft-tree gamma ([NB] Key design 1, the tree case): a drafter's children
+    at a node are its topk tokens by logit, ties to the smaller id; gamma is
+    the target probability of that set.
 R23 Exact-KL Cactus: gamma* is the largest g in [c, 1] whose target h keeps
     KL(h || pt) <= delta ([CA] Key design 1's optimisation, Key design 2's
     root), 1 when even the one-hot target fits the budget (-log c <= delta),
@@ -80,6 +83,9 @@ __all__ = [
     "realised_ratio",
     "acceptance_length_estimate",
     "spec_counterfactual_gamma",
+    "tree_children",
+    "tree_gamma",
+    "spec_tree_gamma",
     "normalhedge_scale",
     "normalhedge_weights",
     "normalhedge_step",
@@ -451,6 +457,44 @@ def spec_counterfactual_gamma(target_bits, drafts_bits, traj_tokens, temperature
                     a[k] = realised_ratio(pt[k, x], pd[k, x])
             est[b, i] = acceptance_length_estimate(gamma[b, :, i], a)
     return {"gamma": gamma, "est_len": est, "loss": (K + 1.0) - est}
+
+
+# ---------------------------------------------------------------------------
+# HedgeSpec acceptance under a greedy draft tree
+# ---------------------------------------------------------------------------
+
+def tree_children(z_draft, topk: int) -> np.ndarray:
+    """Children a drafter keeps at a tree node: its topk most likely tokens.
+
+    [NB] Key design 1 (the draft-tree case, its Theorem 2) names the children
+    that the drafter builds or prunes at the node; reading R24 takes them as the
+    drafter's topk tokens by logit (its softmax keeps the order at any
+    temperature), ties to the smaller token id.  Token ids, best first.
+    """
+    z = np.asarray(z_draft, dtype=np.float64)
+    order = np.lexsort((np.arange(z.shape[0]), -z))   # logit descending, then id ascending
+    return order[:min(int(topk), z.shape[0])]
+
+
+def tree_gamma(pt, z_draft, topk: int) -> float:
+    """Acceptance probability at a greedy draft-tree node ([NB] Key design 1, its
+    Theorem 2 case): the target's total probability on the node's children."""
+    pt = np.asarray(pt, dtype=np.float64)
+    return float(np.sum(pt[tree_children(z_draft, topk)]))
+
+
+def spec_tree_gamma(target_bits, drafts_bits, topk: int, temperature=1.0):
+    """gamma[b, k, i] = tree_gamma(pt_{b,k}, drafter i's logits at (b, k), topk).
+
+    target_bits [B, >=K, V], drafts_bits [N, B, K, V] (bf16 bits)."""
+    N, B, K, V = np.shape(drafts_bits)
+    gamma = np.zeros((B, K, N))
+    for b in range(B):
+        for k in range(K):
+            pt = softmax_t(widen_bf16(target_bits[b, k]), temperature)
+            for i in range(N):
+                gamma[b, k, i] = tree_gamma(pt, widen_bf16(drafts_bits[i, b, k]), topk)
+    return gamma
 
 
 # ---------------------------------------------------------------------------
