@@ -45,6 +45,8 @@ GAMMA_WORKLOADS = ("hedge_eval", "pool21", "small_mixed")
 
 def kernel_of(key: str) -> str:
     """The library's kernel that a workload's step launches."""
+    if key.endswith("_tree"):
+        return "tree_kernel"
     return "gamma_kernel" if key in GAMMA_WORKLOADS else "verify_kernel"
 
 
@@ -205,6 +207,47 @@ class GammaLike(Workload):
         return done * K, time.perf_counter() - t0, time.process_time() - c0, f"{done} sequences of this batch, one at a time"
 
 
+class TreeLike(GammaLike):
+    """spec_tree_gamma over one GammaWorkload's target and drafter rows (topk children)."""
+
+    def __init__(self, key, w, topk):
+        super().__init__(key, w)
+        B, K, N, V = w.B, w.K, w.N, w.V
+        self.topk = topk
+        self.desc = f"{w.name}, draft-tree gamma with {topk} children per node"
+        self.algo_bytes = 2 * V * (B * K + N * B * K) + B * K * N * 4
+
+    def setup(self, copies_min_bytes):
+        import torch
+        from speculative_sampling_verification_row_amd import binding
+        from speculative_sampling_verification_row_amd import inputs as gen
+        self.torch, self.binding = torch, binding
+        log(f"generating inputs: {self.desc}")
+        self.x = gen.make_gamma_inputs(self.w)
+        K = self.w.K
+        t = _dev(torch, self.x["target"][:, :K])
+        d = _dev(torch, self.x["drafts"])
+        per = 2 * (t.numel() + d.numel())
+        n = max(1, -(-copies_min_bytes // per))
+        self.copies = [(t, d)] + [(t.clone(), d.clone()) for _ in range(n - 1)]
+        self.ws = binding.make_tree_workspace(self.w.B, K, self.w.N, self.w.V, self.topk)
+        self.calls = [binding.prepare_tree_gamma(t, d, self.topk, self.w.temperature, workspace=self.ws)
+                      for t, d in self.copies]
+        log(f"{len(self.copies)} input copies of {per / 1e6:.1f} MB")
+
+    def cpu_sample(self, budget_s):
+        import oracle
+        x, B, K = self.x, self.w.B, self.w.K
+        done, t0, c0 = 0, time.perf_counter(), time.process_time()
+        while True:
+            b = done % B
+            oracle.spec_tree_gamma(x["target"][b:b + 1, :K], x["drafts"][:, b:b + 1], self.topk)
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        return done * K, time.perf_counter() - t0, time.process_time() - c0, f"{done} sequences of this batch, one at a time"
+
+
 def workloads():
     from speculative_sampling_verification_row_amd import inputs as gen
     return {
@@ -216,6 +259,8 @@ def workloads():
         "hedge_eval": lambda: GammaLike("hedge_eval", gen.HEDGE_EVAL),
         "pool21": lambda: GammaLike("pool21", gen.POOL21),
         "small_mixed": lambda: GammaLike("small_mixed", gen.SMALL_MIXED),
+        "hedge_eval_tree": lambda: TreeLike("hedge_eval_tree", gen.HEDGE_EVAL, topk=8),
+        "pool21_tree": lambda: TreeLike("pool21_tree", gen.POOL21, topk=8),
     }
 
 

@@ -218,6 +218,36 @@ int spec_counterfactual_gamma(const spec_bf16* target, int64_t target_row_stride
                               void* workspace, size_t workspace_bytes, spec_stream_t stream);
 
 /*
+ * spec_tree_gamma -- HedgeSpec acceptance probabilities under a greedy draft tree.
+ *
+ * [NB] Key design 1, the draft-tree case (its Theorem 2): at the node of
+ * position k the acceptance probability of drafter i is the total target
+ * probability of the children drafter i keeps there.  Here the children are the
+ * drafter's topk most likely tokens (the topk largest logits of its row k, ties
+ * to the smaller token id; its softmax keeps that order at any temperature):
+ *   gamma[b][k][i] = sum over those tokens x of pt_k(x),
+ * with pt_k = softmax(target row k / temperature) of sequence b.
+ *
+ * target  [B][target_rows_per_seq][V] bf16 (rows 0..K-1 are read), row stride
+ *         target_row_stride elements; drafts [N][B][K][V] bf16, row stride
+ *         draft_row_stride, drafter stride drafter_stride elements (as
+ *         spec_counterfactual_gamma);  gamma [B][K][N] float32 out.
+ * Limits: 1 <= N <= SPEC_MAX_N, 1 <= topk <= 64 (SPEC_ERR_PARAM otherwise; a
+ * topk of V or more keeps every token, gamma = 1), target_rows_per_seq >= K.
+ * Workspace: spec_tree_workspace_bytes(B, K, N, V, topk) bytes (a workspace
+ * sized for V serves every smaller V), zeroed once (spec_workspace_init); every
+ * call leaves it zero.  Other conventions
+ * (alignment, strides, status codes, asynchrony) as spec_verify.
+ */
+int spec_tree_gamma(const spec_bf16* target, int64_t target_row_stride, int target_rows_per_seq,
+                    const spec_bf16* drafts, int64_t draft_row_stride, int64_t drafter_stride,
+                    int B, int K, int N, int V, int topk, float temperature,
+                    float* gamma, void* workspace, size_t workspace_bytes, spec_stream_t stream);
+
+/* Workspace bytes of spec_tree_gamma for vocabularies up to V; 0 for sizes out of range. */
+size_t spec_tree_workspace_bytes(int B, int K, int N, int V, int topk);
+
+/*
  * hedge_update -- one NormalHedge round per sequence ([NH]; named by [NB] Key
  * design 3 as the full-information learner; one learner per sequence).
  *

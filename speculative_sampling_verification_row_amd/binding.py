@@ -42,6 +42,8 @@ _SIGNATURES = {
     "spec_verify": (_I, [_P, _I64, _P, _I64, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P]),
     "spec_cactus_verify": (_I, [_P, _I64, _P, _I64, _P, _P, _P, _I, _I, _I, _F, _F, _P, _P, _P, _P, _P, _SZ, _P]),
     "spec_cactus_kl_verify": (_I, [_P, _I64, _P, _I64, _P, _P, _P, _I, _I, _I, _F, _F, _P, _P, _P, _P, _P, _SZ, _P]),
+    "spec_tree_gamma": (_I, [_P, _I64, _I, _P, _I64, _I64, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P]),
+    "spec_tree_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "spec_counterfactual_gamma": (_I, [_P, _I64, _I, _P, _I64, _I64, _P, _I, _I, _I, _I, _F, _P, _P, _P,
                                        _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "hedge_update": (_I, [_P, _P, _P, _P, _F, _P, _P, _I, _I, _P]),
@@ -226,6 +228,39 @@ def _prepare_verify(name, target, draft, tokens, r, u, delta, temperature, works
     args = (_ptr(t), ts, _ptr(d), ds, _ptr(tokens), _ptr(r), _ptr(u), B, K, V, float(delta), float(temperature),
             _ptr(A), _ptr(tok), _ptr(mask), _ptr(gstar), _ptr(ws), ws.numel())
     return Launcher(name, args, (A, tok, mask, gstar), keep + (gstar,))
+
+
+def tree_workspace_bytes(B: int, K: int, N: int, V: int, topk: int) -> int:
+    return int(load().spec_tree_workspace_bytes(B, K, N, V, topk))
+
+
+def make_tree_workspace(B: int, K: int, N: int, V: int, topk: int, device="cuda") -> torch.Tensor:
+    """A zeroed spec_tree_gamma workspace for vocabularies up to V; every completed call
+    leaves it zero again."""
+    return torch.zeros(tree_workspace_bytes(B, K, N, V, topk), dtype=torch.uint8, device=device)
+
+
+def spec_tree_gamma(target, drafts, topk: int, temperature: float = 1.0, *, workspace=None, stream=None):
+    """Draft-tree acceptance probabilities.  target [B, R >= K, V], drafts [N, B, K, V] bf16.
+    Returns gamma [B, K, N] float32."""
+    return prepare_tree_gamma(target, drafts, topk, temperature, workspace=workspace).launch(stream)[0]
+
+
+def prepare_tree_gamma(target, drafts, topk: int, temperature: float = 1.0, *, workspace=None) -> Launcher:
+    """spec_tree_gamma with its tensors fixed (see Launcher)."""
+    _need_cuda(target, drafts)
+    N, B, K, V = drafts.shape
+    if target.shape[0] != B or target.shape[2] != V or target.shape[1] < K:
+        raise ValueError("target must be [B, R >= K, V]")
+    R = target.shape[1]
+    t, ts = as_rows(target)
+    d, ds = as_rows(drafts)
+    dstr = ds * B * K
+    gamma = torch.empty((B, K, N), dtype=torch.float32, device=target.device)
+    ws = make_tree_workspace(B, K, N, V, topk, target.device) if workspace is None else workspace
+    args = (_ptr(t), ts, R, _ptr(d), ds, dstr, B, K, N, V, int(topk), float(temperature), _ptr(gamma), _ptr(ws),
+            ws.numel())
+    return Launcher("spec_tree_gamma", args, (gamma,), (t, d, gamma, ws))
 
 
 def spec_counterfactual_gamma(target, drafts, traj_tokens, temperature: float = 1.0, *, sel=None,

@@ -54,7 +54,7 @@
 namespace specv {
 
 enum : uint32_t { ST_ACCEPT = 1, ST_REJECT = 2, ST_INVALID = 3 };
-enum : int { MODE_VERIFY = 0, MODE_GAMMA = 1 };
+enum : int { MODE_VERIFY = 0, MODE_GAMMA = 1, MODE_TREE = 2 };
 // Sampling-weight modes of the draw passes.
 enum : int { W_RESID = 0, W_TARGET_H = 1, W_TARGET = 2 };
 
@@ -114,6 +114,7 @@ struct Params {
   int ngroups; // gamma groups (B * K): a position's target row and its N drafter rows
   int ncu;     // compute units; workgroup g sits in dispatch slot g / ncu
   int slots;   // workgroups per compute unit in this launch (1: no weighting)
+  int topk;    // draft-tree calls: children per node (1..kMaxTopk)
   // outputs
   int32_t* accepted_len;
   int32_t* out_token;
@@ -128,6 +129,7 @@ struct Params {
   unsigned long long* part;   // [B][R][S][kWaves] statistics words
   unsigned long long* tot;    // [B][kMaxSlices][kMaxSlices] draw slice totals, [reader][writer] (fp64 | kValid)
   unsigned long long* gpart;  // [B][K][N][S][kWaves] gamma partial sums (fp64 | kValid)
+  unsigned long long* cand;   // draft-tree calls: [B][K][N][pieces][topk] piece records
 };
 
 __device__ __forceinline__ const uint4* as_chunks(const uint16_t* row) { return reinterpret_cast<const uint4*>(row); }
@@ -152,6 +154,7 @@ __device__ __forceinline__ unsigned long long* part_row(const Params& p, int b, 
 // target 1, draft 1, ..., then the bonus target row K.  Gamma calls: position by
 // position, target row k then every drafter's row k; the fused bonus row last.
 __device__ __forceinline__ int order_row(const Params& p, int i) {
+  if (p.mode == MODE_TREE) return i;  // draft-tree calls: target rows 0..K-1 only
   if (p.mode == MODE_VERIFY) {
     if (i >= 2 * p.K) return p.K;
     const int k = i >> 1;
@@ -1516,6 +1519,436 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 }
 
 // ---------------------------------------------------------------------------
+// Draft-tree gamma ([NB] Key design 1, the greedy draft-tree case)
+// ---------------------------------------------------------------------------
+//
+// gamma[b][k][i] = sum of pt_k over the topk tokens of drafter i's row k (logit
+// descending, ties to the smaller id): the target's probability of landing on one
+// of the children drafter i keeps at the node.  Phase 0 streams the target rows
+// 0..K-1 for their statistics (static_phase).  A piece unit -- one wave, a piece
+// of kPieceTok tokens of drafter i's row k -- streams the piece once and
+// publishes its topk best tokens, with wave operations only (no workgroup
+// barrier, so the four waves of a workgroup stream independently, the next
+// piece's loads in flight while one is ranked).  A merge unit (b, k, i) takes the
+// row's topk from its pieces' records, gathers their target logits and sums pt.
+// Piece units wait for nothing, merge units only for piece units and phase 0,
+// and every workgroup runs its piece units before its merge units, so every
+// wait ends.
+//
+// A token is ranked by one 32-bit key inside a piece, (order-preserving key of
+// its bf16 logit) << 16 | (0xffff - its offset in the piece), and by one 64-bit
+// record across pieces, key << 32 | (0xffffffff - token id): larger is better,
+// and ties of the logit go to the smaller id.  Records are never zero, so each
+// one is its own "published" flag, and a piece's record count, min(topk, tokens
+// of the piece inside the row), is known to its reader.
+
+constexpr int kMaxTopk = 64;
+constexpr int kPieceTok = 64 * kVec * kTilesPerSlice;   // 4096 tokens: 8 loads of 16 bytes per lane
+constexpr int kPieceChunks = kPieceTok / kVec;
+constexpr int kMaxPieces = kMaxV / kPieceTok;
+constexpr int kWaveCand = 512;                          // a piece's candidates held in LDS
+
+struct TreeLds {
+  MergeLds m;
+  uint32_t cand[kWaves][kWaveCand + 4];  // (+4: zeros after the last, for 16-byte reads)
+  uint32_t ranked[kWaves][kMaxTopk];     // a piece's best keys in rank order
+  float lmax[kWaves][64];                // the lanes' best logits
+  int ncand[kWaves];
+  unsigned long long rec[kMaxTopk * kMaxSlices];
+  uint32_t tau[2 * kWaves];
+  double red[kWaves];
+  int nrec;
+};
+
+// Order-preserving 16-bit key of a bf16 logit; -0 counts as +0.
+__device__ __forceinline__ uint32_t bf16_key(uint32_t b) {
+  b = b == 0x8000u ? 0u : b;
+  return (b & 0x8000u) ? (~b & 0xffffu) : (b | 0x8000u);
+}
+
+// Piece keys of one chunk: token offset off0 + e in the piece, `valid` of its 8
+// tokens inside the row (the rest key 0, below every token).
+__device__ __forceinline__ void chunk_keys(const uint4 w, int off0, int valid, uint32_t k[8]) {
+  const uint32_t h[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t b = (h[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+    k[e] = e < valid ? (bf16_key(b) << 16) | (0xffffu - static_cast<uint32_t>(off0 + e)) : 0u;
+  }
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o)));
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// LDS written by some lanes of this wave is then read by others: the writes
+// complete first.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// The piece's keys at or above `tau` (nonzero), counted over the wave.
+__device__ __forceinline__ int wave_count_at_least(const uint4 v[kTilesPerSlice], int base, int V, uint32_t tau) {
+  int c = 0;
+#pragma unroll
+  for (int t = 0; t < kTilesPerSlice; ++t) {
+    const int off0 = (t * 64 + lane_id()) * kVec;
+    uint32_t k[8];
+    chunk_keys(v[t], off0, min(max(V - (base + off0), 0), kVec), k);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c += (k[e] != 0u && k[e] >= tau) ? 1 : 0;
+  }
+  return wave_sum_i(c);
+}
+
+// Piece x of row (b K + k) N + i: loads of its 4096 tokens (lane l, load t:
+// tokens (64 t + l) 8 .. + 8 of the piece).  A row past the last (none) reads a
+// buffer of no bytes (zero, without touching memory).
+__device__ __forceinline__ void piece_load(const Params& p, int row, int x, bool none, uint4 v[kTilesPerSlice]) {
+  const int i = row % p.N, bk = row / p.N, k = bk % p.K, b = bk / p.K;
+  const uint32_t row_bytes = none ? 0u : static_cast<uint32_t>((p.V + kVec - 1) / kVec) * 16u;
+  const __amdgpu_buffer_rsrc_t dr = row_buffer(draft_row(p, none ? 0 : b, none ? 0 : i, none ? 0 : k), row_bytes);
+#pragma unroll
+  for (int t = 0; t < kTilesPerSlice; ++t)
+    v[t] = buffer_load16(dr, lane_id() * 16u, static_cast<uint32_t>(x * kPieceChunks + t * 64) * 16u);
+}
+
+// A piece's records, one per lane (lane r: the record of rank r), stored after the
+// next piece's loads are issued: loads and stores retire in order, so a store
+// issued before them would make the wait for the next piece also wait for it.
+// A lane without a record stores past the end of its buffer, which drops it, so
+// the store is one unconditional instruction that the waits can count.
+struct PieceRecords {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t off;
+  unsigned long long val;
+};
+constexpr int kStoreAgent = 16;  // sc1: written through to where other compute units read it
+
+__device__ __forceinline__ PieceRecords no_records(const Params& p) {
+  return PieceRecords{row_buffer(p.cand, 0u), 0u, 0ull};
+}
+__device__ __forceinline__ void store_records(const PieceRecords& r) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 d = {static_cast<uint32_t>(r.val), static_cast<uint32_t>(r.val >> 32)};
+  __builtin_amdgcn_raw_buffer_store_b64(d, r.rs, r.off, 0, kStoreAgent);
+}
+
+// Piece unit u (one wave): the topk best tokens of the piece (logits in v), as
+// records in rank order (returned, to be stored by the caller).  Candidates are
+// the tokens whose logit reaches the topk-th best lane maximum (topk lanes, so
+// topk tokens, at or above it; lanes with no token inside the row count as -inf,
+// which only lowers it).  Their exact 32-bit keys (ties to the smaller id) then
+// rank them.  Ranks are counted against values read back from LDS (16-byte
+// broadcast reads), not lane by lane.  FULL: every token of the piece lies inside
+// the row (all pieces but a row's last, unless V is a multiple of the piece).
+template <bool FULL>
+__device__ __forceinline__ PieceRecords piece_unit(const Params& p, int row, int x, const uint4 (&v)[kTilesPerSlice],
+                                                  TreeLds& L) {
+  const int V = p.V, kk = p.topk;
+  const int P = (V + kPieceTok - 1) / kPieceTok;
+  const int w = wave_id(), lane = lane_id();
+  const int base = x * kPieceTok;
+  uint32_t* cand = L.cand[w];
+  auto valid_of = [&](int off0) { return FULL ? kVec : min(max(V - (base + off0), 0), kVec); };
+  // the lane's best logit
+  float m = -__builtin_inff();
+#pragma unroll
+  for (int t = 0; t < kTilesPerSlice; ++t) {
+    float z[8];
+    unpack8(v[t], z, valid_of((t * 64 + lane) * kVec));
+    m = max3f(max3f(z[0], z[1], z[2]), max3f(z[3], z[4], z[5]), max3f(z[6], z[7], m));
+  }
+  L.lmax[w][lane] = m;
+  if (lane == 0) L.ncand[w] = 0;
+  wave_lds_sync();
+  int rank = 0;  // lanes with a larger maximum
+#pragma unroll
+  for (int j = 0; j < 64; j += 4) {
+    const float4 o = *reinterpret_cast<const float4*>(&L.lmax[w][j]);
+    rank += (o.x > m ? 1 : 0) + (o.y > m ? 1 : 0) + (o.z > m ? 1 : 0) + (o.w > m ? 1 : 0);
+  }
+  const float tau = -wave_max(rank < kk ? -m : -__builtin_inff());
+  // candidates (logit >= tau, inside the row) to LDS, with their exact keys; a
+  // load without any in the wave (nearly all of them) costs one ballot
+#pragma unroll
+  for (int t = 0; t < kTilesPerSlice; ++t) {
+    const int off0 = (t * 64 + lane) * kVec;
+    const int valid = valid_of(off0);
+    float z[8];
+    unpack8(v[t], z, 8);
+    uint32_t hit = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) hit |= ((FULL || e < valid) && z[e] >= tau) ? (1u << e) : 0u;
+    if (__builtin_amdgcn_ballot_w64(hit != 0u) == 0ull) continue;
+    const uint4 wv = v[t];
+    while (hit != 0u) {
+      const int e = __builtin_ctz(hit);
+      hit &= hit - 1u;
+      // element e's bf16 bits by selects (an index into z would put z in scratch)
+      const uint32_t word = e < 4 ? (e < 2 ? wv.x : wv.y) : (e < 6 ? wv.z : wv.w);
+      const uint32_t bits = (e & 1) ? (word >> 16) : (word & 0xffffu);
+      const int q = atomicAdd(&L.ncand[w], 1);
+      if (q < kWaveCand) cand[q] = (bf16_key(bits) << 16) | (0xffffu - static_cast<uint32_t>(off0 + e));
+    }
+  }
+  wave_lds_sync();
+  int C = L.ncand[w];
+  if (C > kWaveCand) {
+    // rare: the exact topk-th best key by bisection (C > kWaveCand >= topk keys reach
+    // tau), then its candidates again
+    uint32_t lo = 0u, hi = 0xffffffffu;
+    while (lo < hi) {
+      const uint32_t mid = static_cast<uint32_t>((static_cast<uint64_t>(lo) + hi + 1u) / 2u);  // in (lo, hi]
+      if (wave_count_at_least(v, base, V, mid) >= kk)
+        lo = mid;
+      else
+        hi = mid - 1u;
+    }
+    if (lane == 0) L.ncand[w] = 0;
+    wave_lds_sync();
+#pragma unroll
+    for (int t = 0; t < kTilesPerSlice; ++t) {
+      const int off0 = (t * 64 + lane) * kVec;
+      uint32_t kv[8];
+      chunk_keys(v[t], off0, valid_of(off0), kv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (kv[e] != 0u && kv[e] >= lo) cand[atomicAdd(&L.ncand[w], 1)] = kv[e];  // exactly topk of them
+    }
+    wave_lds_sync();
+    C = L.ncand[w];
+  }
+  if (lane < 4) cand[C + lane] = 0u;  // below every key
+  wave_lds_sync();
+  // rank of each candidate among them; the topk best go to `ranked` in rank order
+  for (int q0 = 0; q0 < C; q0 += 64) {
+    const int q = q0 + lane;
+    const uint32_t me = q < C ? cand[q] : 0u;
+    int r = 0;
+    for (int j = 0; j < C; j += 4) {
+      const uint4 o = *reinterpret_cast<const uint4*>(cand + j);
+      r += (o.x > me ? 1 : 0) + (o.y > me ? 1 : 0) + (o.z > me ? 1 : 0) + (o.w > me ? 1 : 0);
+    }
+    if (q < C && r < kk) L.ranked[w][r] = me;
+  }
+  wave_lds_sync();
+  // lane r: the record of rank r
+  const int nrec = min(kk, C);
+  const uint32_t me = lane < nrec ? L.ranked[w][lane] : 0u;
+  const uint32_t tok = static_cast<uint32_t>(base) + (0xffffu - (me & 0xffffu));
+  PieceRecords rec;
+  rec.rs = row_buffer(p.cand + (static_cast<size_t>(row) * P + x) * static_cast<size_t>(kk), static_cast<uint32_t>(kk) * 8u);
+  rec.off = static_cast<uint32_t>(lane < nrec ? lane : kk) * 8u;
+  rec.val = (static_cast<unsigned long long>(me >> 16) << 32) | (0xffffffffu - tok);
+  return rec;
+}
+
+// Records a piece publishes: min(topk, its tokens inside the row).
+__device__ __forceinline__ int piece_records(const Params& p, int x) {
+  return min(p.topk, min(kPieceTok, p.V - x * kPieceTok));
+}
+
+// Merge unit v = (b K + k) N + i.
+__device__ __forceinline__ void tree_merge(const Params& p, int v, TreeLds& L) {
+  const int S = p.S, K = p.K, N = p.N, kk = p.topk;
+  const int P = (p.V + kPieceTok - 1) / kPieceTok;
+  const int i = v % N, bk = v / N, k = bk % K, b = bk / K;
+  const int tid = threadIdx.x;
+  unsigned long long* recs = p.cand + static_cast<size_t>(v) * P * static_cast<size_t>(kk);
+  // the target row's statistics (phase 0)
+  merge_rows(p, b, 1, [&](int) { return k; }, L.m);
+  // a bound at or below the row's kk-th best record: the best kk-th record of the
+  // pieces with kk records
+  uint32_t tlo = 0u, thi = 0u;
+  for (int x = tid; x < P; x += kThreads) {
+    if (piece_records(p, x) != kk) continue;
+    const unsigned long long w = poll_word(p.flags, recs + static_cast<size_t>(x) * kk + (kk - 1));
+    const uint32_t h = static_cast<uint32_t>(w >> 32), l = static_cast<uint32_t>(w);
+    if (h > thi || (h == thi && l > tlo)) {
+      thi = h;
+      tlo = l;
+    }
+  }
+  // 64-bit maximum over the block, as (high, low) words
+  unsigned long long tw = (static_cast<unsigned long long>(thi) << 32) | tlo;
+  {
+    uint32_t h = wave_max_u32(thi);
+    uint32_t l = wave_max_u32(thi == h ? tlo : 0u);
+    if (lane_id() == 0) {
+      L.tau[wave_id()] = h;
+      L.tau[kWaves + wave_id()] = l;
+    }
+    if (tid == 0) L.nrec = 0;
+    __syncthreads();
+    tw = 0ull;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      tw = max(tw, (static_cast<unsigned long long>(L.tau[w]) << 32) | L.tau[kWaves + w]);
+  }
+  // the records at or above the bound, to LDS (every expected record is read)
+  constexpr int kRecCap = kMaxTopk * kMaxSlices;
+  auto gather = [&](unsigned long long bound) {
+    for (int q = tid; q < P * kk; q += kThreads) {
+      const int x = q / kk, j = q - x * kk;
+      if (j >= piece_records(p, x)) continue;
+      const unsigned long long w = poll_word(p.flags, recs + static_cast<size_t>(x) * kk + j);
+      if (w >= bound && w != 0ull) {
+        const int c = atomicAdd(&L.nrec, 1);
+        if (c < kRecCap) L.rec[c] = w;
+      }
+    }
+    __syncthreads();
+  };
+  gather(tw);
+  if (L.nrec > kRecCap) {
+    // rare: pieces other than the bound's may each hold up to kk - 1 records above
+    // it.  The kk-th best of the pieces' best records is a bound too, and only the
+    // kk pieces whose best reaches it hold records at or above it: kk^2 <= kRecCap.
+    __syncthreads();
+    for (int x = tid; x < P; x += kThreads) L.rec[x] = poll_word(p.flags, recs + static_cast<size_t>(x) * kk);
+    if (tid == 0) L.nrec = 0;
+    __syncthreads();
+    unsigned long long t2 = 0ull;
+    for (int x0 = wave_id() * 64; x0 < P; x0 += kThreads) {
+      const int x = x0 + lane_id();
+      const unsigned long long me = x < P ? L.rec[x] : 0ull;
+      int r = 0;
+      for (int c0 = 0; c0 < P; c0 += 64) {
+        const unsigned long long o = c0 + lane_id() < P ? L.rec[c0 + lane_id()] : 0ull;
+        const uint32_t ohi = static_cast<uint32_t>(o >> 32), olo = static_cast<uint32_t>(o);
+#pragma unroll
+        for (int j = 0; j < 64; ++j)
+          r += ((static_cast<unsigned long long>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ohi), j))) << 32) |
+                static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(olo), j))) > me ? 1 : 0;
+      }
+      if (x < P && r == kk - 1) t2 = me;
+    }
+    // the one piece best of rank kk - 1, to every thread
+    const uint32_t h = wave_max_u32(static_cast<uint32_t>(t2 >> 32));
+    const uint32_t l = wave_max_u32(static_cast<uint32_t>(t2 >> 32) == h ? static_cast<uint32_t>(t2) : 0u);
+    if (lane_id() == 0) {
+      L.tau[wave_id()] = h;
+      L.tau[kWaves + wave_id()] = l;
+    }
+    __syncthreads();
+    unsigned long long b2 = 0ull;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) b2 = max(b2, (static_cast<unsigned long long>(L.tau[w]) << 32) | L.tau[kWaves + w]);
+    __syncthreads();
+    gather(max(tw, b2));
+  }
+  const int C = min(L.nrec, kRecCap);
+  if (tid == 0 && L.nrec > C) st_agent(&p.flags[3], 1u);  // cannot happen: a fault word, never an overrun
+  const RowStats st{L.m.rk[0], L.m.rs[0]};
+  const uint16_t* trow = target_row(p, b, k);
+  double s = 0.0;
+  for (int q0 = wave_id() * 64; q0 < C; q0 += kThreads) {
+    const int q = q0 + lane_id();
+    const unsigned long long me = q < C ? L.rec[q] : 0ull;
+    int r = 0;
+    for (int c0 = 0; c0 < C; c0 += 64) {
+      const unsigned long long other = c0 + lane_id() < C ? L.rec[c0 + lane_id()] : 0ull;  // 0: below every record
+      const uint32_t ohi = static_cast<uint32_t>(other >> 32), olo = static_cast<uint32_t>(other);
+#pragma unroll
+      for (int j = 0; j < 64; ++j) {
+        const unsigned long long o =
+            (static_cast<unsigned long long>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ohi), j))) << 32) |
+            static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(olo), j));
+        r += o > me ? 1 : 0;
+      }
+    }
+    if (q < C && r < kk) {
+      const uint32_t tok = 0xffffffffu - static_cast<uint32_t>(me);
+      if (tok < static_cast<uint32_t>(p.V))
+        s += token_prob(bf16_at(trow, static_cast<int>(tok)), p.c, st);
+      else
+        st_agent(&p.flags[3], 1u);  // not a record of this call: the fault word, never an index
+    }
+  }
+  s = wave_sum(s);
+  if (lane_id() == 0) L.red[wave_id()] = s;
+  __syncthreads();
+  if (tid == 0) {
+    double g = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) g += L.red[w];
+    p.gamma[v] = static_cast<float>(g);
+  }
+  // every record of the row back to zero
+  for (int q = tid; q < P * kk; q += kThreads) {
+    const int x = q / kk, j = q - x * kk;
+    if (j < piece_records(p, x)) st_agent_u64(recs + static_cast<size_t>(x) * kk + j, 0ull);
+  }
+  // the last of the row's N merge units clears its statistics words
+  stores_complete();
+  __syncthreads();
+  if (tid == 0) {
+    const int last = ticket(&p.done[bk]) == static_cast<uint32_t>(N - 1) ? 1 : 0;
+    if (last) st_agent(&p.done[bk], 0u);
+    L.nrec = last;
+  }
+  __syncthreads();
+  if (L.nrec) {
+    unsigned long long* w = part_row(p, b, k);
+    for (int q = tid; q < S * kWaves; q += kThreads) st_agent_u64(w + q, 0ull);
+  }
+}
+
+// Draft-tree calls (spec_tree_gamma): phase 0 over the target rows, then the piece
+// units (one per wave at a time), then the merge units g, g + G, ...
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void tree_kernel(Params p) {
+  __shared__ TreeLds L;
+  const int G = gridDim.x, g = blockIdx.x;
+  static_phase(p, G, g);
+  // whole-piece units of wave w: u = g kWaves + w, + G kWaves, ... (row u / Pw,
+  // piece u % Pw); the next unit's loads are in flight while one is ranked
+  const int rows = p.B * p.K * p.N;
+  const int Pw = p.V / kPieceTok;  // whole pieces per row
+  const int T1 = rows * Pw, GW = G * kWaves;
+  uint4 va[kTilesPerSlice], vb[kTilesPerSlice];
+  int u = g * kWaves + wave_id();
+  PieceRecords rec = no_records(p);
+  auto load_unit = [&](int uu, uint4 (&v)[kTilesPerSlice]) {
+    const bool none = uu >= T1;
+    piece_load(p, none ? 0 : uu / Pw, none ? 0 : uu % Pw, none, v);
+  };
+  load_unit(u, va);
+  while (u < T1) {
+    load_unit(u + GW, vb);
+    store_records(rec);
+    rec = piece_unit<true>(p, u / Pw, u % Pw, va, L);
+    u += GW;
+    if (u >= T1) break;
+    load_unit(u + GW, va);
+    store_records(rec);
+    rec = piece_unit<true>(p, u / Pw, u % Pw, vb, L);
+    u += GW;
+  }
+  store_records(rec);
+  // a row's last piece when V is not a multiple of the piece: one per row
+  if (Pw * kPieceTok < p.V) {
+    for (int r = g * kWaves + wave_id(); r < rows; r += GW) {
+      piece_load(p, r, Pw, false, va);
+      store_records(piece_unit<false>(p, r, Pw, va, L));
+    }
+  }
+  const int T2 = p.B * p.K * p.N;
+  for (int v = g; v < T2; v += G) {
+    __syncthreads();
+    tree_merge(p, v, L);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // NormalHedge ([NH]); one wave per sequence, lane i = drafter i.
 // ---------------------------------------------------------------------------
 constexpr int kHedgeBisect = 64;
@@ -1591,6 +2024,7 @@ __global__ void fill_zero_kernel(uint32_t* p, size_t n) {
 
 struct Shape {
   int B, K, N, V, mode, fused;
+  int topk;  // draft-tree calls
   int R, RT, S, nsub, P1, P2, nlast;
   int64_t RS, total0, ngroups;  // checked below 2^31 before a launch
 };
@@ -1603,24 +2037,34 @@ static Shape make_shape(int B, int K, int N, int V, int mode, int fused) {
   s.V = V;
   s.mode = mode;
   s.fused = fused;
+  s.topk = 0;
   s.RT = mode == MODE_VERIFY ? K + 1 : K + fused;
   s.R = s.RT + N * K;
+  if (mode == MODE_TREE) s.R = s.RT = K;  // the statistics list holds the target rows only
   s.S = (V + kSliceTok - 1) / kSliceTok;
   s.nsub = (V + kSub - 1) / kSub;
   s.P1 = mode == MODE_VERIFY || fused ? s.S : 0;
   s.P2 = mode == MODE_VERIFY ? 0 : 1;
   s.nlast = mode == MODE_VERIFY ? 0 : s.P1 + s.P2;
+  if (mode == MODE_TREE) {
+    s.P1 = s.P2 = 0;
+    s.nlast = N;  // merge units per target row (tickets per row)
+  }
   s.RS = static_cast<int64_t>(s.R) * s.S;
   // gamma calls: the groups take the rows of positions 0..K-1; the list holds the bonus rows
   s.total0 = mode == MODE_VERIFY ? static_cast<int64_t>(B) * s.RS : (fused ? static_cast<int64_t>(B) * s.S : 0);
   s.ngroups = mode == MODE_VERIFY ? 0 : static_cast<int64_t>(B) * K;
+  if (mode == MODE_TREE) {
+    s.total0 = static_cast<int64_t>(B) * s.RS;
+    s.ngroups = 0;
+  }
   return s;
 }
 
 // Byte offsets of the workspace regions.  They depend on (B, K, N, mode) only
 // (every region is sized for the longest row), so one workspace serves every V.
 struct WsLayout {
-  size_t flags, done, part, tot, gpart, total;
+  size_t flags, done, part, tot, gpart, cand, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -1632,13 +2076,16 @@ static WsLayout ws_layout(const Shape& s) {
   L.flags = o;
   o = align256(o + 16);
   L.done = o;
-  o = align256(o + 4 * B);
+  o = align256(o + 4 * B * (s.mode == MODE_TREE ? static_cast<size_t>(s.K) : 1));  // tree: a ticket per target row
   L.part = o;
   o = align256(o + 8 * B * static_cast<size_t>(s.R) * kMaxSlices * kWaves);
   L.tot = o;
   o = align256(o + 8 * B * static_cast<size_t>(kMaxSlices) * kMaxSlices);
   L.gpart = o;
   o = align256(o + (s.mode == MODE_GAMMA ? 8 * B * static_cast<size_t>(s.K) * s.N * kMaxSlices * kWaves : 0));
+  L.cand = o;
+  // draft-tree records: sized by the call's V (a workspace for V serves every smaller V)
+  o = align256(o + (s.mode == MODE_TREE ? 8 * B * static_cast<size_t>(s.K) * s.N * ((s.V + kPieceTok - 1) / kPieceTok) * s.topk : 0));
   L.total = o;
   return L;
 }
@@ -1656,6 +2103,7 @@ static int bind_workspace(Params& p, const Shape& s, void* ws, size_t bytes) {
   p.part = reinterpret_cast<unsigned long long*>(base + L.part);
   p.tot = reinterpret_cast<unsigned long long*>(base + L.tot);
   p.gpart = reinterpret_cast<unsigned long long*>(base + L.gpart);
+  p.cand = reinterpret_cast<unsigned long long*>(base + L.cand);
   return SPEC_OK;
 }
 
@@ -1674,7 +2122,7 @@ static int compute_units() {
 
 template <class Kernel>
 static int resident_workgroups(Kernel kernel, int which) {
-  static int cache[3][64] = {{0}};
+  static int cache[4][64] = {{0}};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (dev >= 0 && dev < 64 && cache[which][dev] > 0) return cache[which][dev];
@@ -1702,11 +2150,15 @@ static void plan_units(Params& p, const Shape& s) {
 static int launch_flow(Params& p, const Shape& s, hipStream_t stream) {
   // a slice is 32 KB of logits, so 2^31 slices exceed any device's memory; the
   // limit keeps the schedule in 32-bit arithmetic (with room for j * G + g)
-  if (s.total0 > 0x3fffffffLL || static_cast<int64_t>(s.B) * s.P1 > 0x3fffffffLL || s.ngroups > 0x3fffffffLL)
+  if (s.total0 > 0x3fffffffLL || static_cast<int64_t>(s.B) * s.P1 > 0x3fffffffLL || s.ngroups > 0x3fffffffLL ||
+      static_cast<int64_t>(s.B) * s.K * s.N * ((s.V + kPieceTok - 1) / kPieceTok) > 0x1fffffffLL)
     return SPEC_ERR_SHAPE;
   const bool verify = s.mode == MODE_VERIFY;
-  int grid = verify ? (p.kl_exact ? resident_workgroups(verify_kernel<true>, 2) : resident_workgroups(verify_kernel<false>, 0))
-                    : resident_workgroups(gamma_kernel, 1);
+  const bool tree = s.mode == MODE_TREE;
+  int grid = tree     ? resident_workgroups(tree_kernel, 3)
+             : verify ? (p.kl_exact ? resident_workgroups(verify_kernel<true>, 2)
+                                    : resident_workgroups(verify_kernel<false>, 0))
+                      : resident_workgroups(gamma_kernel, 1);
   if (grid <= 0) return SPEC_ERR_HIP;
   const int ncu = compute_units();
   const int slots = ncu > 0 && grid % ncu == 0 ? grid / ncu : 1;
@@ -1714,6 +2166,9 @@ static int launch_flow(Params& p, const Shape& s, hipStream_t stream) {
   if (s.ngroups * s.S > want) want = s.ngroups * s.S;
   if (static_cast<int64_t>(s.B) * s.P1 > want) want = static_cast<int64_t>(s.B) * s.P1;
   if (static_cast<int64_t>(s.B) * s.P2 > want) want = static_cast<int64_t>(s.B) * s.P2;
+  // piece units, four per workgroup at a time
+  const int64_t tree_units = tree ? (static_cast<int64_t>(s.B) * s.K * s.N * ((s.V + kPieceTok - 1) / kPieceTok) + 3) / 4 : 0;
+  if (tree_units > want) want = tree_units;
   if (grid > want) grid = static_cast<int>(want);
   // every workgroup is resident at once (the schedule's waits rely on it); a gamma
   // slot and a sequence's draw units need S workgroups at once
@@ -1721,7 +2176,9 @@ static int launch_flow(Params& p, const Shape& s, hipStream_t stream) {
   plan_units(p, s);
   p.ncu = ncu;
   p.slots = slots;  // make_split weights the slots only when the grid is all of them
-  if (verify && p.kl_exact)
+  if (tree)
+    hipLaunchKernelGGL(tree_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
+  else if (verify && p.kl_exact)
     hipLaunchKernelGGL(verify_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, p);
   else if (verify)
     hipLaunchKernelGGL(verify_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, p);
@@ -1888,6 +2345,50 @@ int spec_counterfactual_gamma(const spec_bf16* target, int64_t target_row_stride
   p.gamma = gamma;
   p.est_len = est_len;
   p.loss = loss;
+  return launch_flow(p, s, stream);
+}
+
+size_t spec_tree_workspace_bytes(int B, int K, int N, int V, int topk) {
+  if (B < 1 || K < 1 || N < 1 || K > SPEC_MAX_K || N > SPEC_MAX_N || B > SPEC_MAX_B || topk < 1 || topk > kMaxTopk ||
+      V < 1 || V > SPEC_MAX_V)
+    return 0;
+  Shape sh = make_shape(B, K, N, V, MODE_TREE, 0);
+  sh.topk = topk;
+  return ws_layout(sh).total;
+}
+
+int spec_tree_gamma(const spec_bf16* target, int64_t target_row_stride, int target_rows_per_seq,
+                    const spec_bf16* drafts, int64_t draft_row_stride, int64_t drafter_stride, int B, int K, int N,
+                    int V, int topk, float temperature, float* gamma, void* workspace, size_t workspace_bytes,
+                    spec_stream_t stream) {
+  int st = check_common(B, K, V, temperature);
+  if (st != SPEC_OK) return st;
+  if (N < 1 || N > SPEC_MAX_N) return SPEC_ERR_SHAPE;
+  if (topk < 1 || topk > kMaxTopk) return SPEC_ERR_PARAM;
+  if (!target || !drafts || !gamma) return SPEC_ERR_NULL;
+  if (target_rows_per_seq < K) return SPEC_ERR_SHAPE;
+  if (!stride_ok(target_row_stride, V) || !stride_ok(draft_row_stride, V)) return SPEC_ERR_SHAPE;
+  if (drafter_stride < 0 || (drafter_stride % 8) != 0 || (N > 1 && drafter_stride == 0)) return SPEC_ERR_SHAPE;
+  if (!aligned16(target) || !aligned16(drafts)) return SPEC_ERR_ALIGN;
+  Shape s = make_shape(B, K, N, V, MODE_TREE, 0);
+  s.topk = topk;
+  Params p{};
+  st = bind_workspace(p, s, workspace, workspace_bytes);
+  if (st != SPEC_OK) return st;
+  p.target = target;
+  p.t_stride = target_row_stride;
+  p.t_rows = target_rows_per_seq;
+  p.draft = drafts;
+  p.d_stride = draft_row_stride;
+  p.drafter_stride = drafter_stride;
+  p.B = B;
+  p.K = K;
+  p.N = N;
+  p.V = V;
+  p.c = log2e_over(temperature);
+  p.mode = MODE_TREE;
+  p.topk = topk;
+  p.gamma = gamma;
   return launch_flow(p, s, stream);
 }
 

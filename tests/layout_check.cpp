@@ -40,6 +40,31 @@ int main() {
               }
             }
       }
+  // draft-tree calls: ticket per target row, target statistics words, slice records
+  const int topks[] = {1, 2, 8, 33, 64};
+  for (int B : Bs)
+    for (int K : Ks)
+      for (int N : Ns)
+        for (int tk : topks) {
+          for (int V : Vs) {
+            const size_t total = spec_tree_workspace_bytes(B, K, N, V, tk);
+            Shape s = make_shape(B, K, N, V, MODE_TREE, 0);
+            s.topk = tk;
+            const WsLayout L = ws_layout(s);
+            ++checked;
+            const size_t part_words = static_cast<size_t>(B) * s.R * s.S * kWaves;
+            const size_t rec_words = static_cast<size_t>(B) * K * N * ((V + kPieceTok - 1) / kPieceTok) * tk;
+            const bool ok = s.R == K && s.RT == K && s.total0 == static_cast<int64_t>(B) * K * s.S &&
+                            L.done >= 16 && L.done + 4 * static_cast<size_t>(B) * K <= L.part &&
+                            L.part + 8 * part_words <= L.tot && L.cand + 8 * rec_words <= L.total &&
+                            L.total <= total && s.S <= kMaxSlices &&
+                            (V < 2 || L.total >= ws_layout([&] { Shape t = make_shape(B, K, N, V / 2, MODE_TREE, 0); t.topk = tk; return t; }()).total);
+            if (!ok) {
+              ++bad;
+              if (bad < 10) printf("tree layout violation B=%d K=%d N=%d V=%d topk=%d\n", B, K, N, V, tk);
+            }
+          }
+        }
   printf("checked %d layouts, %d violations\n", checked, bad);
   // phase-0 schedule: every slice of the list is dealt exactly once, and a
   // workgroup's list ends for good at its first T0 (static_phase stops there)

@@ -32,7 +32,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ["spec_verify", "spec_cactus_verify", "spec_cactus_kl_verify", "spec_counterfactual_gamma", "hedge_update",
+    for n in ["spec_verify", "spec_cactus_verify", "spec_cactus_kl_verify", "spec_counterfactual_gamma",
+              "spec_tree_gamma", "spec_tree_workspace_bytes", "hedge_update",
               "spec_workspace_bytes", "spec_workspace_init", "spec_status_str"]:
         assert n in names, names
 
@@ -158,3 +159,26 @@ def test_package_imports_no_oracle():
             "from speculative_sampling_verification_row_amd import binding, inputs, hedge; "
             "assert not any(m == 'oracle' or m.startswith('oracle.') for m in sys.modules), 'oracle imported'")
     subprocess.run([sys.executable, "-c", code], check=True, cwd=ROOT)
+
+
+def test_tree_workspace_and_validation(lib):
+    assert lib.spec_tree_workspace_bytes(4, 5, 7, 1000, 0) == 0 and lib.spec_tree_workspace_bytes(4, 5, 7, 1000, 65) == 0
+    assert lib.spec_tree_workspace_bytes(4, 5, 7, 0, 8) == 0 and lib.spec_tree_workspace_bytes(4, 5, 7, (1 << 20) + 1, 8) == 0
+    a = lib.spec_tree_workspace_bytes(32, 5, 7, 128256, 8)
+    # records: 32 pieces of 4096 tokens x 8 per row; statistics words of the K target rows
+    assert a % 256 == 0 and a >= 8 * 32 * 5 * 7 * 32 * 8 + 8 * 32 * 5 * 64 * 4
+    assert lib.spec_tree_workspace_bytes(32, 5, 7, 128256, 16) > a
+    assert lib.spec_tree_workspace_bytes(32, 5, 7, 1000, 8) < a
+
+    def call(**kw):
+        a = dict(t=fake(4096), ts=128, tr=3, d=fake(8192), ds=128, dstr=128 * 6, B=2, K=3, N=4, V=100, topk=8,
+                 T=1.0, g=fake(512), ws=fake(1 << 20), wsb=64)   # wsb too small: never launches
+        a.update(kw)
+        return lib.spec_tree_gamma(a["t"], a["ts"], a["tr"], a["d"], a["ds"], a["dstr"], a["B"], a["K"], a["N"],
+                                   a["V"], a["topk"], a["T"], a["g"], a["ws"], a["wsb"], None)
+    assert call(topk=0) == -3 and call(topk=65) == -3
+    assert call(N=0) == -2 and call(tr=2) == -2 and call(ds=50) == -2 and call(dstr=130) == -2
+    assert call(g=None) == -1 and call(t=None) == -1
+    assert call(T=0.0) == -3
+    assert call(d=fake(8200)) == -4
+    assert call() == -5
