@@ -49,6 +49,11 @@ R15 Cactus acceptance phi(n) = min(1, h_n / pd(n)) and recovery
 R16 Cactus: c = 1 gives gamma* = 1 and s := 0; delta = 0 gives s = 1.0
     exactly, so h == pt bit for bit and the position is plain SpS.
 R17 Cactus bonus is drawn from pt at row m (h is defined per candidate only).
+R25 Acceptance-probability objective ([NB] Key design 3): f = 1 - gamma per
+    position; a chunk's K position losses enter the learner as their sum (the
+    exponential weights depend on the cumulative loss only).  Censoring delay:
+    round s's losses are usable once K more tokens (accepted_len + 1 per round)
+    have been verified after round s.
 R24 Draft-tree gamma ([NB] Key design 1, the tree case): a drafter's children
     at a node are its topk tokens by logit, ties to the smaller id; gamma is
     the target probability of that set.
@@ -92,6 +97,11 @@ __all__ = [
     "normalhedge_select",
     "hedge_update",
     "hedge_delayed_rounds",
+    "acceptance_prob_loss",
+    "hedge_exp_step",
+    "hedge_exp_update",
+    "censored_delays",
+    "hedge_delayed_rounds_rule",
 ]
 
 
@@ -602,3 +612,91 @@ def hedge_delayed_rounds(losses, delays, v_select, loss_scale):
             sel[t, b] = normalhedge_select(W[b], float(v_select[t][b]))
             pending.append((t + 1 + int(delays[t][b]), t))
     return sel, R, W
+
+
+# ---------------------------------------------------------------------------
+# Acceptance-probability objective with exponential-weights Hedge
+# ---------------------------------------------------------------------------
+
+def acceptance_prob_loss(gamma):
+    """[NB] Key design 3's loss when the acceptance probability is optimised:
+    f = 1 - gamma at every position (reading R25: a chunk's losses, its K
+    positions, enter the learner together, as their sum).  gamma [B, K, N] ->
+    loss [B, N] in [0, K]."""
+    g = np.asarray(gamma, dtype=np.float64)
+    return np.sum(1.0 - g, axis=1)
+
+
+def hedge_exp_step(L, loss, eta: float):
+    """One exponential-weights (Hedge) update, [NB] Key design 3's other learner:
+    cumulative loss L += loss, weights proportional to exp(-eta L) (computed
+    against min L, which leaves them unchanged).  Returns (L, w)."""
+    L = np.asarray(L, dtype=np.float64) + np.asarray(loss, dtype=np.float64)
+    u = np.exp(-float(eta) * (L - L.min()))
+    return L, u / u.sum()
+
+
+def hedge_exp_update(cum_loss, weights, loss, has_loss, loss_scale, eta, v_select=None):
+    """Batched per-sequence Hedge, as hedge_update but with exponential weights
+    (learning rate eta >= 0).  cum_loss [B, N] float64 and weights [B, N]
+    float64 are the state.  Returns (cum_loss, weights, sel or None)."""
+    L = np.array(cum_loss, dtype=np.float64, copy=True)
+    W = np.array(weights, dtype=np.float64, copy=True)
+    scale = float(np.float32(loss_scale))
+    e = float(np.float32(eta))
+    for b in range(L.shape[0]):
+        if has_loss is None or has_loss[b]:
+            L[b], W[b] = hedge_exp_step(L[b], np.asarray(loss[b], dtype=np.float64) * scale, e)
+    sel = None
+    if v_select is not None:
+        sel = np.array([normalhedge_select(W[b], float(v_select[b])) for b in range(L.shape[0])], dtype=np.int64)
+    return L, W, sel
+
+
+def censored_delays(accepted_len, K: int):
+    """Delays that censoring causes ([NB] Key design 3): round s's chunk is only
+    fully scored once K more tokens have been verified after it.  Round r
+    verifies accepted_len[r] + 1 tokens, so round s's loss waits d rounds, d the
+    smallest with sum_{r = s+1 .. s+d} (accepted_len[r] + 1) >= K (reading R25;
+    d <= K <= 2K, the note's bound).  Rounds whose window runs past the last
+    never complete (delay -1).  accepted_len [T, B] -> delays [T, B]."""
+    A = np.asarray(accepted_len, dtype=np.int64)
+    T, B = A.shape
+    d = np.full((T, B), -1, dtype=np.int64)
+    for b in range(B):
+        for s in range(T):
+            got = 0
+            for r in range(s + 1, T):
+                got += int(A[r, b]) + 1
+                if got >= K:
+                    d[s, b] = r - s
+                    break
+    return d
+
+
+def hedge_delayed_rounds_rule(losses, delays, v_select, loss_scale, eta=None):
+    """hedge_delayed_rounds with the learner chosen: NormalHedge (eta None) or
+    exponential-weights Hedge with learning rate eta.  A delay of -1 never
+    arrives.  Returns (sel [T, B], state [B, N] (regret or cumulative loss),
+    weights [B, N])."""
+    losses = np.asarray(losses, dtype=np.float64)
+    T, B, N = losses.shape
+    S = np.zeros((B, N))
+    W = np.full((B, N), 1.0 / N)
+    sel = np.zeros((T, B), dtype=np.int64)
+    scale = float(np.float32(loss_scale))
+    e = None if eta is None else float(np.float32(eta))
+    for b in range(B):
+        pending = []
+        for t in range(T):
+            ready = sorted(p for p in pending if p[0] <= t)
+            pending = [p for p in pending if p[0] > t]
+            for _, s in ready:
+                if e is None:
+                    S[b], W[b] = normalhedge_step(S[b], W[b], losses[s, b] * scale)
+                else:
+                    S[b], W[b] = hedge_exp_step(S[b], losses[s, b] * scale, e)
+            sel[t, b] = normalhedge_select(W[b], float(v_select[t][b]))
+            if int(delays[t][b]) >= 0:
+                pending.append((t + 1 + int(delays[t][b]), t))
+    return sel, S, W

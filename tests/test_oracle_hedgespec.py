@@ -250,3 +250,83 @@ def test_delayed_rounds_order():
     assert list(sel[:, 0]) == [0, 0, 0, 0]
     np.testing.assert_allclose(R[0], [0.5, 0.5])
     np.testing.assert_allclose(W[0], [0.5, 0.5])
+
+
+# ---------------------------------------------------------------------------
+# Acceptance-probability objective, exponential-weights Hedge, censoring delay (R25)
+# ---------------------------------------------------------------------------
+
+def test_hedge_exp_weights_are_softmax_of_minus_eta_loss():
+    from scipy.special import softmax
+    rng = np.random.default_rng(30)
+    for _ in range(100):
+        N = int(rng.integers(1, 22))
+        eta = float(rng.uniform(0.0, 5.0))
+        L = rng.uniform(0, 50, N)
+        loss = rng.uniform(0, 1, N)
+        L2, w = oracle.hedge_exp_step(L, loss, eta)
+        np.testing.assert_allclose(L2, L + loss, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(w, softmax(-eta * (L + loss)), rtol=1e-12, atol=1e-15)
+    _, w0 = oracle.hedge_exp_step(np.arange(5.0), np.zeros(5), 0.0)
+    np.testing.assert_allclose(w0, np.full(5, 0.2), rtol=0, atol=1e-15)
+    _, wb = oracle.hedge_exp_step(np.array([3.0, 1.0, 2.0]), np.zeros(3), 1e4)
+    assert wb[1] > 1 - 1e-12
+
+
+def test_hedge_exp_regret_bound():
+    """Exponential weights with eta = sqrt(8 ln N / T) on losses in [0, 1]: expected loss minus
+    the best drafter's is at most sqrt(T ln N / 2) (the classical Hedge bound)."""
+    rng = np.random.default_rng(31)
+    N, T = 7, 3000
+    eta = np.sqrt(8 * np.log(N) / T)
+    for trial in range(5):
+        losses = rng.uniform(0, 1, (T, N)) * rng.uniform(0.2, 1.0, N)   # a drafter-dependent scale
+        L, w, got = np.zeros(N), np.full(N, 1.0 / N), 0.0
+        for t in range(T):
+            got += float(w @ losses[t])
+            L, w = oracle.hedge_exp_step(L, losses[t], eta)
+        assert got - losses.sum(0).min() <= np.sqrt(T * np.log(N) / 2) + 1e-9
+
+
+def test_acceptance_prob_loss():
+    g = np.array([[[1.0, 0.0], [1.0, 0.5], [1.0, 0.25]]])       # [B=1, K=3, N=2]
+    np.testing.assert_allclose(oracle.acceptance_prob_loss(g), [[0.0, 2.25]], rtol=0, atol=1e-15)
+
+
+def test_censored_delays():
+    # accepted lengths per round, K = 3: round 0 needs rounds 1 and 2 (1 + 2 tokens)
+    np.testing.assert_array_equal(oracle.censored_delays([[2], [0], [1], [4], [0]], 3).ravel(), [2, 2, 1, -1, -1])
+    rng = np.random.default_rng(32)
+    K, T = 5, 60
+    A = rng.integers(0, K + 1, (T, 3))
+    d = oracle.censored_delays(A, K)
+    for b in range(3):
+        for s in range(T):
+            if d[s, b] < 0:
+                assert (A[s + 1:, b] + 1).sum() < K
+            else:
+                assert 1 <= d[s, b] <= K
+                assert (A[s + 1:s + 1 + d[s, b], b] + 1).sum() >= K > (A[s + 1:s + d[s, b], b] + 1).sum()
+
+
+def test_delayed_rule_normalhedge_matches_existing_queue():
+    rng = np.random.default_rng(33)
+    T, B, N, K = 40, 3, 5, 4
+    losses = rng.uniform(0, K, (T, B, N))
+    delays = rng.integers(0, 2 * K + 1, (T, B))
+    v = rng.random((T, B), dtype=np.float32)
+    a = oracle.hedge_delayed_rounds(losses, delays, v, 1.0 / K)
+    b = oracle.hedge_delayed_rounds_rule(losses, delays, v, 1.0 / K, eta=None)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_planted_exp_sign_mistake_is_caught(monkeypatch):
+    from scipy.special import softmax
+    def wrong(L, loss, eta):
+        L = np.asarray(L, dtype=np.float64) + np.asarray(loss, dtype=np.float64)
+        u = np.exp(float(eta) * (L - L.max()))
+        return L, u / u.sum()
+    monkeypatch.setattr(so, "hedge_exp_step", wrong)
+    _, w = so.hedge_exp_step(np.array([0.0, 1.0, 2.0]), np.zeros(3), 1.0)
+    assert not np.allclose(w, softmax(-np.array([0.0, 1.0, 2.0])))
