@@ -272,6 +272,36 @@ int hedge_update(double* cum_regret, double* weights,
                  const float* v_select, int32_t* sel_out,
                  int B, int N, spec_stream_t stream);
 
+/*
+ * hedge_exp_update -- one exponential-weights Hedge round per sequence ([NB]
+ * Key design 3 names Hedge beside NormalHedge as the full-information learner).
+ *
+ * For every b with has_loss[b] != 0 (or every b if has_loss is NULL):
+ *   cum_loss[b][i] += loss[b][i] * loss_scale;
+ *   weights[b][i] = exp(-eta cum_loss[b][i]) / sum_j exp(-eta cum_loss[b][j])
+ * (fp64, evaluated against min_j cum_loss[b][j]).  Then, if v_select is not
+ * NULL, sel_out[b] = the inverse CDF of weights[b] at v_select[b], as
+ * hedge_update.
+ *
+ * cum_loss, weights  [B][N] float64 in/out, caller-owned learner state
+ *                    (initialise to 0 and 1/N)
+ * loss [B][N] float32; has_loss [B] uint8 or NULL; loss_scale and eta finite
+ * and >= 0 (SPEC_ERR_PARAM otherwise); v_select [B] float32 or NULL; sel_out
+ * [B] int32 (required when v_select is given).  1 <= N <= SPEC_MAX_N.
+ */
+int hedge_exp_update(double* cum_loss, double* weights, const float* loss, const uint8_t* has_loss,
+                     float loss_scale, float eta, const float* v_select, int32_t* sel_out,
+                     int B, int N, spec_stream_t stream);
+
+/*
+ * spec_acceptance_loss -- [NB] Key design 3's loss when the acceptance probability
+ * is optimised: f = 1 - gamma at every position, a chunk's K positions summed:
+ *   loss[b][i] = sum_k (1 - gamma[b][k][i])   (fp64 sum, stored as float32)
+ * gamma [B][K][N] float32 (spec_counterfactual_gamma or spec_tree_gamma),
+ * loss [B][N] float32 out, in [0, K].
+ */
+int spec_acceptance_loss(const float* gamma, float* loss, int B, int K, int N, spec_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -42,6 +42,8 @@ _SIGNATURES = {
     "spec_verify": (_I, [_P, _I64, _P, _I64, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P]),
     "spec_cactus_verify": (_I, [_P, _I64, _P, _I64, _P, _P, _P, _I, _I, _I, _F, _F, _P, _P, _P, _P, _P, _SZ, _P]),
     "spec_cactus_kl_verify": (_I, [_P, _I64, _P, _I64, _P, _P, _P, _I, _I, _I, _F, _F, _P, _P, _P, _P, _P, _SZ, _P]),
+    "hedge_exp_update": (_I, [_P, _P, _P, _P, _F, _F, _P, _P, _I, _I, _P]),
+    "spec_acceptance_loss": (_I, [_P, _P, _I, _I, _I, _P]),
     "spec_tree_gamma": (_I, [_P, _I64, _I, _P, _I64, _I64, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P]),
     "spec_tree_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "spec_counterfactual_gamma": (_I, [_P, _I64, _I, _P, _I64, _I64, _P, _I, _I, _I, _I, _F, _P, _P, _P,
@@ -334,3 +336,40 @@ def hedge_update(cum_regret, weights, loss, loss_scale: float, *, has_loss=None,
                           _ptr(v_select), _ptr(sel_out), B, N, _stream(stream))
     _check("hedge_update", st)
     return sel_out
+
+
+def hedge_exp_update(cum_loss, weights, loss, loss_scale: float, eta: float, *, has_loss=None, v_select=None,
+                     sel_out=None, stream=None):
+    """One exponential-weights Hedge round per sequence, in place on cum_loss / weights ([B, N]
+    float64).  Returns sel_out [B] int32 when v_select is given."""
+    lib = load()
+    _need_cuda(cum_loss, weights, loss, has_loss, v_select)
+    if cum_loss.dtype != torch.float64 or weights.dtype != torch.float64:
+        raise ValueError("learner state must be float64")
+    if not (cum_loss.is_contiguous() and weights.is_contiguous()):
+        raise ValueError("learner state must be contiguous")
+    B, N = cum_loss.shape
+    loss = loss.to(torch.float32).contiguous()
+    if has_loss is not None:
+        has_loss = has_loss.to(torch.uint8).contiguous()
+    if v_select is not None:
+        v_select = v_select.to(torch.float32).contiguous()
+        if sel_out is None:
+            sel_out = torch.empty(B, dtype=torch.int32, device=cum_loss.device)
+    st = lib.hedge_exp_update(_ptr(cum_loss), _ptr(weights), _ptr(loss), _ptr(has_loss), float(loss_scale),
+                              float(eta), _ptr(v_select), _ptr(sel_out), B, N, _stream(stream))
+    _check("hedge_exp_update", st)
+    return sel_out
+
+
+def spec_acceptance_loss(gamma, *, out=None, stream=None):
+    """Acceptance-probability loss of a chunk: sum over positions of 1 - gamma.
+    gamma [B, K, N] float32 -> loss [B, N] float32."""
+    lib = load()
+    _need_cuda(gamma)
+    gamma = gamma.to(torch.float32).contiguous()
+    B, K, N = gamma.shape
+    if out is None:
+        out = torch.empty((B, N), dtype=torch.float32, device=gamma.device)
+    _check("spec_acceptance_loss", lib.spec_acceptance_loss(_ptr(gamma), _ptr(out), B, K, N, _stream(stream)))
+    return out

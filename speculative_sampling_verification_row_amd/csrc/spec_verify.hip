@@ -1953,6 +1953,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // ---------------------------------------------------------------------------
 constexpr int kHedgeBisect = 64;
 
+// Next drafter of sequence b: inverse CDF of the weights at v[b] (ascending
+// drafter index), lane q holding drafter q's weight; every lane runs the same
+// loop over shuffled weights, lane 0 stores.
+__device__ __forceinline__ void hedge_select(double wcur, const float* v, int32_t* sel, int b, int N) {
+  double tot = 0.0;
+  for (int q = 0; q < N; ++q) tot += __shfl(wcur, q, 64);
+  const double x = static_cast<double>(v[b]) * tot;
+  double run = 0.0;
+  int pick = -1, last_pos = -1;
+  for (int q = 0; q < N; ++q) {
+    const double wq = __shfl(wcur, q, 64);
+    if (wq > 0.0) last_pos = q;
+    run += wq;
+    if (pick < 0 && run > x) pick = q;
+  }
+  if (threadIdx.x == 0) sel[b] = pick >= 0 ? pick : last_pos;
+}
+
 __global__ __launch_bounds__(64) void hedge_kernel(double* R, double* W, const float* loss, const uint8_t* has,
                                                    float scale, const float* v, int32_t* sel, int N) {
   const int b = blockIdx.x;
@@ -1994,23 +2012,45 @@ __global__ __launch_bounds__(64) void hedge_kernel(double* R, double* W, const f
     }
     wfinal = act ? wn : 0.0;
   }
-  if (v != nullptr) {
-    // next drafter: inverse CDF of the weights at v (ascending drafter index);
-    // every lane runs the same loop over shuffled weights, lane 0 stores.
-    const double wcur = wfinal;
-    double tot = 0.0;
-    for (int q = 0; q < N; ++q) tot += __shfl(wcur, q, 64);
-    const double x = static_cast<double>(v[b]) * tot;
-    double run = 0.0;
-    int pick = -1, last_pos = -1;
-    for (int q = 0; q < N; ++q) {
-      const double wq = __shfl(wcur, q, 64);
-      if (wq > 0.0) last_pos = q;
-      run += wq;
-      if (pick < 0 && run > x) pick = q;
+  if (v != nullptr) hedge_select(wfinal, v, sel, b, N);
+}
+
+// [NB] Key design 3's other learner: exponential-weights Hedge, one wave per
+// sequence, lane i = drafter i: cumulative loss L_i += loss_i * scale, weights
+// proportional to exp(-eta L_i) (taken against min L, which leaves them unchanged),
+// then the selection as hedge_kernel's.
+__global__ __launch_bounds__(64) void hedge_exp_kernel(double* L, double* W, const float* loss, const uint8_t* has,
+                                                       float scale, float eta, const float* v, int32_t* sel, int N) {
+  const int b = blockIdx.x;
+  const int i = threadIdx.x;
+  const bool act = i < N;
+  const int idx = b * N + i;
+  double wfinal = act ? W[idx] : 0.0;
+  if (has == nullptr || has[b] != 0) {
+    const double Li = act ? L[idx] + static_cast<double>(loss[idx]) * static_cast<double>(scale) : 0.0;
+    double mn = act ? Li : __builtin_inf();
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) mn = fmin(mn, __shfl_xor(mn, m, 64));
+    const double u = act ? exp(-static_cast<double>(eta) * (Li - mn)) : 0.0;
+    const double wn = u / wave_sum(u);
+    if (act) {
+      L[idx] = Li;
+      W[idx] = wn;
     }
-    if (i == 0) sel[b] = pick >= 0 ? pick : last_pos;
+    wfinal = act ? wn : 0.0;
   }
+  if (v != nullptr) hedge_select(wfinal, v, sel, b, N);
+}
+
+// [NB] Key design 3's acceptance-probability loss of a chunk: the sum over its K
+// positions of 1 - gamma (fp64), per sequence and drafter.
+__global__ void acceptance_loss_kernel(const float* gamma, float* loss, int B, int K, int N) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= B * N) return;
+  const int b = idx / N, i = idx - b * N;
+  double s = 0.0;
+  for (int k = 0; k < K; ++k) s += 1.0 - static_cast<double>(gamma[(static_cast<size_t>(b) * K + k) * N + i]);
+  loss[idx] = static_cast<float>(s);
 }
 
 __global__ void fill_zero_kernel(uint32_t* p, size_t n) {
@@ -2390,6 +2430,25 @@ int spec_tree_gamma(const spec_bf16* target, int64_t target_row_stride, int targ
   p.topk = topk;
   p.gamma = gamma;
   return launch_flow(p, s, stream);
+}
+
+int hedge_exp_update(double* cum_loss, double* weights, const float* loss, const uint8_t* has_loss, float loss_scale,
+                     float eta, const float* v_select, int32_t* sel_out, int B, int N, spec_stream_t stream) {
+  if (B < 1 || N < 1 || N > SPEC_MAX_N) return SPEC_ERR_SHAPE;
+  if (!cum_loss || !weights || !loss) return SPEC_ERR_NULL;
+  if (v_select && !sel_out) return SPEC_ERR_NULL;
+  if (!(loss_scale >= 0.0f) || !isfinite(loss_scale) || !(eta >= 0.0f) || !isfinite(eta)) return SPEC_ERR_PARAM;
+  hipLaunchKernelGGL(hedge_exp_kernel, dim3(B), dim3(64), 0, stream, cum_loss, weights, loss, has_loss, loss_scale, eta,
+                     v_select, sel_out, N);
+  return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+int spec_acceptance_loss(const float* gamma, float* loss, int B, int K, int N, spec_stream_t stream) {
+  if (B < 1 || K < 1 || N < 1 || B > SPEC_MAX_B || K > SPEC_MAX_K || N > SPEC_MAX_N) return SPEC_ERR_SHAPE;
+  if (!gamma || !loss) return SPEC_ERR_NULL;
+  const int n = B * N;
+  hipLaunchKernelGGL(acceptance_loss_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, gamma, loss, B, K, N);
+  return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 
 int hedge_update(double* cum_regret, double* weights, const float* loss, const uint8_t* has_loss, float loss_scale,

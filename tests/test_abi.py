@@ -33,7 +33,8 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["spec_verify", "spec_cactus_verify", "spec_cactus_kl_verify", "spec_counterfactual_gamma",
-              "spec_tree_gamma", "spec_tree_workspace_bytes", "hedge_update",
+              "spec_tree_gamma", "spec_tree_workspace_bytes", "hedge_update", "hedge_exp_update",
+              "spec_acceptance_loss",
               "spec_workspace_bytes", "spec_workspace_init", "spec_status_str"]:
         assert n in names, names
 
@@ -182,3 +183,25 @@ def test_tree_workspace_and_validation(lib):
     assert call(T=0.0) == -3
     assert call(d=fake(8200)) == -4
     assert call() == -5
+
+
+def test_hedge_exp_and_loss_validation(lib):
+    ok = [fake(4096), fake(8192), fake(1024), None, 0.2, 0.5, None, None, 4, 7, None]  # never called as is
+    for pos, val, code in [(9, 65, -2), (8, 0, -2), (4, float("nan"), -3), (5, -1.0, -3), (5, float("inf"), -3),
+                           (0, None, -1), (2, None, -1), (6, fake(64), -1)]:
+        a = list(ok)
+        a[pos] = val
+        assert lib.hedge_exp_update(*a) == code, (pos, val)
+    assert lib.spec_acceptance_loss(fake(64), fake(128), 0, 5, 7, None) == -2
+    assert lib.spec_acceptance_loss(fake(64), fake(128), 2, 65, 7, None) == -2
+    assert lib.spec_acceptance_loss(None, fake(128), 2, 5, 7, None) == -1
+
+
+def test_host_censored_delays_match_oracle():
+    import numpy as np
+    import oracle
+    from speculative_sampling_verification_row_amd.hedge import censored_delays
+    rng = np.random.default_rng(5)
+    for K in [1, 3, 8]:
+        A = rng.integers(0, K + 1, (50, 4))
+        np.testing.assert_array_equal(np.array(censored_delays(A.tolist(), K)), oracle.censored_delays(A, K))

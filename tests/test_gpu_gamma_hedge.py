@@ -157,3 +157,40 @@ def test_hedge_checkpoint_resume_bit_identical(binding):
         binding.hedge_update(R2, W2, dev_f32(losses[t]), 1.0 / K)
     torch.cuda.synchronize()
     assert torch.equal(R, R2) and torch.equal(W, W2)
+
+
+def test_acceptance_loss_kernel(binding):
+    banner("acceptance loss B=32 K=5 N=7")
+    rng = np.random.default_rng(40)
+    g = rng.random((32, 5, 7), dtype=np.float32)
+    g[0, :, 0] = 1.0
+    g[1, :, 1] = 0.0
+    got = to_np(binding.spec_acceptance_loss(dev_f32(g)))
+    ref = oracle.acceptance_prob_loss(g.astype(np.float64))
+    assert_rel(got, ref, rel=1e-6, label="acceptance loss")
+    assert got[0, 0] == 0.0 and got[1, 1] == 5.0
+
+
+@pytest.mark.parametrize("eta", [0.0, 0.3, 2.0])
+def test_hedge_exp_256_rounds_censored(binding, eta):
+    """Exponential-weights Hedge over T=256 rounds, B=32 learners of N=7 drafters, losses
+    f = sum of 1 - gamma over K=5 positions, delays from censoring (K later tokens)."""
+    banner(f"hedge-exp 256 rounds eta={eta}")
+    from speculative_sampling_verification_row_amd.hedge import DelayedHedge
+    T, B, N, K = 256, 32, 7, 5
+    rng = np.random.default_rng(41)
+    gam = rng.beta(2.0, 1.0 + np.arange(N), (T, B, K, N)).astype(np.float32)   # drafter-dependent quality
+    losses = np.stack([oracle.acceptance_prob_loss(gam[t].astype(np.float64)) for t in range(T)]).astype(np.float32)
+    A = rng.integers(0, K + 1, (T, B))
+    delays = oracle.censored_delays(A, K)
+    v = rng.random((T, B), dtype=np.float32)
+    sel_o, L_o, W_o = oracle.hedge_delayed_rounds_rule(losses, delays, v, 1.0 / K, eta=eta)
+    h = DelayedHedge(B, N, 1.0 / K, eta=eta)
+    sel_g = np.zeros((T, B), dtype=np.int64)
+    for t in range(T):
+        sel_g[t] = to_np(h.select(t, dev_f32(v[t])))
+        h.push(t, dev_f32(losses[t]), delays[t])
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(to_np(h.cum_regret), L_o, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(to_np(h.weights), W_o, rtol=1e-9, atol=1e-12)
+    assert (sel_g == sel_o).mean() == 1.0, np.argwhere(sel_g != sel_o)[:10]
