@@ -40,7 +40,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-GAMMA_WORKLOADS = ("hedge_eval", "pool21", "small_mixed")
+GAMMA_WORKLOADS = ("hedge_eval", "pool21", "small_mixed", "hedge_loop")
 
 
 def kernel_of(key: str) -> str:
@@ -248,6 +248,43 @@ class TreeLike(GammaLike):
         return done * K, time.perf_counter() - t0, time.process_time() - c0, f"{done} sequences of this batch, one at a time"
 
 
+class LoopLike(GammaLike):
+    """One HedgeSpec round resident on the device, replayed from a captured graph: the
+    delayed-feedback queue with NormalHedge selects each sequence's drafter, then the fused
+    spec_counterfactual_gamma evaluates all N drafters and verifies the selected one.  One
+    step = one round.  The rows are the same every round (resident; the round's rows would
+    be written into the same buffers)."""
+
+    ROUNDS = 4096
+
+    def __init__(self, key, w):
+        import dataclasses
+        super().__init__(key, dataclasses.replace(w, fused=True, draft_from="drafter0"))
+        self.desc = f"{self.w.name}, fused HedgeSpec round (queue + NormalHedge + gamma + verify) from a graph"
+
+    def setup(self, copies_min_bytes):
+        import torch
+        from speculative_sampling_verification_row_amd import inputs as gen
+        from speculative_sampling_verification_row_amd.loop import HedgeSpecLoop
+        self.torch = torch
+        log(f"generating inputs: {self.desc}")
+        self.x = x = gen.make_gamma_inputs(self.w)
+        i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+        f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+        sch = gen.hedge_schedule(self.ROUNDS, self.w.B, self.w.K)
+        self.loop = HedgeSpecLoop(_dev(torch, x["target"]), _dev(torch, x["drafts"]), i32(x["traj"]),
+                                  i32(x["draft_tokens"]), f32(x["r"]), f32(x["u"]), i32(sch["delays"]), f32(sch["v"]),
+                                  1.0 / self.w.K, self.w.temperature)
+        self.loop.step()          # eager round: library set-up outside the capture
+        torch.cuda.synchronize()
+        self.loop.reset()
+        self.loop.capture()
+        log("captured one round as a graph")
+
+    def launch(self, i):
+        self.loop.replay()
+
+
 def workloads():
     from speculative_sampling_verification_row_amd import inputs as gen
     return {
@@ -261,6 +298,7 @@ def workloads():
         "small_mixed": lambda: GammaLike("small_mixed", gen.SMALL_MIXED),
         "hedge_eval_tree": lambda: TreeLike("hedge_eval_tree", gen.HEDGE_EVAL, topk=8),
         "pool21_tree": lambda: TreeLike("pool21_tree", gen.POOL21, topk=8),
+        "hedge_loop": lambda: LoopLike("hedge_loop", gen.HEDGE_EVAL),
     }
 
 

@@ -294,6 +294,32 @@ int hedge_exp_update(double* cum_loss, double* weights, const float* loss, const
                      int B, int N, spec_stream_t stream);
 
 /*
+ * hedge_queue_update -- one round of per-sequence NormalHedge under delayed
+ * feedback, with the feedback queue resident on the device ([NB] Key design 3:
+ * the stochastic-setting reduction keeps a queue of losses and applies each as it
+ * becomes available), so that rounds can follow each other without the host
+ * (e.g. in a captured graph).  Sequence b's call at round t = round[b]:
+ *   1. if t > 0, queues round t-1's loss[b][*] * loss_scale, usable at round
+ *      t + delays[(t-1) B + b] (a delay of -1 never arrives);
+ *   2. applies every queued loss usable at round t, one NormalHedge step each
+ *      (as hedge_update), in order of (usable round, origin round);
+ *   3. draws round t's drafter: sel_out[b] = inverse CDF of weights[b] at
+ *      v_select[t B + b]; sel_hist[t B + b] = sel_out[b];
+ *   4. round[b] = t + 1.  Calls with round[b] >= T do nothing.
+ * This is the schedule of hedge_update applied as the host-side queue does
+ * (losses of round s usable at round s + 1 + d_s).
+ *
+ * cum_regret, weights [B][N] float64 state (0 and 1/N to start);
+ * queue_loss [B][Q][N] float64 and queue_due [B][Q] int32 the queue (queue_due
+ * all -1 to start); round [B] int32 (0 to start); loss [B][N] float32 (round
+ * t-1's); delays [T][B] int32 in [-1, Q-2]; v_select [T][B] float32; sel_out
+ * [B], sel_hist [T][B] int32.  2 <= Q <= 256, 1 <= N <= SPEC_MAX_N.
+ */
+int hedge_queue_update(double* cum_regret, double* weights, double* queue_loss, int32_t* queue_due, int32_t* round,
+                       const float* loss, const int32_t* delays, float loss_scale, const float* v_select,
+                       int32_t* sel_out, int32_t* sel_hist, int B, int N, int Q, int T, spec_stream_t stream);
+
+/*
  * spec_acceptance_loss -- [NB] Key design 3's loss when the acceptance probability
  * is optimised: f = 1 - gamma at every position, a chunk's K positions summed:
  *   loss[b][i] = sum_k (1 - gamma[b][k][i])   (fp64 sum, stored as float32)

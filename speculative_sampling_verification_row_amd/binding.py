@@ -44,6 +44,7 @@ _SIGNATURES = {
     "spec_cactus_kl_verify": (_I, [_P, _I64, _P, _I64, _P, _P, _P, _I, _I, _I, _F, _F, _P, _P, _P, _P, _P, _SZ, _P]),
     "hedge_exp_update": (_I, [_P, _P, _P, _P, _F, _F, _P, _P, _I, _I, _P]),
     "spec_acceptance_loss": (_I, [_P, _P, _I, _I, _I, _P]),
+    "hedge_queue_update": (_I, [_P, _P, _P, _P, _P, _P, _P, _F, _P, _P, _P, _I, _I, _I, _I, _P]),
     "spec_tree_gamma": (_I, [_P, _I64, _I, _P, _I64, _I64, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P]),
     "spec_tree_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "spec_counterfactual_gamma": (_I, [_P, _I64, _I, _P, _I64, _I64, _P, _I, _I, _I, _I, _F, _P, _P, _P,

@@ -1953,10 +1953,42 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // ---------------------------------------------------------------------------
 constexpr int kHedgeBisect = 64;
 
+// One NormalHedge step of a wave, lane i = drafter i (act: i < N): with the loss l
+// (already scaled), lhat = sum_i w_i l_i, R_i += lhat - l_i, then the weights
+// from [R]+ ([NH]; uniform when every [R_i]+ is 0).  Every lane of the wave must
+// call it: the wave sums read all 64 lanes.
+__device__ __forceinline__ void normalhedge_step(double& R, double& w, double l, bool act, int N) {
+  const double lhat = wave_sum(act ? w * l : 0.0);
+  R = act ? R + (lhat - l) : 0.0;
+  const double rp = act ? fmax(R, 0.0) : 0.0;
+  double M = rp;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) M = fmax(M, __shfl_xor(M, m, 64));
+  if (M > 0.0) {
+    // (1/N) sum exp(rp^2 / 2c) = e, bisection on [M^2 / (2 (1 + ln N)), M^2 / 2]
+    double lo = M * M / (2.0 * (1.0 + log(static_cast<double>(N))));
+    double hi = M * M / 2.0;
+    for (int it = 0; it < kHedgeBisect; ++it) {
+      const double mid = 0.5 * (lo + hi);
+      const double f = wave_sum(act ? exp(rp * rp / (2.0 * mid)) : 0.0) / static_cast<double>(N);
+      if (f > 2.71828182845904523536)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    const double cc = 0.5 * (lo + hi);
+    const double wu = act ? (rp / cc) * exp(rp * rp / (2.0 * cc)) : 0.0;
+    const double tot = wave_sum(wu);  // every lane takes part (lanes past N add 0)
+    w = act ? wu / tot : 0.0;
+  } else {
+    w = act ? 1.0 / static_cast<double>(N) : 0.0;
+  }
+}
+
 // Next drafter of sequence b: inverse CDF of the weights at v[b] (ascending
 // drafter index), lane q holding drafter q's weight; every lane runs the same
-// loop over shuffled weights, lane 0 stores.
-__device__ __forceinline__ void hedge_select(double wcur, const float* v, int32_t* sel, int b, int N) {
+// loop over shuffled weights, lane 0 stores.  Every lane returns the pick.
+__device__ __forceinline__ int hedge_select(double wcur, const float* v, int32_t* sel, int b, int N) {
   double tot = 0.0;
   for (int q = 0; q < N; ++q) tot += __shfl(wcur, q, 64);
   const double x = static_cast<double>(v[b]) * tot;
@@ -1968,7 +2000,9 @@ __device__ __forceinline__ void hedge_select(double wcur, const float* v, int32_
     run += wq;
     if (pick < 0 && run > x) pick = q;
   }
-  if (threadIdx.x == 0) sel[b] = pick >= 0 ? pick : last_pos;
+  const int s = pick >= 0 ? pick : last_pos;
+  if (threadIdx.x == 0) sel[b] = s;
+  return s;
 }
 
 __global__ __launch_bounds__(64) void hedge_kernel(double* R, double* W, const float* loss, const uint8_t* has,
@@ -1979,38 +2013,13 @@ __global__ __launch_bounds__(64) void hedge_kernel(double* R, double* W, const f
   const int idx = b * N + i;
   double wfinal = act ? W[idx] : 0.0;
   if (has == nullptr || has[b] != 0) {
+    double Ri = act ? R[idx] : 0.0;
     const double l = act ? static_cast<double>(loss[idx]) * static_cast<double>(scale) : 0.0;
-    const double wi = act ? W[idx] : 0.0;
-    const double lhat = wave_sum(wi * l);
-    const double Ri = act ? R[idx] + (lhat - l) : 0.0;
-    const double rp = act ? fmax(Ri, 0.0) : 0.0;
-    double M = rp;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) M = fmax(M, __shfl_xor(M, m, 64));
-    double wn;
-    if (M > 0.0) {
-      // (1/N) sum exp(rp^2 / 2c) = e, bisection on [M^2 / (2 (1 + ln N)), M^2 / 2]
-      double lo = M * M / (2.0 * (1.0 + log(static_cast<double>(N))));
-      double hi = M * M / 2.0;
-      for (int it = 0; it < kHedgeBisect; ++it) {
-        const double mid = 0.5 * (lo + hi);
-        const double f = wave_sum(act ? exp(rp * rp / (2.0 * mid)) : 0.0) / static_cast<double>(N);
-        if (f > 2.71828182845904523536)
-          lo = mid;
-        else
-          hi = mid;
-      }
-      const double cc = 0.5 * (lo + hi);
-      const double wu = act ? (rp / cc) * exp(rp * rp / (2.0 * cc)) : 0.0;
-      wn = wu / wave_sum(wu);
-    } else {
-      wn = 1.0 / static_cast<double>(N);
-    }
+    normalhedge_step(Ri, wfinal, l, act, N);
     if (act) {
       R[idx] = Ri;
-      W[idx] = wn;
+      W[idx] = wfinal;
     }
-    wfinal = act ? wn : 0.0;
   }
   if (v != nullptr) hedge_select(wfinal, v, sel, b, N);
 }
@@ -2040,6 +2049,82 @@ __global__ __launch_bounds__(64) void hedge_exp_kernel(double* L, double* W, con
     wfinal = act ? wn : 0.0;
   }
   if (v != nullptr) hedge_select(wfinal, v, sel, b, N);
+}
+
+// [NB] Key design 3's delayed feedback, resident on the device: one wave per
+// sequence b, lane i = drafter i.  round[b] counts the calls of sequence b.  A
+// call at round t (t = round[b]):
+//   1. pushes round t - 1's loss (when t > 0) into ring slot (t - 1) % Q with its
+//      usable round t + d (d = delays[(t - 1) B + b], -1: never);
+//   2. applies every queued loss usable at t, one NormalHedge step each, in order
+//      of (usable round, origin round), and frees their slots;
+//   3. draws round t's drafter: sel[b] = inverse CDF of the weights at
+//      v[t B + b], also kept in sel_hist[t B + b];
+//   4. round[b] = t + 1.
+// The same queue and order as the host-side DelayedNormalHedge.  Slots hold the
+// scaled loss (fp64) and the usable round (-1: free); the usable rounds are worked
+// on in LDS during the call.  Delays of at most Q - 2 rounds keep a slot from
+// being reused before its loss is applied (Q >= 2K + 2 covers the note's 2K).
+constexpr int kMaxQueue = 256;
+__global__ __launch_bounds__(64) void hedge_queue_kernel(double* R, double* W, double* qloss, int32_t* qdue,
+                                                         int32_t* round, const float* loss, const int32_t* delays,
+                                                         float scale, const float* v, int32_t* sel, int32_t* sel_hist,
+                                                         int B, int N, int Q, int T) {
+  const int b = blockIdx.x;
+  const int i = threadIdx.x;
+  const bool act = i < N;
+  const int idx = b * N + i;
+  const int t = round[b];
+  if (t >= T) return;  // the schedules are exhausted: nothing more (never reached by a well-formed loop)
+  __shared__ int32_t due[kMaxQueue];
+  double Ri = act ? R[idx] : 0.0, wi = act ? W[idx] : 0.0;
+  int32_t* gdue = qdue + static_cast<size_t>(b) * Q;
+  double* ql = qloss + static_cast<size_t>(b) * Q * N;
+  for (int q = i; q < Q; q += 64) due[q] = gdue[q];
+  __syncthreads();
+  // this call's push stays in a register too: reading the slot back from global
+  // memory in the same call is not relied on
+  int pslot = -1;
+  double pushed = 0.0;
+  if (t > 0) {
+    const int d = delays[(t - 1) * B + b];
+    pslot = (t - 1) % Q;
+    pushed = act ? static_cast<double>(loss[idx]) * static_cast<double>(scale) : 0.0;
+    if (act) ql[pslot * N + i] = pushed;
+    if (i == 0) due[pslot] = d >= 0 ? t + d : -1;
+  }
+  __syncthreads();
+  // ready slots, earliest (usable round, origin round) first; origin of slot q is the
+  // latest round r <= t - 1 with r % Q == q
+  for (;;) {
+    int best = -1;
+    long long key = 0x7fffffffffffffffLL;
+    for (int q = 0; q < Q; ++q) {
+      const int u = due[q];
+      if (u < 0 || u > t) continue;
+      const int origin = (t - 1) - (((t - 1) % Q - q) % Q + Q) % Q;
+      const long long k2 = (static_cast<long long>(u) << 32) | static_cast<uint32_t>(origin);
+      if (k2 < key) {
+        key = k2;
+        best = q;
+      }
+    }
+    if (best < 0) break;
+    normalhedge_step(Ri, wi, act ? (best == pslot ? pushed : ql[best * N + i]) : 0.0, act, N);
+    __syncthreads();
+    if (i == 0) due[best] = -1;
+    __syncthreads();
+  }
+  if (act) {
+    R[idx] = Ri;
+    W[idx] = wi;
+  }
+  for (int q = i; q < Q; q += 64) gdue[q] = due[q];
+  const int pick = hedge_select(wi, v + static_cast<size_t>(t) * B, sel, b, N);
+  if (i == 0) {
+    sel_hist[static_cast<size_t>(t) * B + b] = pick;
+    round[b] = t + 1;
+  }
 }
 
 // [NB] Key design 3's acceptance-probability loss of a chunk: the sum over its K
@@ -2440,6 +2525,19 @@ int hedge_exp_update(double* cum_loss, double* weights, const float* loss, const
   if (!(loss_scale >= 0.0f) || !isfinite(loss_scale) || !(eta >= 0.0f) || !isfinite(eta)) return SPEC_ERR_PARAM;
   hipLaunchKernelGGL(hedge_exp_kernel, dim3(B), dim3(64), 0, stream, cum_loss, weights, loss, has_loss, loss_scale, eta,
                      v_select, sel_out, N);
+  return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+int hedge_queue_update(double* cum_regret, double* weights, double* queue_loss, int32_t* queue_due, int32_t* round,
+                       const float* loss, const int32_t* delays, float loss_scale, const float* v_select,
+                       int32_t* sel_out, int32_t* sel_hist, int B, int N, int Q, int T, spec_stream_t stream) {
+  if (B < 1 || N < 1 || N > SPEC_MAX_N || Q < 2 || Q > kMaxQueue || T < 1) return SPEC_ERR_SHAPE;
+  if (!cum_regret || !weights || !queue_loss || !queue_due || !round || !loss || !delays || !v_select || !sel_out ||
+      !sel_hist)
+    return SPEC_ERR_NULL;
+  if (!(loss_scale >= 0.0f) || !isfinite(loss_scale)) return SPEC_ERR_PARAM;
+  hipLaunchKernelGGL(hedge_queue_kernel, dim3(B), dim3(64), 0, stream, cum_regret, weights, queue_loss, queue_due,
+                     round, loss, delays, loss_scale, v_select, sel_out, sel_hist, B, N, Q, T);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 

@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["spec_verify", "spec_cactus_verify", "spec_cactus_kl_verify", "spec_counterfactual_gamma",
               "spec_tree_gamma", "spec_tree_workspace_bytes", "hedge_update", "hedge_exp_update",
-              "spec_acceptance_loss",
+              "spec_acceptance_loss", "hedge_queue_update",
               "spec_workspace_bytes", "spec_workspace_init", "spec_status_str"]:
         assert n in names, names
 
@@ -205,3 +205,13 @@ def test_host_censored_delays_match_oracle():
     for K in [1, 3, 8]:
         A = rng.integers(0, K + 1, (50, 4))
         np.testing.assert_array_equal(np.array(censored_delays(A.tolist(), K)), oracle.censored_delays(A, K))
+
+
+def test_hedge_queue_validation(lib):
+    P_ = fake(4096)
+    base = [P_, P_, P_, P_, P_, P_, P_, 0.2, P_, P_, P_, 4, 7, 12, 100, None]  # never called as is
+    for pos, val, code in [(11, 0, -2), (12, 65, -2), (13, 1, -2), (13, 257, -2), (14, 0, -2), (7, float("nan"), -3),
+                           (0, None, -1), (4, None, -1), (10, None, -1)]:
+        a = list(base)
+        a[pos] = val
+        assert lib.hedge_queue_update(*a) == code, (pos, val)
