@@ -55,12 +55,18 @@ def log(msg: str) -> None:
 
 
 def source_hash() -> str:
+    """Hash of the kernel sources' code: comments and whitespace are left out, so that
+    only a change of the code itself makes recorded counters stale."""
     csrc = os.path.join(ROOT, "speculative_sampling_verification_row_amd", "csrc")
     h = hashlib.sha256()
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".hpp", ".h", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+            with open(os.path.join(csrc, name), "r") as f:
+                text = f.read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
+            text = " ".join(text.split())
+            h.update(name.encode() + b"\0" + text.encode())
     return h.hexdigest()[:16]
 
 

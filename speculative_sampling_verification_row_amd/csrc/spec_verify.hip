@@ -1,10 +1,14 @@
 // libspecverify: batched speculative-sampling verification on gfx950.
 //
-// Two persistent kernels: `verify_kernel` serves spec_verify, spec_cactus_verify
+// Three persistent kernels: `verify_kernel` serves spec_verify, spec_cactus_verify
 // and (an instance of its own) spec_cactus_kl_verify, `gamma_kernel` serves
-// spec_counterfactual_gamma.  A grid is
-// the number of workgroups the device holds at once (G), and every workgroup g
-// runs its phases on a fixed schedule; nothing is claimed from a shared counter.
+// spec_counterfactual_gamma, and `tree_kernel` serves spec_tree_gamma (its
+// phases are described where it is defined).  A grid is the number of
+// workgroups the device holds at once (G), and every workgroup g runs its
+// phases on a fixed schedule; nothing is claimed from a shared counter.  Small
+// one-wave kernels serve the learners: hedge_update, hedge_exp_update and
+// hedge_queue_update (the delayed-feedback queue resident on the device), and
+// spec_acceptance_loss.
 //
 //   gamma groups -- (gamma calls) slots of S workgroups stream a position's
 //       target row and its N drafter rows once (gamma_groups).
