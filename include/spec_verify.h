@@ -255,8 +255,8 @@ size_t spec_tree_workspace_bytes(int B, int K, int N, int V, int topk);
  * l_i = loss[b][i] * loss_scale and w = weights[b]:
  *   lhat = sum_i w_i l_i;  cum_regret[b][i] += lhat - l_i;
  *   if no cum_regret[b][i] > 0: weights[b] = uniform; otherwise find c > 0 with
- *   (1/N) sum_i exp([R_i]+^2 / (2c)) = e (fp64 bisection on
- *   [M^2 / (2(1 + ln N)), M^2 / 2], M = max [R]+) and set
+ *   (1/N) sum_i exp([R_i]+^2 / (2c)) = e (fp64 Newton steps from the left end of
+ *   [M^2 / (2(1 + ln N)), M^2 / 2], M = max [R]+, to 1e-15 of c) and set
  *   weights[b][i] proportional to ([R_i]+ / c) exp([R_i]+^2 / (2c)).
  * Then, if v_select is not NULL, sel_out[b] = the inverse CDF of weights[b]
  * at v_select[b] (the next drafter, drawn from the weights).

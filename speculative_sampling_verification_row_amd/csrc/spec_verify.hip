@@ -1955,7 +1955,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // ---------------------------------------------------------------------------
 // NormalHedge ([NH]); one wave per sequence, lane i = drafter i.
 // ---------------------------------------------------------------------------
-constexpr int kHedgeBisect = 64;
+constexpr int kHedgeBisect = 64;  // most Newton steps for the NormalHedge scale
 
 // One NormalHedge step of a wave, lane i = drafter i (act: i < N): with the loss l
 // (already scaled), lhat = sum_i w_i l_i, R_i += lhat - l_i, then the weights
@@ -1969,18 +1969,25 @@ __device__ __forceinline__ void normalhedge_step(double& R, double& w, double l,
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) M = fmax(M, __shfl_xor(M, m, 64));
   if (M > 0.0) {
-    // (1/N) sum exp(rp^2 / 2c) = e, bisection on [M^2 / (2 (1 + ln N)), M^2 / 2]
-    double lo = M * M / (2.0 * (1.0 + log(static_cast<double>(N))));
-    double hi = M * M / 2.0;
+    // the scale c > 0 with (1/N) sum exp(rp^2 / 2c) = e.  phi(c) = sum exp(rp^2 / 2c) - N e
+    // is convex and decreasing, and phi >= 0 at lo = M^2 / (2 (1 + ln N)) (the bracket's
+    // left end), so Newton steps from lo rise to the root without passing it; they
+    // stop once a step is below 1e-15 of c, or after kHedgeBisect steps
+    const double Ne = static_cast<double>(N) * 2.71828182845904523536;
+    const double hi = M * M / 2.0;
+    double cc = M * M / (2.0 * (1.0 + log(static_cast<double>(N))));
     for (int it = 0; it < kHedgeBisect; ++it) {
-      const double mid = 0.5 * (lo + hi);
-      const double f = wave_sum(act ? exp(rp * rp / (2.0 * mid)) : 0.0) / static_cast<double>(N);
-      if (f > 2.71828182845904523536)
-        lo = mid;
-      else
-        hi = mid;
+      const double a = act ? rp * rp / (2.0 * cc) : 0.0;
+      const double e = act ? exp(a) : 0.0;
+      const double phi = wave_sum(e) - Ne;
+      const double dphi = -wave_sum(e * a) / cc;  // d/dc of sum exp(rp^2 / 2c)
+      if (!(phi > 0.0) || !(dphi < 0.0)) break;   // at (or, by rounding, past) the root
+      const double cn = fmin(cc - phi / dphi, hi);
+      if (!(cn > cc)) break;
+      const bool done = cn - cc <= 1e-15 * cn;
+      cc = cn;
+      if (done) break;
     }
-    const double cc = 0.5 * (lo + hi);
     const double wu = act ? (rp / cc) * exp(rp * rp / (2.0 * cc)) : 0.0;
     const double tot = wave_sum(wu);  // every lane takes part (lanes past N add 0)
     w = act ? wu / tot : 0.0;
