@@ -120,3 +120,29 @@ def test_tree_hedge_eval_size_sampled(binding):
         pt = oracle.softmax_t(oracle.widen_bf16(x["target"][b, k]), 1.0)
         ref = [oracle.tree_gamma(pt, oracle.widen_bf16(x["drafts"][i, b, k]), 8) for i in range(7)]
         assert_rel(got[b, k], np.array(ref), label=f"tree full ({b},{k})")
+
+
+def test_tree_merge_overflow_bound_at_max_vocab(binding):
+    """V = 2^20 (256 pieces of 4096 tokens), every piece holding the same logits: each piece's
+    64th best record ties on the logit and loses on the id to piece 0's, so ~16k records reach
+    the merge's first bound and the second bound (the 64th best of the pieces' bests) must take
+    over.  The children are the best token of pieces 0..63."""
+    banner("tree merge overflow V=2^20 topk=64")
+    V, topk = 1 << 20, 64
+    rng = np.random.default_rng(70)
+    piece = rng.normal(0, 2.0, 4096)
+    d = bf16_bits_from_f64(np.tile(piece, V // 4096)).reshape(1, 1, 1, V)
+    t = bf16_bits_from_f64(rng.normal(0, 4.0, (1, 1, V)))
+    got = run_tree(binding, t, d, topk)
+    ref = oracle.spec_tree_gamma(t, d, topk)
+    assert_rel(got, ref, label="tree merge overflow")
+    kids = oracle.tree_children(oracle.widen_bf16(d[0, 0, 0]), topk)
+    assert np.all(kids // 4096 < 64) and len(set((kids % 4096).tolist())) == 1
+
+
+def test_tree_single_drafter_position_max_topk_ragged(binding):
+    banner("tree N=1 K=1 V=100003 topk=64 and topk=1")
+    t, d = tree_case(3, 1, 1, 100003, seed=71)
+    for topk in (1, 64):
+        got = run_tree(binding, t, d, topk)
+        assert_rel(got, oracle.spec_tree_gamma(t, d, topk), label=f"tree N=1 topk={topk}")
