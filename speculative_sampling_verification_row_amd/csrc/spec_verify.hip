@@ -1969,25 +1969,31 @@ __device__ __forceinline__ void normalhedge_step(double& R, double& w, double l,
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) M = fmax(M, __shfl_xor(M, m, 64));
   if (M > 0.0) {
-    // the scale c > 0 with (1/N) sum exp(rp^2 / 2c) = e.  phi(c) = sum exp(rp^2 / 2c) - N e
-    // is convex and decreasing, and phi >= 0 at lo = M^2 / (2 (1 + ln N)) (the bracket's
-    // left end), so Newton steps from lo rise to the root without passing it; they
-    // stop once a step is below 1e-15 of c, or after kHedgeBisect steps
-    const double Ne = static_cast<double>(N) * 2.71828182845904523536;
-    const double hi = M * M / 2.0;
-    double cc = M * M / (2.0 * (1.0 + log(static_cast<double>(N))));
+    // the scale c > 0 with (1/N) sum exp(rp^2 / 2c) = e, found in s = 1 / (2c):
+    // psi(s) = log sum exp(rp^2 s) - log(N e) is a log-sum-exp of lines, so convex and
+    // increasing (slope: the exp-weighted mean of rp^2), with psi >= 0 at
+    // s = (1 + ln N) / M^2 (c at the bracket's left end M^2 / (2 (1 + ln N))) and
+    // psi <= 0 at s = 1 / M^2 (c = M^2 / 2).  Newton steps from the first descend to
+    // the root without passing it; once a step is below 1e-8 of s the error left is
+    // of the order of its square.  Exponents are taken against M^2 (all <= 0).
+    const double M2 = M * M;
+    const double lnNe = log(static_cast<double>(N)) + 1.0;
+    const double s_lo = 1.0 / M2;
+    double sv = lnNe / M2;
     for (int it = 0; it < kHedgeBisect; ++it) {
-      const double a = act ? rp * rp / (2.0 * cc) : 0.0;
-      const double e = act ? exp(a) : 0.0;
-      const double phi = wave_sum(e) - Ne;
-      const double dphi = -wave_sum(e * a) / cc;  // d/dc of sum exp(rp^2 / 2c)
-      if (!(phi > 0.0) || !(dphi < 0.0)) break;   // at (or, by rounding, past) the root
-      const double cn = fmin(cc - phi / dphi, hi);
-      if (!(cn > cc)) break;
-      const bool done = cn - cc <= 1e-15 * cn;
-      cc = cn;
+      const double q = act ? rp * rp : 0.0;
+      const double e = act ? exp((q - M2) * sv) : 0.0;
+      const double S = wave_sum(e);
+      const double psi = M2 * sv + log(S) - lnNe;
+      const double dpsi = wave_sum(q * e) / S;
+      if (!(psi > 0.0) || !(dpsi > 0.0)) break;   // at (or, by rounding, past) the root
+      const double sn = fmax(sv - psi / dpsi, s_lo);
+      if (!(sn < sv)) break;
+      const bool done = sv - sn <= 1e-8 * sn;
+      sv = sn;
       if (done) break;
     }
+    const double cc = 1.0 / (2.0 * sv);
     const double wu = act ? (rp / cc) * exp(rp * rp / (2.0 * cc)) : 0.0;
     const double tot = wave_sum(wu);  // every lane takes part (lanes past N add 0)
     w = act ? wu / tot : 0.0;
