@@ -319,3 +319,15 @@ def test_cactus_kl_full_qwen_vocab_sampled(B):
     ref = oracle_verify(sub, delta=1.0, kl=True)
     print(compare_verify(ref, A[pick], o[pick], m[pick], "cactus-kl full"))
     assert_rel(g[pick], ref["gamma_star"], label="gamma* kl full")
+
+
+@pytest.mark.parametrize("delta", [1e-6, 40.0])
+def test_cactus_kl_extreme_budgets(B, delta):
+    """A tiny budget keeps gamma* within rounding of c (the small-x series of the divergence);
+    delta = 40 clips gamma* to 1 for every candidate with c >= e^-40."""
+    banner(f"cactus-kl delta={delta} B=8 m=6 V=9000")
+    x = sps_case(8, 6, 9000, seed=39, sigma_t=3.0, sigma_d=1.0, peak=0.0)
+    A, o, m, g = run_verify(B, x, delta=delta, kl=True)
+    ref = oracle_verify(x, delta=delta, kl=True)
+    compare_verify(ref, A, o, m, f"cactus-kl extreme {delta}")
+    assert_rel(g, ref["gamma_star"], label=f"gamma* kl {delta}")
