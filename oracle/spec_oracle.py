@@ -65,7 +65,10 @@ R23 Exact-KL Cactus: gamma* is the largest g in [c, 1] whose target h keeps
 
 from __future__ import annotations
 
+import decimal
+import functools
 import math
+import struct
 
 import numpy as np
 
@@ -75,6 +78,7 @@ __all__ = [
     "accept_ratio",
     "accept_test",
     "inverse_cdf",
+    "cdf_neighbours",
     "residual_weights",
     "acceptance_mass",
     "sps_sequence",
@@ -102,6 +106,7 @@ __all__ = [
     "hedge_exp_update",
     "censored_delays",
     "hedge_delayed_rounds_rule",
+    "hedge_censored_rounds",
 ]
 
 
@@ -181,6 +186,17 @@ def inverse_cdf(w, u: float):
     return j, float(min(x - prev, c[j] - x) / total)
 
 
+def cdf_neighbours(w, j: int):
+    """The positive-mass indices just before and just after j in the inverse-CDF order
+    (-1 where there is none): the tokens a draw whose threshold sits within rounding of
+    one of j's two CDF steps can land on instead of j (the matching rule's near-tie
+    band, reading R13)."""
+    pos = np.flatnonzero(np.asarray(w, dtype=np.float64) > 0.0)
+    before = pos[pos < j]
+    after = pos[pos > j]
+    return (int(before[-1]) if before.size else -1), (int(after[0]) if after.size else -1)
+
+
 def residual_weights(pt, pd) -> np.ndarray:
     """(p - q)+ : the part of the target the draft under-covers ([LT] §2.2, §6.4 Step 3a)."""
     return np.maximum(np.asarray(pt) - np.asarray(pd), 0.0)
@@ -224,10 +240,11 @@ def sps_sequence(pt_rows, pd_rows, tokens, r, u):
         w = residual_weights(pt_rows[A], pd_rows[A])
         if not np.sum(w) > 0.0:  # R10
             w = pt_rows[A]
-        token, margin_u = inverse_cdf(w, float(u[A]))
     else:
-        token, margin_u = inverse_cdf(pt_rows[K], float(u[K]))  # R11 bonus
-    return {"A": A, "token": token, "accept": accept, "margin_r": margin_r, "margin_u": margin_u}
+        w = pt_rows[K]  # R11 bonus
+    token, margin_u = inverse_cdf(w, float(u[A]))
+    return {"A": A, "token": token, "accept": accept, "margin_r": margin_r, "margin_u": margin_u,
+            "neighbours": cdf_neighbours(w, token)}
 
 
 def spec_verify(target_bits, draft_bits, draft_tokens, r_accept, u_resample, temperature=1.0):
@@ -246,6 +263,7 @@ def spec_verify(target_bits, draft_bits, draft_tokens, r_accept, u_resample, tem
         "accept_mask": np.zeros((B, K), dtype=bool),
         "margin_r": np.zeros((B, K)),
         "margin_u": np.zeros(B),
+        "neighbours": np.zeros((B, 2), dtype=np.int64),
     }
     for b in range(B):
         pt = softmax_t(widen_bf16(target_bits[b]), temperature)
@@ -256,6 +274,7 @@ def spec_verify(target_bits, draft_bits, draft_tokens, r_accept, u_resample, tem
         out["accept_mask"][b] = res["accept"]
         out["margin_r"][b] = res["margin_r"]
         out["margin_u"][b] = res["margin_u"]
+        out["neighbours"][b] = res["neighbours"]
     return out
 
 
@@ -272,20 +291,24 @@ def cactus_gamma_star(c: float, delta: float) -> float:
     return min(c + math.sqrt(2.0 * delta * c * (1.0 - c)), 1.0)
 
 
-def _kl_share(g: float, c: float, d: float) -> float:
-    """c * phi(g / c) with phi(t) = t ln t - t + 1 >= 0, and d = g - c given exactly.
+def _kl_context(g: float, c: float) -> decimal.Context:
+    """A decimal context for the divergence of g from c (0 < c < 1, 0 <= g <= 1).
 
-    Written as g ln(1 + d / c) - d; when d / c is small the two parts cancel,
-    so phi(1 + x) = sum_{k>=2} (-1)^k x^k / (k (k - 1)) is summed instead
-    (x^2 / 2 - x^3 / 6 + ..., through x^8: below 1e-15 of it for |x| < 0.01).
+    Each operation rounds to the context's precision P, so each logarithm
+    carries an absolute error of about 10^-P and the sum about (1 + g) 10^-P.
+    The divergence is the integral from c to g of (g - t) / (t (1 - t)) dt, so
+    it is at least (g - c)^2 / (2 m) with m the largest t (1 - t) between c and
+    g.  P is that bound's number of leading zero digits plus 40: the result then
+    keeps about 39 correct digits, far more than the float64 it is rounded to.
     """
-    if g <= 0.0:
-        return c                    # phi(0) = 1
-    x = d / c if c > 0.0 else math.inf
-    if abs(x) < 0.01:
-        return c * sum((-1.0) ** k * x ** k / (k * (k - 1)) for k in range(2, 9))
-    lr = math.log1p(x) if x < 1e10 else math.log(g) - math.log(c)
-    return g * lr - d
+    d = abs(g - c)
+    zeros = 0
+    if d > 0.0:
+        lo, hi = min(g, c), max(g, c)
+        m = 0.25 if lo <= 0.5 <= hi else max(lo * (1.0 - lo), hi * (1.0 - hi))
+        bound_log10 = 2.0 * math.log10(d) - math.log10(2.0 * m)
+        zeros = max(0, int(math.ceil(-bound_log10)))
+    return decimal.Context(prec=40 + zeros, Emin=-decimal.MAX_EMAX, Emax=decimal.MAX_EMAX)
 
 
 def cactus_kl(g: float, c: float) -> float:
@@ -293,20 +316,36 @@ def cactus_kl(g: float, c: float) -> float:
 
     The tokens other than n keep pt's proportions, so the divergence over the
     vocabulary collapses to the two-outcome one,
-    g ln(g / c) + (1 - g) ln((1 - g) / (1 - c)), with 0 ln 0 = 0 and +inf where
-    g > 0 meets c = 0.  It is evaluated as c phi(g / c) + (1 - c) phi((1 - g) / (1 - c)),
-    phi(t) = t ln t - t + 1: the same sum (the added -t + 1 terms cancel
-    between the two outcomes), but as two non-negative parts that do not
-    cancel each other.
+        g ln(g / c) + (1 - g) ln((1 - g) / (1 - c)),
+    with 0 ln 0 = 0 and +inf where g > 0 meets c = 0 (or g < 1 meets c = 1).
+    That definition is evaluated as written, in decimal arithmetic with enough
+    digits to survive the cancellation of its two terms near g = c
+    (_kl_context), and rounded once to float64.
     """
     if g > 0.0 and c <= 0.0:
         return math.inf
     if g < 1.0 and c >= 1.0:
         return math.inf
-    d = g - c
-    return _kl_share(g, c, d) + _kl_share(1.0 - g, 1.0 - c, -d)
+    if g == c:
+        return 0.0
+    ctx = _kl_context(g, c)
+    G, C = decimal.Decimal(g), decimal.Decimal(c)
+    one = decimal.Decimal(1)
+    t1 = ctx.multiply(G, ctx.ln(ctx.divide(G, C))) if g > 0.0 else decimal.Decimal(0)
+    G1, C1 = ctx.subtract(one, G), ctx.subtract(one, C)
+    t2 = ctx.multiply(G1, ctx.ln(ctx.divide(G1, C1))) if g < 1.0 else decimal.Decimal(0)
+    return float(ctx.add(t1, t2))
 
 
+def _next_double_between(lo: float, hi: float) -> float:
+    """The double halfway (in order) between two non-negative doubles lo < hi: the
+    midpoint of their bit patterns, which order as integers."""
+    a = struct.unpack("<q", struct.pack("<d", lo))[0]
+    b = struct.unpack("<q", struct.pack("<d", hi))[0]
+    return struct.unpack("<d", struct.pack("<q", (a + b) // 2))[0]
+
+
+@functools.lru_cache(maxsize=1 << 16)
 def cactus_gamma_star_kl(c: float, delta: float) -> float:
     """gamma* as the exact root of the KL constraint, without the Taylor step.
 
@@ -314,8 +353,9 @@ def cactus_gamma_star_kl(c: float, delta: float) -> float:
     clipped to [c, 1]; Key design 3 notes that this equation (x log x terms)
     has no closed form.  Read as the optimisation of Key design 1: the largest
     g in [c, 1] with cactus_kl(g, c) <= delta.  The divergence grows with g on
-    [c, 1], so bisection in float64 finds it, down to adjacent doubles; the
-    lower end (inside the budget) is returned.  Reading R23.
+    [c, 1], so bisection finds it; the bisection runs over the doubles of the
+    bracket themselves (at most 63 halvings) and ends at adjacent doubles, the
+    lower of which (inside the budget) is returned.  Reading R23.
     """
     if delta <= 0.0 or c <= 0.0:
         return c            # only g = c keeps the divergence at 0 (or finite, at c = 0)
@@ -323,7 +363,7 @@ def cactus_gamma_star_kl(c: float, delta: float) -> float:
         return 1.0          # the budget reaches the one-hot target: clipped to 1
     lo, hi = c, 1.0         # cactus_kl(lo) <= delta < cactus_kl(hi)
     while True:
-        mid = 0.5 * (lo + hi)
+        mid = _next_double_between(lo, hi)
         if mid <= lo or mid >= hi:
             return lo
         if cactus_kl(mid, c) <= delta:
@@ -376,11 +416,11 @@ def cactus_sequence(pt_rows, pd_rows, tokens, r, u, delta: float, exact_kl: bool
         w = residual_weights(h, pd_rows[A])
         if not np.sum(w) > 0.0:  # R10, with h as the position's target
             w = h
-        token, margin_u = inverse_cdf(w, float(u[A]))
     else:
-        token, margin_u = inverse_cdf(pt_rows[m], float(u[m]))
+        w = pt_rows[m]
+    token, margin_u = inverse_cdf(w, float(u[A]))
     return {"A": A, "token": token, "accept": accept, "margin_r": margin_r,
-            "margin_u": margin_u, "gamma_star": gstar}
+            "margin_u": margin_u, "gamma_star": gstar, "neighbours": cdf_neighbours(w, token)}
 
 
 def spec_cactus_verify(verifier_bits, draft_bits, draft_tokens, r_accept, u_resample,
@@ -400,6 +440,7 @@ def spec_cactus_verify(verifier_bits, draft_bits, draft_tokens, r_accept, u_resa
         "margin_r": np.zeros((B, m)),
         "margin_u": np.zeros(B),
         "gamma_star": np.zeros((B, m)),
+        "neighbours": np.zeros((B, 2), dtype=np.int64),
     }
     for b in range(B):
         pt = softmax_t(widen_bf16(verifier_bits[b]), temperature)
@@ -411,6 +452,7 @@ def spec_cactus_verify(verifier_bits, draft_bits, draft_tokens, r_accept, u_resa
         out["margin_r"][b] = res["margin_r"]
         out["margin_u"][b] = res["margin_u"]
         out["gamma_star"][b] = res["gamma_star"]
+        out["neighbours"][b] = res["neighbours"]
     return out
 
 
@@ -700,3 +742,50 @@ def hedge_delayed_rounds_rule(losses, delays, v_select, loss_scale, eta=None):
             if int(delays[t][b]) >= 0:
                 pending.append((t + 1 + int(delays[t][b]), t))
     return sel, S, W
+
+
+def hedge_censored_rounds(round_outcome, T: int, B: int, N: int, K: int, Q: int, loss_scale, v_select, eta=None):
+    """T rounds of per-sequence learning with the delay that censoring causes, run online
+    ([NB] Key design 3; reading R25): round s's loss is usable once K more tokens have
+    been verified after round s, a round verifying its accepted length plus one token
+    (none when the accepted length is negative: nothing was verified).
+
+    round_outcome(t, sel) plays round t with drafters sel [B] and returns its
+    (losses [B, N], accepted_len [B]).  Before each round's selection, the learner
+    of sequence b first counts the previous round's tokens for every queued loss,
+    applies (oldest round first) those that have reached K, then queues the previous
+    round's loss; a loss still queued Q rounds after its round is dropped (it never
+    arrives; only rounds that verified nothing can keep one waiting that long).  The
+    learner is NormalHedge (eta None) or exponential-weights Hedge with rate eta.
+    Returns (sel [T, B], state [B, N], weights [B, N], accepted_len [T, B],
+    weights before each round's draw [T, B, N]).
+    """
+    S = np.zeros((B, N))
+    W = np.full((B, N), 1.0 / N)
+    W_before = np.zeros((T, B, N))
+    sel = np.zeros((T, B), dtype=np.int64)
+    acc = np.zeros((T, B), dtype=np.int64)
+    scale = float(np.float32(loss_scale))
+    e = None if eta is None else float(np.float32(eta))
+    queued = [[] for _ in range(B)]   # per sequence: [origin round, tokens verified since]
+    losses = {}
+    for t in range(T):
+        for b in range(B):
+            if t > 0:
+                a = int(acc[t - 1, b])
+                for q in queued[b]:
+                    q[1] += a + 1 if a >= 0 else 0
+                ready = sorted(q[0] for q in queued[b] if q[1] >= K)
+                for s in ready:
+                    if e is None:
+                        S[b], W[b] = normalhedge_step(S[b], W[b], losses[s][b] * scale)
+                    else:
+                        S[b], W[b] = hedge_exp_step(S[b], losses[s][b] * scale, e)
+                queued[b] = [q for q in queued[b] if q[1] < K and q[0] > (t - 1) - Q]
+                queued[b].append([t - 1, 0])
+            W_before[t, b] = W[b]
+            sel[t, b] = normalhedge_select(W[b], float(v_select[t][b]))
+        loss_t, acc_t = round_outcome(t, sel[t].copy())
+        losses[t] = np.asarray(loss_t, dtype=np.float64)
+        acc[t] = np.asarray(acc_t, dtype=np.int64)
+    return sel, S, W, acc, W_before

@@ -187,7 +187,7 @@ def _binary_kl_scipy(g, c):
 def test_exact_kl_inverts_the_divergence():
     """For a chosen gamma in (c, 1), delta := KL((g,1-g) || (c,1-c)) must give gamma back."""
     rng = np.random.default_rng(10)
-    for _ in range(3000):
+    for _ in range(800):
         c = float(10 ** rng.uniform(-8, 0)) * 0.999
         g = c + (1.0 - c) * float(rng.uniform(0.001, 0.999))
         delta = _binary_kl_scipy(g, c)
@@ -250,7 +250,7 @@ def test_exact_kl_edges_monotone_and_corollary6():
     assert oracle.cactus_gamma_star_kl(0.7, 0.999 * -math.log(0.7)) < 1.0
     rng = np.random.default_rng(12)
     below = 0
-    for _ in range(2000):
+    for _ in range(400):
         c = float(rng.uniform(1e-6, 1.0))
         ds = np.sort(10 ** rng.uniform(-6, 0.5, 6))
         gs = [oracle.cactus_gamma_star_kl(c, float(d)) for d in ds]
@@ -260,7 +260,7 @@ def test_exact_kl_edges_monotone_and_corollary6():
             if gt <= 0.5:
                 below += 1
                 assert gt <= g * (1 + 1e-15), (c, d, gt, g)
-    assert below > 1000
+    assert below > 200
     for c in [0.05, 0.3, 0.5, 0.8]:
         ratio = (oracle.cactus_gamma_star_kl(c, 1e-10) - c) / (oracle.cactus_gamma_star(c, 1e-10) - c)
         assert abs(ratio - 1.0) < 1e-3

@@ -185,6 +185,50 @@ def test_normalhedge_weights_properties():
     np.testing.assert_allclose(w, 1.0 / 3.0, atol=1e-15)
 
 
+def test_normalhedge_weights_are_the_potential_gradient():
+    """[NH]: the weights are the gradient of the potential Phi(R) = sum_i exp([R_i]+^2 / (2c))
+    at the solved scale c, normalised.  The gradient is taken by central finite differences
+    of Phi itself, so a wrong exponent (say [R]+^2 / c), a dropped [R]+ / c factor or a
+    transposed index in the oracle's closed form fails here."""
+    rng = np.random.default_rng(31)
+    for _ in range(60):
+        N = int(rng.integers(2, 22))
+        R = rng.normal(0.3, 1.0, N) * float(10 ** rng.uniform(-1, 1))
+        rp = np.maximum(R, 0.0)
+        if not np.any(rp > 0.0):
+            continue
+        c = oracle.normalhedge_scale(rp)
+
+        def phi(x):
+            xp = np.maximum(x, 0.0)
+            return float(np.sum(np.exp(xp * xp / (2.0 * c))))
+
+        h = 1e-6 * max(1.0, float(rp.max()))
+        grad = np.zeros(N)
+        for i in range(N):
+            e = np.zeros(N)
+            e[i] = h
+            grad[i] = (phi(R + e) - phi(R - e)) / (2.0 * h)
+        grad[rp == 0.0] = 0.0  # [R_i]+ has a kink at 0: its one-sided slope there is 0
+        w = oracle.normalhedge_weights(R)
+        np.testing.assert_allclose(w, grad / grad.sum(), rtol=1e-6, atol=1e-12)
+
+
+def test_planted_normalhedge_exponent_is_caught(monkeypatch):
+    """The gradient pin catches exp([R]+^2 / c) in place of exp([R]+^2 / (2c))."""
+    import oracle.spec_oracle as so
+
+    def wrong(R):
+        rp = np.maximum(np.asarray(R, dtype=np.float64), 0.0)
+        c = so.normalhedge_scale(rp)
+        w = (rp / c) * np.exp(rp * rp / c)
+        return w / w.sum()
+
+    monkeypatch.setattr(oracle, "normalhedge_weights", wrong)
+    with pytest.raises(AssertionError):
+        test_normalhedge_weights_are_the_potential_gradient()
+
+
 def test_normalhedge_learns_best_expert_and_regret_shrinks():
     rng = np.random.default_rng(8)
     N, T = 7, 400
@@ -330,3 +374,45 @@ def test_planted_exp_sign_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(so, "hedge_exp_step", wrong)
     _, w = so.hedge_exp_step(np.array([0.0, 1.0, 2.0]), np.zeros(3), 1.0)
     assert not np.allclose(w, softmax(-np.array([0.0, 1.0, 2.0])))
+
+
+def test_censored_rounds_online_equals_censored_schedule():
+    """The online censoring rule (tokens counted as rounds complete) equals the offline rule:
+    the delays censored_delays derives from the whole history of accepted lengths, applied by
+    hedge_delayed_rounds_rule, for either learner."""
+    rng = np.random.default_rng(50)
+    for trial, eta in enumerate([None, 0.7, None, 2.0]):
+        T, B, N, K = 60, 6, 5, int(rng.integers(1, 6))
+        losses = rng.uniform(0, K, (T, B, N))
+        A = rng.integers(0, K + 1, (T, B))
+        v = rng.random((T, B), dtype=np.float32)
+
+        def outcome(t, sel):
+            return losses[t], A[t]
+
+        sel_on, S_on, W_on, acc, _ = oracle.hedge_censored_rounds(outcome, T, B, N, K, K + 1, 1.0 / K, v, eta=eta)
+        np.testing.assert_array_equal(acc, A)
+        d = oracle.censored_delays(A, K)
+        sel_off, S_off, W_off = oracle.hedge_delayed_rounds_rule(losses, d, v, 1.0 / K, eta=eta)
+        np.testing.assert_array_equal(sel_on, sel_off)
+        np.testing.assert_allclose(S_on, S_off, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(W_on, W_off, rtol=0, atol=1e-15)
+
+
+def test_censored_rounds_hand_example():
+    """K = 3; accepted lengths 2, 0, 1, 4: round 0 is complete after round 2 (1 + 2 = 3 tokens),
+    so its loss first moves the weights at round 3's selection; rounds that verify nothing
+    (accepted length -1) add no tokens."""
+    T, B, N, K = 5, 1, 2, 3
+    losses = np.zeros((T, B, N))
+    losses[0, 0] = [1.0, 0.0]
+    A = np.array([[2], [0], [1], [4], [0]])
+    v = np.full((T, B), 0.75, dtype=np.float32)
+    sel, S, W, _, _ = oracle.hedge_censored_rounds(lambda t, s: (losses[t], A[t]), T, B, N, K, K + 1, 1.0, v)
+    # uniform weights (v = 0.75 -> drafter 1) until round 0's loss lands before round 3
+    assert list(sel[:3, 0]) == [1, 1, 1] and sel[3, 0] == 1 and W[0, 1] == 1.0
+    # nothing verified: the queue never fills
+    A2 = np.array([[-1], [-1], [-1], [-1], [-1]])
+    _, S2, W2, _, _ = oracle.hedge_censored_rounds(lambda t, s: (losses[t], A2[t]), T, B, N, K, K + 1, 1.0, v)
+    np.testing.assert_array_equal(S2, 0.0)
+    np.testing.assert_array_equal(W2, 0.5)
