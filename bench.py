@@ -45,6 +45,8 @@ GAMMA_WORKLOADS = ("hedge_eval", "pool21", "small_mixed", "hedge_loop")
 
 def kernel_of(key: str) -> str:
     """The library's kernel that a workload's step launches."""
+    if key == "stream_read":
+        return "stream_read_kernel"
     if key.endswith("_tree"):
         return "tree_kernel"
     return "gamma_kernel" if key in GAMMA_WORKLOADS else "verify_kernel"
@@ -68,6 +70,68 @@ def source_hash() -> str:
             text = " ".join(text.split())
             h.update(name.encode() + b"\0" + text.encode())
     return h.hexdigest()[:16]
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_cores() -> int:
+    """The process's CPU share, at most 16 (the GPU machine's share for one GPU)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return max(1, min(16, n))
+
+
+def _oracle_sequence(job):
+    """One sequence of a workload through the oracle (all-core leg; a spawned worker)."""
+    kind, d, b, extra = job
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    import oracle
+    ld = lambda k: np.load(os.path.join(d, k + ".npy"), mmap_mode="r")
+    sl = slice(b, b + 1)
+    if kind == "sps":
+        oracle.spec_verify(ld("target")[sl], ld("draft")[sl], ld("draft_tokens")[sl], ld("r")[sl], ld("u")[sl])
+    elif kind == "cactus":
+        oracle.spec_cactus_verify(ld("target")[sl], ld("draft")[sl], ld("draft_tokens")[sl], ld("r")[sl],
+                                  ld("u")[sl], extra["delta"], exact_kl=extra["exact_kl"])
+    elif kind == "gamma":
+        K = extra["K"]
+        oracle.spec_counterfactual_gamma(ld("target")[sl, :K], ld("drafts")[:, sl], ld("traj")[sl])
+        if extra["fused"]:
+            s_ = int(ld("sel")[b])
+            oracle.spec_verify(ld("target")[sl], ld("drafts")[s_, sl], ld("draft_tokens")[sl], ld("r")[sl],
+                               ld("u")[sl])
+    elif kind == "tree":
+        K = extra["K"]
+        oracle.spec_tree_gamma(ld("target")[sl, :K], ld("drafts")[:, sl], extra["topk"])
+    return b
+
+
+def cpu_all_cores(kind: str, x: dict, extra: dict, B: int, n_seq: int, cores: int):
+    """The oracle over n_seq sequences of the batch (cycling), row-parallel on `cores` spawned
+    processes reading memory-mapped inputs.  Returns the wall seconds."""
+    import multiprocessing as mp
+    import shutil
+    import tempfile
+    d = tempfile.mkdtemp(prefix="bench_oracle_")
+    try:
+        for k, v in x.items():
+            if isinstance(v, np.ndarray):
+                np.save(os.path.join(d, k + ".npy"), v)
+        with mp.get_context("spawn").Pool(cores) as pool:
+            pool.map(_oracle_sequence, [(kind, d, b % B, extra) for b in range(cores)])  # warm the workers
+            t0 = time.perf_counter()
+            pool.map(_oracle_sequence, [(kind, d, b % B, extra) for b in range(n_seq)], chunksize=1)
+            return time.perf_counter() - t0
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
 
 
 # ---------------------------------------------------------------------------
@@ -137,6 +201,11 @@ class SpsLike(Workload):
     def launch(self, i):
         self.calls[i % len(self.calls)].launch()
 
+    def cpu_kind(self):
+        if self.delta is None:
+            return "sps", {}
+        return "cactus", {"delta": self.delta, "exact_kl": self.exact_kl}
+
     def cpu_sample(self, budget_s):
         import oracle
         x, B = self.x, self.w.B
@@ -196,6 +265,9 @@ class GammaLike(Workload):
     def launch(self, i):
         self.calls[i % len(self.calls)].launch()
 
+    def cpu_kind(self):
+        return "gamma", {"K": self.w.K, "fused": bool(self.w.fused)}
+
     def cpu_sample(self, budget_s):
         import oracle
         x, B, K = self.x, self.w.B, self.w.K
@@ -241,6 +313,9 @@ class TreeLike(GammaLike):
                       for t, d in self.copies]
         log(f"{len(self.copies)} input copies of {per / 1e6:.1f} MB")
 
+    def cpu_kind(self):
+        return "tree", {"K": self.w.K, "topk": self.topk}
+
     def cpu_sample(self, budget_s):
         import oracle
         x, B, K = self.x, self.w.B, self.w.K
@@ -256,17 +331,19 @@ class TreeLike(GammaLike):
 
 class LoopLike(GammaLike):
     """One HedgeSpec round resident on the device, replayed from a captured graph: the
-    delayed-feedback queue with NormalHedge selects each sequence's drafter, then the fused
-    spec_counterfactual_gamma evaluates all N drafters and verifies the selected one.  One
-    step = one round.  The rows are the same every round (resident; the round's rows would
-    be written into the same buffers)."""
+    learner (NormalHedge, delay from censoring counted on the device) selects each
+    sequence's drafter, then the fused spec_counterfactual_gamma evaluates all N drafters
+    and verifies the selected one.  One step = one round.  Consecutive rounds read
+    different copies of the rows (a graph per copy, >= 1 GiB in all), as fresh rows would
+    arrive, so the Infinity Cache does not serve a round from the last one's reads."""
 
     ROUNDS = 4096
 
     def __init__(self, key, w):
         import dataclasses
         super().__init__(key, dataclasses.replace(w, fused=True, draft_from="drafter0"))
-        self.desc = f"{self.w.name}, fused HedgeSpec round (queue + NormalHedge + gamma + verify) from a graph"
+        self.desc = (f"{self.w.name}, fused HedgeSpec round (censoring queue + NormalHedge + gamma + verify) "
+                     "from a graph")
 
     def setup(self, copies_min_bytes):
         import torch
@@ -277,23 +354,52 @@ class LoopLike(GammaLike):
         self.x = x = gen.make_gamma_inputs(self.w)
         i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
         f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+        t, d = _dev(torch, x["target"]), _dev(torch, x["drafts"])
+        per = 2 * (t.numel() + d.numel())
+        n = max(1, -(-copies_min_bytes // per))
+        small = {"traj": i32(x["traj"]), "draft_tokens": i32(x["draft_tokens"]), "r_accept": f32(x["r"]),
+                 "u_resample": f32(x["u"])}
+        rows = [dict(small, target=t, drafts=d)] + [dict(small, target=t.clone(), drafts=d.clone())
+                                                    for _ in range(n - 1)]
         sch = gen.hedge_schedule(self.ROUNDS, self.w.B, self.w.K)
-        self.loop = HedgeSpecLoop(_dev(torch, x["target"]), _dev(torch, x["drafts"]), i32(x["traj"]),
-                                  i32(x["draft_tokens"]), f32(x["r"]), f32(x["u"]), i32(sch["delays"]), f32(sch["v"]),
-                                  1.0 / self.w.K, self.w.temperature)
+        self.loop = HedgeSpecLoop(rows, f32(sch["v"]), 1.0 / self.w.K, self.w.temperature)
         self.loop.step()          # eager round: library set-up outside the capture
         torch.cuda.synchronize()
         self.loop.reset()
         self.loop.capture()
-        log("captured one round as a graph")
+        self.loop.reset()
+        log(f"captured a round per row copy ({n} copies of {per / 1e6:.1f} MB) as graphs")
 
     def launch(self, i):
         self.loop.replay()
 
 
+class StreamRead(Workload):
+    """The streaming-read probe over the same bytes as llama_sps's logits: a plain read with
+    the statistics phase's access pattern, the read ceiling of the verification kernels."""
+
+    def __init__(self, key, nbytes):
+        self.key, self.positions, self.algo_bytes = key, 0, nbytes
+        self.desc = f"streaming read of {nbytes / 1e6:.1f} MB (the statistics phase's access pattern)"
+
+    def setup(self, copies_min_bytes):
+        import torch
+        from speculative_sampling_verification_row_amd import binding
+        self.probe = binding.StreamProbe()
+        n = max(1, -(-copies_min_bytes // self.algo_bytes))
+        self.bufs = [torch.ones(self.algo_bytes // 2, dtype=torch.int16, device="cuda") for _ in range(n)]
+        self.grid = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+        self.out = torch.empty(self.grid * 256, dtype=torch.int32, device="cuda")
+        log(f"{n} buffers of {self.algo_bytes / 1e6:.1f} MB, grid {self.grid}")
+
+    def launch(self, i):
+        self.probe.read(self.bufs[i % len(self.bufs)], self.out, self.grid)
+
+
 def workloads():
     from speculative_sampling_verification_row_amd import inputs as gen
     return {
+        "stream_read": lambda: StreamRead("stream_read", 180589376),
         "llama_sps": lambda: SpsLike("llama_sps", gen.LLAMA_SPS),
         "qwen_cactus": lambda: SpsLike("qwen_cactus", gen.QWEN_CACTUS, delta=1.0),
         "qwen_cactus_d0": lambda: SpsLike("qwen_cactus_d0", gen.QWEN_CACTUS, delta=0.0),
@@ -434,12 +540,33 @@ def main(argv=None):
     traffic = load_traffic(wl.key, wl.algo_bytes)
 
     cpu = None
-    if args.cpu_seconds > 0:
-        log(f"oracle CPU baseline, ~{args.cpu_seconds:.0f} s")
+    if args.cpu_seconds > 0 and wl.positions > 0:
+        log(f"oracle CPU baseline, one core, ~{args.cpu_seconds:.0f} s")
         pos, secs, cpu_secs, sample = wl.cpu_sample(args.cpu_seconds)
-        cores = max(1, int(round(cpu_secs / secs)))
-        cpu = {"value": pos / secs, "unit": "positions/s", "cores": cores, "kind": "oracle",
-               "sample": f"{sample} ({pos} positions in {secs:.1f} s, float64 numpy)"}
+        cores1 = max(1, int(round(cpu_secs / secs)))
+        single = {"value": pos / secs, "unit": "positions/s", "cores": cores1,
+                  "sample": f"{sample} ({pos} positions in {secs:.1f} s, float64 numpy)"}
+        cpu = dict(single, kind="oracle", cpu_model=cpu_model())
+        ncores = host_cores()
+        if ncores > 1 and hasattr(wl, "cpu_kind"):
+            kind, extra = wl.cpu_kind()
+            per_seq = pos / wl.w.K          # sequences the one-core leg did
+            n_seq = max(ncores, int(per_seq / secs * args.cpu_seconds * ncores))
+            log(f"oracle CPU baseline, {ncores} processes, {n_seq} sequences")
+            wall = cpu_all_cores(kind, wl.x, extra, wl.w.B, n_seq, ncores)
+            cpu = {"value": n_seq * wl.w.K / wall, "unit": "positions/s", "cores": ncores, "kind": "oracle",
+                   "sample": f"{n_seq} sequences of this batch (cycling), one per task, on {ncores} spawned "
+                             f"processes in {wall:.1f} s, float64 numpy",
+                   "cpu_model": cpu_model(), "single_core": single}
+
+    if wl.key == "stream_read":
+        print(json.dumps({"metric": "streaming read bandwidth", "value": achieved, "unit": "GB/s",
+                          "n_gpus": 1, "steps": K, "ms_per_step": ms_step, "higher_is_better": True,
+                          "config": {"workload": wl.desc, "bytes_per_step": wl.algo_bytes},
+                          "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                       "frac": achieved / HBM_PEAK_GBS, "kernel": kernel_of(wl.key),
+                                       "mean_launch_ms": mean_launch_s * 1e3}}), flush=True)
+        return 0
 
     out = {
         "metric": "verified draft positions/sec at V=128k-152k",

@@ -72,6 +72,9 @@ enum {
   SPEC_ERR_HIP = -6        /* the HIP launch failed */
 };
 
+/* Learners of hedge_censored_update. */
+enum { SPEC_LEARNER_NORMALHEDGE = 0, SPEC_LEARNER_HEDGE = 1 };
+
 /* Limits checked by every call. */
 #define SPEC_MAX_B 65536       /* sequences per call */
 #define SPEC_MAX_V (1 << 20)   /* vocabulary size */
@@ -318,6 +321,40 @@ int hedge_exp_update(double* cum_loss, double* weights, const float* loss, const
 int hedge_queue_update(double* cum_regret, double* weights, double* queue_loss, int32_t* queue_due, int32_t* round,
                        const float* loss, const int32_t* delays, float loss_scale, const float* v_select,
                        int32_t* sel_out, int32_t* sel_hist, int B, int N, int Q, int T, spec_stream_t stream);
+
+/*
+ * hedge_censored_update -- one round of per-sequence learning under the delay that
+ * censoring causes ([NB] Key design 3: a round's loss can only be scored once the
+ * chunk after it is verified, so feedback arrives late; the learner keeps a queue
+ * and applies each loss once it is complete).  Round s's loss is usable once K
+ * more tokens have been verified after round s, each round verifying its
+ * accepted drafts plus one token; the tokens are counted on the device, from the
+ * accepted lengths the rounds produce, so no schedule is needed in advance.
+ * Sequence b's call at round t = round[b] (< T; later calls do nothing):
+ *   1. if t > 0, adds accepted_len[b] + 1 (round t-1's tokens; 0 if negative) to
+ *      the token count of every queued loss;
+ *   2. applies every queued loss whose count has reached K, oldest round first,
+ *      one learner step each (as hedge_update / hedge_exp_update), and frees it;
+ *   3. if t > 0, queues round t-1's loss[b][*] * loss_scale with count 0 in slot
+ *      (t-1) % Q; a loss still queued in that slot (from round t-1-Q, possible
+ *      only after rounds that verified nothing) is dropped: it never arrives;
+ *   4. draws round t's drafter: sel_out[b] = inverse CDF of weights[b] at
+ *      v_select[t B + b]; sel_hist[t B + b] = sel_out[b]; round[b] = t + 1.
+ * learner: SPEC_LEARNER_NORMALHEDGE (state = cumulative regret, as hedge_update)
+ * or SPEC_LEARNER_HEDGE (state = cumulative loss, weights exp(-eta L), as
+ * hedge_exp_update).
+ *
+ * state, weights [B][N] float64 (0 and 1/N to start); queue_loss [B][Q][N]
+ * float64 and queue_tokens [B][Q] int32 (all -1 to start); round [B] int32 (0 to
+ * start); loss [B][N] float32 and accepted_len [B] int32 (round t-1's, e.g. the
+ * outputs of a fused spec_counterfactual_gamma); v_select [T][B] float32;
+ * sel_out [B], sel_hist [T][B] int32.  1 <= K <= SPEC_MAX_K, K + 1 <= Q <= 256,
+ * 1 <= N <= SPEC_MAX_N; loss_scale and eta finite and >= 0.
+ */
+int hedge_censored_update(double* state, double* weights, double* queue_loss, int32_t* queue_tokens, int32_t* round,
+                          const float* loss, const int32_t* accepted_len, int K, int learner, float eta,
+                          float loss_scale, const float* v_select, int32_t* sel_out, int32_t* sel_hist, int B, int N,
+                          int Q, int T, spec_stream_t stream);
 
 /*
  * spec_acceptance_loss -- [NB] Key design 3's loss when the acceptance probability

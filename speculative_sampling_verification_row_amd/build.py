@@ -1,6 +1,6 @@
 """Compile libspecverify.so for gfx950 with hipcc (in-tree, no JIT cache).
 
-    python -m speculative_sampling_verification_row_amd.build [--asm]
+    python -m speculative_sampling_verification_row_amd.build [--asm OUT_DIR]
 
 Flags: -O3 for gfx950 only; packed-fp32 instructions are disabled
 (-target-feature -packed-fp32-ops) so the compiler never emits them.
@@ -19,6 +19,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libspecverify.so")
 SOURCES = [os.path.join(CSRC, "spec_verify.hip")]
+# the streaming-read probe that measures the read ceiling (a library of its own)
+PROBE_LIB = os.path.join(PKG, "libstreamprobe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "stream_probe.hip")]
 ARCH = "gfx950"
 
 
@@ -36,9 +39,17 @@ def common_flags() -> list:
 
 
 def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
-    """Compile every source into one shared library; returns its path."""
+    """Compile the verification library (and the streaming-read probe beside it); returns
+    the verification library's path."""
+    path = _build_one(SOURCES, out, defines, verbose)
+    if out == LIB:
+        _build_one(PROBE_SOURCES, PROBE_LIB, (), verbose)
+    return path
+
+
+def _build_one(sources, out, defines, verbose):
     tmp = out + ".tmp"
-    cmd = [hipcc()] + common_flags() + [f"-D{d}" for d in defines] + ["-shared"] + SOURCES + ["-o", tmp]
+    cmd = [hipcc()] + common_flags() + [f"-D{d}" for d in defines] + ["-shared"] + sources + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -62,6 +73,9 @@ def dump_asm(out_dir: str) -> None:
 
 if __name__ == "__main__":
     if "--asm" in sys.argv:
-        dump_asm(os.path.join(ROOT, "_work", "asm"))
+        i = sys.argv.index("--asm")
+        if i + 1 >= len(sys.argv):
+            raise SystemExit("--asm needs an output directory")
+        dump_asm(sys.argv[i + 1])
     else:
         print(build(verbose=True))

@@ -1955,7 +1955,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // ---------------------------------------------------------------------------
 // NormalHedge ([NH]); one wave per sequence, lane i = drafter i.
 // ---------------------------------------------------------------------------
-constexpr int kHedgeBisect = 64;  // most Newton steps for the NormalHedge scale
+constexpr int kHedgeNewtonSteps = 64;  // most Newton steps for the NormalHedge scale
 
 // One NormalHedge step of a wave, lane i = drafter i (act: i < N): with the loss l
 // (already scaled), lhat = sum_i w_i l_i, R_i += lhat - l_i, then the weights
@@ -1980,7 +1980,7 @@ __device__ __forceinline__ void normalhedge_step(double& R, double& w, double l,
     const double lnNe = log(static_cast<double>(N)) + 1.0;
     const double s_lo = 1.0 / M2;
     double sv = lnNe / M2;
-    for (int it = 0; it < kHedgeBisect; ++it) {
+    for (int it = 0; it < kHedgeNewtonSteps; ++it) {
       const double q = act ? rp * rp : 0.0;
       const double e = act ? exp((q - M2) * sv) : 0.0;
       const double S = wave_sum(e);
@@ -2041,10 +2041,21 @@ __global__ __launch_bounds__(64) void hedge_kernel(double* R, double* W, const f
   if (v != nullptr) hedge_select(wfinal, v, sel, b, N);
 }
 
-// [NB] Key design 3's other learner: exponential-weights Hedge, one wave per
-// sequence, lane i = drafter i: cumulative loss L_i += loss_i * scale, weights
-// proportional to exp(-eta L_i) (taken against min L, which leaves them unchanged),
-// then the selection as hedge_kernel's.
+// [NB] Key design 3's other learner: exponential-weights Hedge.  One step of a
+// wave, lane i = drafter i (act: i < N): cumulative loss L_i += l_i (already
+// scaled), weights proportional to exp(-eta L_i), taken against min L (which
+// leaves them unchanged).  Every lane of the wave must call it.
+__device__ __forceinline__ void hedge_exp_step(double& L, double& w, double l, double eta, bool act) {
+  L = act ? L + l : 0.0;
+  double mn = act ? L : __builtin_inf();
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) mn = fmin(mn, __shfl_xor(mn, m, 64));
+  const double u = act ? exp(-eta * (L - mn)) : 0.0;
+  const double tot = wave_sum(u);
+  w = act ? u / tot : 0.0;
+}
+
+// One wave per sequence: hedge_exp_step, then the selection as hedge_kernel's.
 __global__ __launch_bounds__(64) void hedge_exp_kernel(double* L, double* W, const float* loss, const uint8_t* has,
                                                        float scale, float eta, const float* v, int32_t* sel, int N) {
   const int b = blockIdx.x;
@@ -2053,17 +2064,13 @@ __global__ __launch_bounds__(64) void hedge_exp_kernel(double* L, double* W, con
   const int idx = b * N + i;
   double wfinal = act ? W[idx] : 0.0;
   if (has == nullptr || has[b] != 0) {
-    const double Li = act ? L[idx] + static_cast<double>(loss[idx]) * static_cast<double>(scale) : 0.0;
-    double mn = act ? Li : __builtin_inf();
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) mn = fmin(mn, __shfl_xor(mn, m, 64));
-    const double u = act ? exp(-static_cast<double>(eta) * (Li - mn)) : 0.0;
-    const double wn = u / wave_sum(u);
+    double Li = act ? L[idx] : 0.0;
+    const double l = act ? static_cast<double>(loss[idx]) * static_cast<double>(scale) : 0.0;
+    hedge_exp_step(Li, wfinal, l, static_cast<double>(eta), act);
     if (act) {
       L[idx] = Li;
-      W[idx] = wn;
+      W[idx] = wfinal;
     }
-    wfinal = act ? wn : 0.0;
   }
   if (v != nullptr) hedge_select(wfinal, v, sel, b, N);
 }
@@ -2137,6 +2144,84 @@ __global__ __launch_bounds__(64) void hedge_queue_kernel(double* R, double* W, d
     W[idx] = wi;
   }
   for (int q = i; q < Q; q += 64) gdue[q] = due[q];
+  const int pick = hedge_select(wi, v + static_cast<size_t>(t) * B, sel, b, N);
+  if (i == 0) {
+    sel_hist[static_cast<size_t>(t) * B + b] = pick;
+    round[b] = t + 1;
+  }
+}
+
+// [NB] Key design 3's delay from censoring, resident on the device: round s's
+// loss is usable once K more tokens have been verified after round s (each round
+// verifies its accepted drafts plus one token).  One wave per sequence b, lane i
+// = drafter i; slots hold the scaled loss (fp64) and the tokens verified since
+// its round (-1: free).  A call at round t (t = round[b] < T):
+//   1. when t > 0, adds round t - 1's accepted_len[b] + 1 tokens (none when it is
+//      negative: nothing was verified) to every queued loss;
+//   2. applies every queued loss that has reached K tokens, oldest round first
+//      (they all become usable now, so this is (usable round, origin) order), one
+//      learner step each, and frees their slots;
+//   3. when t > 0, queues round t - 1's loss in slot (t - 1) % Q with 0 tokens
+//      (a loss still queued there, from round t - 1 - Q, never arrives: only
+//      rounds that verified nothing can leave one that long);
+//   4. draws round t's drafter (sel[b], sel_hist[t B + b]) and sets round[b] = t + 1.
+// The learner is NormalHedge (state: cumulative regret) or exponential-weights
+// Hedge with rate eta (state: cumulative loss).
+enum : int { LEARNER_NORMALHEDGE = 0, LEARNER_HEDGE = 1 };
+
+__global__ __launch_bounds__(64) void hedge_censored_kernel(double* S, double* W, double* qloss, int32_t* qtok,
+                                                            int32_t* round, const float* loss, const int32_t* alen,
+                                                            int K, int learner, float eta, float scale, const float* v,
+                                                            int32_t* sel, int32_t* sel_hist, int B, int N, int Q, int T) {
+  const int b = blockIdx.x;
+  const int i = threadIdx.x;
+  const bool act = i < N;
+  const int idx = b * N + i;
+  const int t = round[b];
+  if (t >= T) return;  // the schedules are exhausted: nothing more
+  __shared__ int32_t tok[kMaxQueue];
+  double Si = act ? S[idx] : 0.0, wi = act ? W[idx] : 0.0;
+  int32_t* gtok = qtok + static_cast<size_t>(b) * Q;
+  double* ql = qloss + static_cast<size_t>(b) * Q * N;
+  const int add = t > 0 && alen[b] >= 0 ? alen[b] + 1 : 0;
+  for (int q = i; q < Q; q += 64) {
+    const int32_t c = gtok[q];
+    tok[q] = c >= 0 ? min(c + add, K) : -1;  // counts stop at K: reaching it is all that matters
+  }
+  __syncthreads();
+  if (t > 0) {
+    // queued slots hold rounds t - 1 - Q .. t - 2; slot q holds the latest r <= t - 2 with r % Q == q
+    const int newest = ((t - 2) % Q + Q) % Q;  // slot of round t - 2 (when t = 1 nothing is queued)
+    for (;;) {
+      int best = -1, best_age = -1;
+      for (int q = 0; q < Q; ++q) {
+        if (tok[q] < K) continue;
+        const int age = ((newest - q) % Q + Q) % Q;  // rounds before t - 2
+        if (age > best_age) {
+          best_age = age;
+          best = q;
+        }
+      }
+      if (best < 0) break;
+      const double l = act ? ql[best * N + i] : 0.0;
+      if (learner == LEARNER_NORMALHEDGE)
+        normalhedge_step(Si, wi, l, act, N);
+      else
+        hedge_exp_step(Si, wi, l, static_cast<double>(eta), act);
+      __syncthreads();
+      if (i == 0) tok[best] = -1;
+      __syncthreads();
+    }
+    const int pslot = (t - 1) % Q;
+    if (act) ql[pslot * N + i] = static_cast<double>(loss[idx]) * static_cast<double>(scale);
+    if (i == 0) tok[pslot] = 0;
+    __syncthreads();
+  }
+  if (act) {
+    S[idx] = Si;
+    W[idx] = wi;
+  }
+  for (int q = i; q < Q; q += 64) gtok[q] = tok[q];
   const int pick = hedge_select(wi, v + static_cast<size_t>(t) * B, sel, b, N);
   if (i == 0) {
     sel_hist[static_cast<size_t>(t) * B + b] = pick;
@@ -2555,6 +2640,22 @@ int hedge_queue_update(double* cum_regret, double* weights, double* queue_loss, 
   if (!(loss_scale >= 0.0f) || !isfinite(loss_scale)) return SPEC_ERR_PARAM;
   hipLaunchKernelGGL(hedge_queue_kernel, dim3(B), dim3(64), 0, stream, cum_regret, weights, queue_loss, queue_due,
                      round, loss, delays, loss_scale, v_select, sel_out, sel_hist, B, N, Q, T);
+  return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+int hedge_censored_update(double* state, double* weights, double* queue_loss, int32_t* queue_tokens, int32_t* round,
+                          const float* loss, const int32_t* accepted_len, int K, int learner, float eta,
+                          float loss_scale, const float* v_select, int32_t* sel_out, int32_t* sel_hist, int B, int N,
+                          int Q, int T, spec_stream_t stream) {
+  if (B < 1 || N < 1 || N > SPEC_MAX_N || K < 1 || K > SPEC_MAX_K || Q < K + 1 || Q > kMaxQueue || T < 1)
+    return SPEC_ERR_SHAPE;
+  if (!state || !weights || !queue_loss || !queue_tokens || !round || !loss || !accepted_len || !v_select || !sel_out ||
+      !sel_hist)
+    return SPEC_ERR_NULL;
+  if (learner != SPEC_LEARNER_NORMALHEDGE && learner != SPEC_LEARNER_HEDGE) return SPEC_ERR_PARAM;
+  if (!(loss_scale >= 0.0f) || !isfinite(loss_scale) || !(eta >= 0.0f) || !isfinite(eta)) return SPEC_ERR_PARAM;
+  hipLaunchKernelGGL(hedge_censored_kernel, dim3(B), dim3(64), 0, stream, state, weights, queue_loss, queue_tokens,
+                     round, loss, accepted_len, K, learner, eta, loss_scale, v_select, sel_out, sel_hist, B, N, Q, T);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 

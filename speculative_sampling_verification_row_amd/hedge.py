@@ -1,22 +1,21 @@
-"""Per-sequence NormalHedge or Hedge learners under delayed feedback.
+"""Per-sequence drafter learners whose delayed-feedback queue lives on the device.
 
 HedgeSpec note, Key design 3: a round's loss is only known once its chunk has
-been verified, so feedback reaches the learner late; the stochastic-setting
-reduction the note adopts keeps a feedback queue and applies each loss as it
-becomes available.  Here the loss of round s becomes usable for the selection
-of round s + 1 + d_s (d_s in [0, 2K] per sequence, supplied by the caller);
-before each selection, every usable loss is applied one at a time in order of
-(usable round, origin round).
+been verified, and the stochastic-setting reduction the note adopts keeps a
+feedback queue and applies each loss once it is available.  Both classes here
+hold the learner state, the queue and the round counters as device tensors and
+advance a round with one kernel launch; they do no queue arithmetic on the host.
 
-The learner is NormalHedge (``eta`` None) or exponential-weights Hedge with
-learning rate ``eta`` (the note names both).  A delay of -1 never arrives: a
-round whose chunk is never followed by K more verified tokens
-(``censored_delays``).
+* ``CensoredLearner`` -- the delay that censoring causes: round s's loss is
+  usable once K more tokens have been verified after round s, counted on the
+  device from the rounds' accepted lengths (``hedge_censored_update``).  The
+  learner is NormalHedge or exponential-weights Hedge (``eta``).
+* ``ScheduledLearner`` -- NormalHedge with a delay schedule given in advance
+  (``hedge_queue_update``): round s's loss usable at round s + 1 + delays[s].
 
-This module is host-side bookkeeping only: it keeps the queue, builds the
-per-step loss matrices and counts delays; every learner update and every
-selection runs in the ``hedge_update`` / ``hedge_exp_update`` kernels on the
-device, with the learner state resident there.
+Each ``step`` call is one round: it takes the previous round's loss (and, for
+the censored learner, its accepted lengths), applies whatever has become usable,
+and draws this round's drafter into ``sel`` (and ``sel_hist[t]``).
 """
 
 from __future__ import annotations
@@ -26,78 +25,74 @@ import torch
 from . import binding
 
 
-def censored_delays(accepted_len, K: int):
-    """Delays from censoring ([NB] Key design 3): round s's losses wait d rounds, d
-    the smallest with sum_{r = s+1 .. s+d} (accepted_len[r] + 1) >= K (each round
-    verifies its accepted drafts plus one token); -1 when the rounds run out.
-    accepted_len [T][B] integers (host) -> list of T lists of B ints."""
-    T = len(accepted_len)
-    B = len(accepted_len[0]) if T else 0
-    out = [[-1] * B for _ in range(T)]
-    for b in range(B):
-        for s in range(T):
-            got = 0
-            for r in range(s + 1, T):
-                got += int(accepted_len[r][b]) + 1
-                if got >= K:
-                    out[s][b] = r - s
-                    break
-    return out
-
-
-class DelayedHedge:
-    def __init__(self, B: int, N: int, loss_scale: float, eta=None, device="cuda"):
-        self.B, self.N = B, N
-        self.loss_scale = float(loss_scale)
-        self.eta = None if eta is None else float(eta)
-        self.device = device
-        # NormalHedge: cumulative regret; Hedge: cumulative loss
-        self.cum_regret = torch.zeros((B, N), dtype=torch.float64, device=device)
+class _DeviceLearner:
+    def __init__(self, B: int, N: int, T: int, Q: int, v_select, device):
+        self.B, self.N, self.T, self.Q = B, N, T, Q
+        self.v = v_select.to(torch.float32).contiguous()
+        if tuple(self.v.shape) != (T, B):
+            raise ValueError("v_select must be [T, B]")
+        self.state = torch.zeros((B, N), dtype=torch.float64, device=device)
         self.weights = torch.full((B, N), 1.0 / N, dtype=torch.float64, device=device)
-        self._pending = [[] for _ in range(B)]   # per sequence: (usable round, origin round)
-        self._loss = {}                          # origin round -> [B, N] float32 device tensor
-        self._zero = torch.zeros((B, N), dtype=torch.float32, device=device)
+        self.queue_loss = torch.zeros((B, Q, N), dtype=torch.float64, device=device)
+        self.round = torch.zeros(B, dtype=torch.int32, device=device)
+        self.sel = torch.zeros(B, dtype=torch.int32, device=device)
+        self.sel_hist = torch.zeros((T, B), dtype=torch.int32, device=device)
 
-    def push(self, origin_round: int, loss: torch.Tensor, delays) -> None:
-        """Queue round `origin_round`'s loss [B, N]; delays[b] in [0, 2K], or -1 (never)."""
-        self._loss[origin_round] = loss.to(torch.float32).contiguous()
-        for b in range(self.B):
-            if int(delays[b]) >= 0:
-                self._pending[b].append((origin_round + 1 + int(delays[b]), origin_round))
-
-    def select(self, round_: int, v: torch.Tensor) -> torch.Tensor:
-        """Apply every loss usable at `round_`, then draw the next drafter per sequence."""
-        ready = []
-        for b in range(self.B):
-            r = sorted(p for p in self._pending[b] if p[0] <= round_)
-            self._pending[b] = [p for p in self._pending[b] if p[0] > round_]
-            ready.append([s for _, s in r])
-        steps = max((len(r) for r in ready), default=0)
-        for step in range(steps):
-            rows, mask = [], []
-            for b in range(self.B):
-                if step < len(ready[b]):
-                    rows.append(self._loss[ready[b][step]][b])
-                    mask.append(1)
-                else:
-                    rows.append(self._zero[b])
-                    mask.append(0)
-            loss = torch.stack(rows)
-            has = torch.tensor(mask, dtype=torch.uint8).to(self.device, non_blocking=False)
-            self._update(loss, has)
-        still_needed = {s for b in range(self.B) for _, s in self._pending[b]}
-        for s in list(self._loss):
-            if s not in still_needed:
-                del self._loss[s]
-        no_loss = torch.zeros(self.B, dtype=torch.uint8, device=self.device)
-        return self._update(self._zero, no_loss, v.to(torch.float32))
-
-    def _update(self, loss, has, v=None):
-        if self.eta is None:
-            return binding.hedge_update(self.cum_regret, self.weights, loss, self.loss_scale, has_loss=has, v_select=v)
-        return binding.hedge_exp_update(self.cum_regret, self.weights, loss, self.loss_scale, self.eta,
-                                        has_loss=has, v_select=v)
+    def _reset_common(self) -> None:
+        """Device fills (no memset nodes), so that a graph may record them."""
+        self.state.zero_()
+        self.weights.fill_(1.0 / self.N)
+        self.queue_loss.zero_()
+        self.round.zero_()
+        self.sel.zero_()
+        self.sel_hist.zero_()
 
 
-# the NormalHedge learner under its earlier name
-DelayedNormalHedge = DelayedHedge
+class CensoredLearner(_DeviceLearner):
+    """NormalHedge (eta None) or Hedge with rate eta, under the censoring delay."""
+
+    def __init__(self, B: int, N: int, K: int, T: int, loss_scale: float, v_select, eta=None,
+                 queue_slots=None, device="cuda"):
+        Q = int(queue_slots) if queue_slots is not None else K + 1
+        super().__init__(B, N, T, Q, v_select, device)
+        self.K = K
+        self.loss_scale = float(loss_scale)
+        self.learner = binding.LEARNER_NORMALHEDGE if eta is None else binding.LEARNER_HEDGE
+        self.eta = 0.0 if eta is None else float(eta)
+        self.queue_tokens = torch.full((B, Q), -1, dtype=torch.int32, device=device)
+
+    def reset(self) -> None:
+        self._reset_common()
+        self.queue_tokens.fill_(-1)
+
+    def step(self, loss, accepted_len, stream=None) -> torch.Tensor:
+        """One round: loss [B, N] float32 and accepted_len [B] int32 of the previous round
+        (read only from the second round on).  Returns sel [B] (this round's drafters)."""
+        binding.hedge_censored_update(self.state, self.weights, self.queue_loss, self.queue_tokens, self.round,
+                                      loss, accepted_len, self.K, self.learner, self.eta, self.loss_scale, self.v,
+                                      self.sel, self.sel_hist, stream)
+        return self.sel
+
+
+class ScheduledLearner(_DeviceLearner):
+    """NormalHedge with delays fixed in advance: delays [T, B] in [-1, Q-2] (-1: never)."""
+
+    def __init__(self, B: int, N: int, K: int, T: int, loss_scale: float, v_select, delays,
+                 queue_slots=None, device="cuda"):
+        Q = int(queue_slots) if queue_slots is not None else 2 * K + 2
+        super().__init__(B, N, T, Q, v_select, device)
+        self.loss_scale = float(loss_scale)
+        self.delays = delays.to(torch.int32).contiguous()
+        if tuple(self.delays.shape) != (T, B):
+            raise ValueError("delays must be [T, B]")
+        self.queue_due = torch.full((B, Q), -1, dtype=torch.int32, device=device)
+
+    def reset(self) -> None:
+        self._reset_common()
+        self.queue_due.fill_(-1)
+
+    def step(self, loss, accepted_len=None, stream=None) -> torch.Tensor:
+        """One round: loss [B, N] float32 of the previous round.  Returns sel [B]."""
+        binding.hedge_queue_update(self.state, self.weights, self.queue_loss, self.queue_due, self.round, loss,
+                                   self.delays, self.loss_scale, self.v, self.sel, self.sel_hist, stream)
+        return self.sel

@@ -6,20 +6,28 @@ on the verified trajectory (gamma, the length estimate and its loss), and the
 loss joins the delayed-feedback queue of the learner.  Here a round is two
 launches on one stream, with every pointer fixed in advance:
 
-  hedge_queue_update         queue round t-1's loss, apply the usable ones
-                             (NormalHedge), draw sel[b] for round t
+  learner step               queue the previous round's loss, count its
+                             verified tokens, apply the losses that have become
+                             usable, draw sel[b] for this round
   spec_counterfactual_gamma  fused: gamma / estimate / loss of all N drafters
-                             and the verification of drafter sel[b]
+                             and the verification of drafter sel[b], whose
+                             accepted length the next learner step counts
 
-so a round needs nothing from the host, and ``capture()`` records one round as a
+so a round needs nothing from the host, and ``capture()`` records a round as a
 graph that ``replay()`` runs again, round after round.  Nothing is allocated
 after construction, and nothing in a round clears memory with a memset (the
 library's workspace is left zero by every call).
 
-The per-round inputs of this loop (logits, drafted tokens, uniforms) are fixed
-buffers: a caller that streams new rows writes them into those buffers between
-rounds.  Only the schedules (delays [T][B], selection uniforms [T][B]) are
-indexed by the round on the device.
+The learner's delay is censoring by default (``CensoredLearner``: a round's loss
+is usable once K more tokens are verified), or a schedule given in advance
+(``delays``, ``ScheduledLearner``).
+
+Rows.  ``rows`` is one set of round inputs (target, drafts, traj, draft_tokens,
+r_accept, u_resample) or a list of such sets; round t reads set t % len(rows),
+each with a graph of its own, so that consecutive rounds read different memory.
+The launches read the caller's tensors themselves (an input that would have to
+be copied to fit the library's layout is refused), so a caller streaming new
+rows writes them into those tensors (``inputs[j]``) between rounds.
 """
 
 from __future__ import annotations
@@ -27,60 +35,81 @@ from __future__ import annotations
 import torch
 
 from . import binding
+from .hedge import CensoredLearner, ScheduledLearner
+
+
+# a row set's keys -> the names of the fused launch's arguments
+_ROW_KEYS = {"target": "target", "drafts": "drafts", "traj": "traj_tokens", "draft_tokens": "draft_tokens",
+             "r_accept": "r_accept", "u_resample": "u_resample"}
 
 
 class HedgeSpecLoop:
-    def __init__(self, target, drafts, traj, draft_tokens, r_accept, u_resample, delays, v_select,
-                 loss_scale: float, temperature: float = 1.0, queue_slots: int | None = None):
-        N, B, K, V = drafts.shape
-        T = int(delays.shape[0])
+    def __init__(self, rows, v_select, loss_scale: float, temperature: float = 1.0, *, delays=None, eta=None,
+                 queue_slots=None):
+        sets = [rows] if isinstance(rows, dict) else list(rows)
+        if not sets:
+            raise ValueError("no rows")
+        N, B, K, V = sets[0]["drafts"].shape
+        T = int(v_select.shape[0])
         self.B, self.K, self.N, self.T = B, K, N, T
-        dev = target.device
-        self.Q = int(queue_slots) if queue_slots is not None else 2 * K + 2
-        self.loss_scale = float(loss_scale)
-        self.delays = delays.to(torch.int32).contiguous()
-        self.v = v_select.to(torch.float32).contiguous()
-        self.R = torch.zeros((B, N), dtype=torch.float64, device=dev)
-        self.W = torch.full((B, N), 1.0 / N, dtype=torch.float64, device=dev)
-        self.qloss = torch.zeros((B, self.Q, N), dtype=torch.float64, device=dev)
-        self.qdue = torch.full((B, self.Q), -1, dtype=torch.int32, device=dev)
-        self.round = torch.zeros(B, dtype=torch.int32, device=dev)
-        self.sel = torch.zeros(B, dtype=torch.int32, device=dev)
-        self.sel_hist = torch.zeros((T, B), dtype=torch.int32, device=dev)
+        dev = sets[0]["target"].device
+        if delays is None:
+            self.learner = CensoredLearner(B, N, K, T, loss_scale, v_select, eta=eta, queue_slots=queue_slots,
+                                           device=dev)
+        else:
+            if eta is not None:
+                raise ValueError("a delay schedule runs NormalHedge (hedge_queue_update)")
+            self.learner = ScheduledLearner(B, N, K, T, loss_scale, v_select, delays, queue_slots=queue_slots,
+                                            device=dev)
         self.ws = binding.make_workspace(B, K, N)
-        self.gamma_call = binding.prepare_counterfactual_gamma(
-            target, drafts, traj, temperature, sel=self.sel, draft_tokens=draft_tokens, r_accept=r_accept,
-            u_resample=u_resample, workspace=self.ws)
-        self.out = self.gamma_call.outputs
-        self._queue = binding.load().hedge_queue_update
-        self._args = (binding._ptr(self.R), binding._ptr(self.W), binding._ptr(self.qloss), binding._ptr(self.qdue),
-                      binding._ptr(self.round), binding._ptr(self.out["loss"]), binding._ptr(self.delays),
-                      self.loss_scale, binding._ptr(self.v), binding._ptr(self.sel), binding._ptr(self.sel_hist),
-                      B, N, self.Q, T)
-        self.graph = None
+        self.calls = []
+        out = None
+        for rs in sets:
+            call = binding.prepare_counterfactual_gamma(
+                rs["target"], rs["drafts"], rs["traj"], temperature, sel=self.learner.sel,
+                draft_tokens=rs["draft_tokens"], r_accept=rs["r_accept"], u_resample=rs["u_resample"],
+                workspace=self.ws, outputs=out, strict=True)
+            out = call.outputs
+            self.calls.append(call)
+        self.out = out
+        self.inputs = [{k: c.inputs[a] for k, a in _ROW_KEYS.items()} for c in self.calls]
+        self.graphs = None
+        self.t = 0
+
+    @property
+    def sel_hist(self):
+        return self.learner.sel_hist
 
     def reset(self) -> None:
         """Learner, queue and round counters back to the start (device fills, no memset)."""
-        self.R.zero_()
-        self.W.fill_(1.0 / self.N)
-        self.qloss.zero_()
-        self.qdue.fill_(-1)
-        self.round.zero_()
-        self.sel.zero_()
-        self.sel_hist.zero_()
+        self.learner.reset()
+        self.t = 0
+
+    def _round(self, j: int, stream=None) -> None:
+        self.learner.step(self.out["loss"], self.out["accepted_len"], stream)
+        self.calls[j].launch(stream)
 
     def step(self, stream=None) -> None:
         """One round, launched eagerly."""
-        st = self._queue(*self._args, binding._stream(stream))
-        if st != binding.SPEC_OK:
-            raise binding.SpecError("hedge_queue_update", st)
-        self.gamma_call.launch(stream)
+        self._round(self.t % len(self.calls), stream)
+        self.t += 1
 
     def capture(self) -> None:
-        """Record one round as a graph (on a side stream, as torch requires)."""
-        self.graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(self.graph):
-            self.step()
+        """Record a round per row set as a graph (on a side stream, as torch requires)."""
+        self.graphs = []
+        for j in range(len(self.calls)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self._round(j)
+            self.graphs.append(g)
 
     def replay(self) -> None:
-        self.graph.replay()
+        """One round from its captured graph."""
+        self.graphs[self.t % len(self.graphs)].replay()
+        self.t += 1
+
+    def check(self) -> None:
+        """Synchronise and raise binding.WorkspaceFault if a round timed out in a wait
+        between workgroups (its outputs, and the learner steps after it, are then
+        unspecified)."""
+        binding.check_workspace(self.ws, "HedgeSpecLoop")

@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["spec_verify", "spec_cactus_verify", "spec_cactus_kl_verify", "spec_counterfactual_gamma",
               "spec_tree_gamma", "spec_tree_workspace_bytes", "hedge_update", "hedge_exp_update",
-              "spec_acceptance_loss", "hedge_queue_update",
+              "spec_acceptance_loss", "hedge_queue_update", "hedge_censored_update",
               "spec_workspace_bytes", "spec_workspace_init", "spec_status_str"]:
         assert n in names, names
 
@@ -197,14 +197,16 @@ def test_hedge_exp_and_loss_validation(lib):
     assert lib.spec_acceptance_loss(None, fake(128), 2, 5, 7, None) == -1
 
 
-def test_host_censored_delays_match_oracle():
-    import numpy as np
-    import oracle
-    from speculative_sampling_verification_row_amd.hedge import censored_delays
-    rng = np.random.default_rng(5)
-    for K in [1, 3, 8]:
-        A = rng.integers(0, K + 1, (50, 4))
-        np.testing.assert_array_equal(np.array(censored_delays(A.tolist(), K)), oracle.censored_delays(A, K))
+def test_hedge_censored_validation(lib):
+    P_ = fake(4096)
+    # state, weights, qloss, qtok, round, loss, alen, K, learner, eta, scale, v, sel, hist, B, N, Q, T, stream
+    base = [P_, P_, P_, P_, P_, P_, P_, 5, 0, 0.0, 0.2, P_, P_, P_, 4, 7, 6, 100, None]  # never called as is
+    for pos, val, code in [(14, 0, -2), (15, 65, -2), (7, 0, -2), (7, 65, -2), (16, 5, -2), (16, 257, -2),
+                           (17, 0, -2), (8, 2, -3), (9, -1.0, -3), (9, float("inf"), -3), (10, float("nan"), -3),
+                           (0, None, -1), (6, None, -1), (11, None, -1), (13, None, -1)]:
+        a = list(base)
+        a[pos] = val
+        assert lib.hedge_censored_update(*a) == code, (pos, val)
 
 
 def test_hedge_queue_validation(lib):

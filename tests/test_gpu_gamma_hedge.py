@@ -8,7 +8,7 @@ import oracle
 from speculative_sampling_verification_row_amd import inputs as gen
 
 from gpu_util import banner, dev_bf16, dev_f32, dev_i32
-from parity import assert_rel, compare_verify, to_np
+from parity import assert_loss, assert_rel, compare_verify, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -56,10 +56,8 @@ def check_gamma(got, ref, seqs=None, label=""):
     l = got["loss"] if seqs is None else got["loss"][seqs]
     wg = assert_rel(g, ref["gamma"], label=f"{label} gamma")
     we = assert_rel(e, ref["est_len"], label=f"{label} est")
-    # the loss K+1-L is small when L is near K+1: compare it with the estimator's absolute error scale
-    K = ref["gamma"].shape[1]
-    assert np.all(np.abs(l - ref["loss"]) <= 1e-5 * (K + 1.0)), f"{label} loss"
-    print(f"{label}: max rel err gamma {wg:.2e} est {we:.2e}")
+    wl = assert_loss(l, ref["loss"], ref["gamma"].shape[1], label=label)
+    print(f"{label}: max rel err gamma {wg:.2e} est {we:.2e} loss {wl:.2e}")
 
 
 def test_small_mixed_full_fused(binding):
@@ -80,25 +78,6 @@ def test_gamma_shapes(binding, V, N, K):
     got = run_gamma(binding, x, fused=True)
     check_gamma(got, oracle_gamma(x), label=f"V={V}")
     compare_verify(oracle_fused_verify(x), got["accepted_len"], got["out_token"], got["accept_mask"], "fused")
-
-
-def test_hedge_eval_reduced(binding):
-    """HedgeSpec evaluation rows at V=128256, N=7, K=5 (6 of the 32 sequences)."""
-    banner("gamma hedge-eval B=6 V=128256 N=7")
-    x = gen.make_gamma_inputs(gen.HEDGE_EVAL, B=6)
-    got = run_gamma(binding, x)
-    check_gamma(got, oracle_gamma(x), label="c3")
-
-
-def test_pool21_full_launch_sampled(binding):
-    """The full 21-drafter launch (B=64, K=8, V=151936, 3.4 GB of logits); the oracle checks 3 sequences."""
-    banner("gamma pool21 full launch")
-    x = gen.make_gamma_inputs(gen.POOL21)
-    got = run_gamma(binding, x, fused=True)
-    seqs = [0, 31, 63]
-    check_gamma(got, oracle_gamma(x, seqs=seqs), seqs=seqs, label="c5")
-    ref = oracle_fused_verify(x, seqs=seqs)
-    print(compare_verify(ref, got["accepted_len"][seqs], got["out_token"][seqs], got["accept_mask"][seqs], "c5"))
 
 
 def test_identical_drafter_gives_gamma_one(binding):
@@ -124,22 +103,25 @@ def test_invalid_traj_and_sel(binding):
 
 
 def test_hedge_delayed_256_rounds(binding):
-    """NormalHedge over T=256 rounds with delays in [0, 2K], B=32 learners of N=7 drafters."""
-    banner("hedge 256 rounds")
-    from speculative_sampling_verification_row_amd.hedge import DelayedNormalHedge
+    """NormalHedge over T=256 rounds with scheduled delays in [0, 2K], B=32 learners of N=7
+    drafters; the queue lives on the device (ScheduledLearner, one launch per round)."""
+    banner("hedge 256 rounds, scheduled delays")
+    from speculative_sampling_verification_row_amd.hedge import ScheduledLearner
     T, B, N, K = 256, 32, 7, 5
     losses = gen.synthetic_losses(T, B, N, K)
     sch = gen.hedge_schedule(T, B, K)
     sel_o, R_o, W_o = oracle.hedge_delayed_rounds(losses, sch["delays"], sch["v"], 1.0 / K)
-    h = DelayedNormalHedge(B, N, 1.0 / K)
-    sel_g = np.zeros((T, B), dtype=np.int64)
+    h = ScheduledLearner(B, N, K, T, 1.0 / K, dev_f32(sch["v"]), dev_i32(sch["delays"]))
+    loss = torch.zeros((B, N), dtype=torch.float32, device="cuda")
     for t in range(T):
-        sel_g[t] = to_np(h.select(t, dev_f32(sch["v"][t])))
-        h.push(t, dev_f32(losses[t]), sch["delays"][t])
+        if t > 0:
+            loss.copy_(dev_f32(losses[t - 1]))
+        h.step(loss)
     torch.cuda.synchronize()
-    np.testing.assert_allclose(to_np(h.cum_regret), R_o, rtol=1e-9, atol=1e-12)
+    # the oracle applied every loss usable by round T-1's selection, as the device did
+    np.testing.assert_allclose(to_np(h.state), R_o, rtol=1e-9, atol=1e-12)
     np.testing.assert_allclose(to_np(h.weights), W_o, rtol=1e-9, atol=1e-12)
-    assert (sel_g == sel_o).mean() == 1.0, np.argwhere(sel_g != sel_o)[:10]
+    assert (to_np(h.sel_hist) == sel_o).mean() == 1.0, np.argwhere(to_np(h.sel_hist) != sel_o)[:10]
 
 
 def test_hedge_checkpoint_resume_bit_identical(binding):
@@ -171,26 +153,35 @@ def test_acceptance_loss_kernel(binding):
     assert got[0, 0] == 0.0 and got[1, 1] == 5.0
 
 
-@pytest.mark.parametrize("eta", [0.0, 0.3, 2.0])
-def test_hedge_exp_256_rounds_censored(binding, eta):
-    """Exponential-weights Hedge over T=256 rounds, B=32 learners of N=7 drafters, losses
-    f = sum of 1 - gamma over K=5 positions, delays from censoring (K later tokens)."""
-    banner(f"hedge-exp 256 rounds eta={eta}")
-    from speculative_sampling_verification_row_amd.hedge import DelayedHedge
+@pytest.mark.parametrize("eta", [None, 0.0, 0.3, 2.0])
+def test_hedge_256_rounds_censored(binding, eta):
+    """NormalHedge (eta None) or exponential-weights Hedge over T=256 rounds, B=32 learners of
+    N=7 drafters, losses f = sum of 1 - gamma over K=5 positions, the delay from censoring
+    counted on the device from each round's accepted length (CensoredLearner), against the
+    oracle's online rule (hedge_censored_rounds, itself pinned to the offline rule: delays from
+    censored_delays over the whole history, then the delayed queue)."""
+    banner(f"hedge 256 rounds censored eta={eta}")
+    from speculative_sampling_verification_row_amd.hedge import CensoredLearner
     T, B, N, K = 256, 32, 7, 5
     rng = np.random.default_rng(41)
     gam = rng.beta(2.0, 1.0 + np.arange(N), (T, B, K, N)).astype(np.float32)   # drafter-dependent quality
     losses = np.stack([oracle.acceptance_prob_loss(gam[t].astype(np.float64)) for t in range(T)]).astype(np.float32)
     A = rng.integers(0, K + 1, (T, B))
-    delays = oracle.censored_delays(A, K)
+    A[rng.random((T, B)) < 0.02] = -1          # a few rounds that verified nothing
     v = rng.random((T, B), dtype=np.float32)
-    sel_o, L_o, W_o = oracle.hedge_delayed_rounds_rule(losses, delays, v, 1.0 / K, eta=eta)
-    h = DelayedHedge(B, N, 1.0 / K, eta=eta)
-    sel_g = np.zeros((T, B), dtype=np.int64)
+    Q = 2 * K + 2
+    sel_o, L_o, W_o, _, _ = oracle.hedge_censored_rounds(lambda t, sel: (losses[t], A[t]), T, B, N, K, Q, 1.0 / K, v,
+                                                      eta=eta)
+    h = CensoredLearner(B, N, K, T, 1.0 / K, dev_f32(v), eta=eta, queue_slots=Q)
+    loss = torch.zeros((B, N), dtype=torch.float32, device="cuda")
+    alen = torch.zeros(B, dtype=torch.int32, device="cuda")
     for t in range(T):
-        sel_g[t] = to_np(h.select(t, dev_f32(v[t])))
-        h.push(t, dev_f32(losses[t]), delays[t])
+        if t > 0:
+            loss.copy_(dev_f32(losses[t - 1]))
+            alen.copy_(dev_i32(A[t - 1]))
+        h.step(loss, alen)
     torch.cuda.synchronize()
-    np.testing.assert_allclose(to_np(h.cum_regret), L_o, rtol=1e-12, atol=1e-12)
+    rtol = 1e-12 if eta is not None else 1e-9
+    np.testing.assert_allclose(to_np(h.state), L_o, rtol=rtol, atol=1e-12)
     np.testing.assert_allclose(to_np(h.weights), W_o, rtol=1e-9, atol=1e-12)
-    assert (sel_g == sel_o).mean() == 1.0, np.argwhere(sel_g != sel_o)[:10]
+    assert (to_np(h.sel_hist) == sel_o).mean() == 1.0, np.argwhere(to_np(h.sel_hist) != sel_o)[:10]

@@ -61,31 +61,44 @@ def test_queue_kernel_matches_oracle_queue(binding):
     assert int(to_np(rnd).min()) == T
 
 
-def small_loop(binding, T=24, seed=0):
-    from speculative_sampling_verification_row_amd.loop import HedgeSpecLoop
+def loop_rows(x):
+    return {"target": dev_bf16(x["target"]), "drafts": dev_bf16(x["drafts"]), "traj": dev_i32(x["traj"]),
+            "draft_tokens": dev_i32(x["draft_tokens"]), "r_accept": dev_f32(x["r"]), "u_resample": dev_f32(x["u"])}
+
+
+def small_inputs(seed):
     w = gen.GammaWorkload("loop", B=4, K=3, N=3, V=3000, target_sigma=2.0, sigma_range=(0.3, 2.0), fused=True,
                           draft_from="drafter0", config_id=97)
-    x = gen.make_gamma_inputs(w, seed=seed)
+    return w, gen.make_gamma_inputs(w, seed=seed)
+
+
+def small_loop(binding, T=24, seed=0, scheduled=False, sets=1):
+    from speculative_sampling_verification_row_amd.loop import HedgeSpecLoop
+    w, x = small_inputs(seed)
+    xs = [x] + [small_inputs(seed + 100 + j)[1] for j in range(sets - 1)]
     rng = np.random.default_rng(seed + 60)
     delays = rng.integers(0, 2 * w.K + 1, (T, w.B)).astype(np.int32)
     v = rng.random((T, w.B), dtype=np.float32)
-    lp = HedgeSpecLoop(dev_bf16(x["target"]), dev_bf16(x["drafts"]), dev_i32(x["traj"]), dev_i32(x["draft_tokens"]),
-                       dev_f32(x["r"]), dev_f32(x["u"]), dev_i32(delays), dev_f32(v), 1.0 / w.K)
-    return lp, x, delays, v
+    rows = [loop_rows(xi) for xi in xs]
+    lp = HedgeSpecLoop(rows if sets > 1 else rows[0], dev_f32(v), 1.0 / w.K,
+                       delays=dev_i32(delays) if scheduled else None)
+    return lp, xs, delays, v
 
 
 def snapshot(lp):
     torch.cuda.synchronize()
-    return [to_np(t).copy() for t in (lp.sel_hist, lp.R, lp.W, lp.out["gamma"], lp.out["loss"],
-                                      lp.out["accepted_len"], lp.out["out_token"])]
+    return [to_np(t).copy() for t in (lp.sel_hist, lp.learner.state, lp.learner.weights, lp.out["gamma"],
+                                      lp.out["loss"], lp.out["accepted_len"], lp.out["out_token"])]
 
 
-def test_loop_graph_replays_equal_eager_rounds(binding):
-    """A captured round replayed T times gives bit for bit what T eager rounds give, three
-    times over, with eager work and synchronisations between the replays."""
-    banner("loop graph vs eager")
+@pytest.mark.parametrize("scheduled,sets", [(False, 1), (True, 1), (False, 2)])
+def test_loop_graph_replays_equal_eager_rounds(binding, scheduled, sets):
+    """Captured rounds replayed T times give bit for bit what T eager rounds give, three
+    times over, with eager work and synchronisations between the replays (censoring or
+    scheduled delays; one row set, or two alternating row sets with a graph each)."""
+    banner(f"loop graph vs eager scheduled={scheduled} sets={sets}")
     T = 24
-    lp, _, _, _ = small_loop(binding, T)
+    lp, _, _, _ = small_loop(binding, T, scheduled=scheduled, sets=sets)
     for _ in range(T):
         lp.step()
     ref = snapshot(lp)
@@ -100,48 +113,154 @@ def test_loop_graph_replays_equal_eager_rounds(binding):
         got = snapshot(lp)
         for a, b in zip(ref, got):
             np.testing.assert_array_equal(a, b)
-        assert binding.workspace_fault(lp.ws) == 0 and int(lp.ws.count_nonzero().item()) == 0
+        lp.check()
+        assert int(lp.ws.count_nonzero().item()) == 0
         junk = torch.randn(1000, device="cuda").sum()   # the program's own eager work between replays
         torch.cuda.synchronize()
         del junk
 
 
-def test_loop_rounds_match_oracle(binding):
+def oracle_round_outcomes(x):
+    """The oracle's loss of every drafter on these rows, and its verification of each drafter
+    (accepted length, near-tie flag per sequence)."""
+    K = x["drafts"].shape[2]
+    ref = oracle.spec_counterfactual_gamma(x["target"][:, :K], x["drafts"], x["traj"])
+    N, B = x["drafts"].shape[:2]
+    A = np.zeros((N, B), dtype=np.int64)
+    tie = np.zeros((N, B), dtype=bool)
+    for i in range(N):
+        vr = oracle.spec_verify(x["target"], x["drafts"][i], x["draft_tokens"], x["r"], x["u"])
+        A[i] = vr["accepted_len"]
+        tie[i] = vr["margin_r"].min(axis=1) < 1e-6
+    return ref, A, tie
+
+
+def check_selections_follow_oracle(hist, W_rounds, v, margin=1e-4):
+    """hist [T, B] from the device; W_rounds [T, B, N] the oracle learner's weights before each
+    round's draw.  Each sequence must match the oracle's draw at every round up to the first
+    whose uniform lies within `margin` of a cumulative weight (after which the two runs may
+    part).  Returns the number of rounds compared."""
+    T, B = hist.shape
+    checked = 0
+    for b in range(B):
+        for t in range(T):
+            w = W_rounds[t, b]
+            c = np.cumsum(w) / w.sum()
+            if np.min(np.abs(c - float(v[t, b]))) <= margin:
+                break
+            assert hist[t, b] == oracle.normalhedge_select(w, float(v[t, b])), (t, b)
+            checked += 1
+    return checked
+
+
+def test_loop_censored_rounds_match_oracle(binding):
     """Every round evaluates the same rows, so every round's loss is the oracle's loss of
-    those rows; the learner's selections must follow the oracle queue wherever the drawn
-    uniform is not within 1e-4 of a cumulative weight."""
-    banner("loop vs oracle")
+    those rows and a round's accepted length is the oracle's verification of the drafter it
+    selected; the device learner, counting the censoring delay from its own accepted lengths,
+    must make the oracle learner's selections (hedge_censored_rounds)."""
+    banner("loop censored vs oracle")
     T = 24
-    lp, x, delays, v = small_loop(binding, T, seed=1)
+    lp, xs, _, v = small_loop(binding, T, seed=1)
+    x = xs[0]
+    for _ in range(T):
+        lp.step()
+    hist, S, W, g, l, A, tok = snapshot(lp)
+    ref, A_by, tie = oracle_round_outcomes(x)
+    assert not tie.any()
+    np.testing.assert_allclose(g, ref["gamma"], rtol=1e-5)
+    K, N, B = x["drafts"].shape[2], x["drafts"].shape[0], x["drafts"].shape[1]
+
+    def outcome(t, sel):
+        return ref["loss"], A_by[sel, np.arange(B)]
+
+    sel_o, S_o, W_o, acc_o, W_rounds = oracle.hedge_censored_rounds(outcome, T, B, N, K, K + 1, 1.0 / K, v)
+    checked = check_selections_follow_oracle(hist, W_rounds, v)
+    assert checked > 0.9 * T * B, checked
+    if checked == T * B:
+        np.testing.assert_array_equal(hist, sel_o)
+        np.testing.assert_allclose(S, S_o, rtol=1e-4, atol=1e-6)
+        np.testing.assert_allclose(W, W_o, rtol=1e-4, atol=1e-6)
+        np.testing.assert_array_equal(A, acc_o[T - 1])
+
+
+def test_loop_scheduled_rounds_match_oracle(binding):
+    """As above with the delay schedule given in advance (ScheduledLearner)."""
+    banner("loop scheduled vs oracle")
+    T = 24
+    lp, xs, delays, v = small_loop(binding, T, seed=1, scheduled=True)
+    x = xs[0]
     for _ in range(T):
         lp.step()
     hist, R, W, g, l, A, tok = snapshot(lp)
     K = x["drafts"].shape[2]
     ref = oracle.spec_counterfactual_gamma(x["target"][:, :K], x["drafts"], x["traj"])
-    np.testing.assert_allclose(g, ref["gamma"], rtol=1e-5)
     losses = np.broadcast_to(ref["loss"], (T,) + ref["loss"].shape)
     sel_o, R_o, W_o = oracle.hedge_delayed_rounds_rule(losses, delays, v, 1.0 / K, eta=None)
     np.testing.assert_allclose(R, R_o, rtol=1e-4, atol=1e-6)
     np.testing.assert_allclose(W, W_o, rtol=1e-4, atol=1e-6)
-    # selections: the oracle's own weights before each round decide which draws are clear
-    Rb = np.zeros_like(R_o)
-    Wb = np.full_like(W_o, 1.0 / W_o.shape[1])
-    checked = 0
-    for b in range(hist.shape[1]):
-        pending = []
-        for t in range(T):
-            ready = sorted(p for p in pending if p[0] <= t)
-            pending = [p for p in pending if p[0] > t]
-            for _, s in ready:
-                Rb[b], Wb[b] = oracle.normalhedge_step(Rb[b], Wb[b], losses[s, b] * np.float32(1.0 / K))
-            c = np.cumsum(Wb[b]) / Wb[b].sum()
-            if np.min(np.abs(c - float(v[t, b]))) > 1e-4:
-                assert hist[t, b] == oracle.normalhedge_select(Wb[b], float(v[t, b])), (t, b)
-                checked += 1
-            pending.append((t + 1 + int(delays[t, b]), t))
+    W_rounds = [oracle.hedge_delayed_rounds_rule(losses[: t + 1], delays[: t + 1], v[: t + 1], 1.0 / K)[2]
+                for t in range(T)]
+    checked = check_selections_follow_oracle(hist, np.array(W_rounds), v)
     assert checked > 0.9 * T * hist.shape[1]
     # the last round's fused verification used drafter hist[T-1][b]
     draft = np.stack([x["drafts"][hist[T - 1, b], b] for b in range(x["target"].shape[0])])
     vref = oracle.spec_verify(x["target"], draft, x["draft_tokens"], x["r"], x["u"])
     ok = vref["margin_r"].min(axis=1) >= 1e-6
     assert np.array_equal(A[ok], vref["accepted_len"][ok])
+
+
+def test_loop_reads_rows_written_between_rounds(binding):
+    """A caller streaming new rows writes them into the loop's inputs between rounds: the
+    captured round must verify and evaluate the new rows (no frozen copy)."""
+    banner("loop rows rewritten between replays")
+    T = 4
+    lp, xs, _, v = small_loop(binding, T, seed=2)
+    lp.capture()
+    lp.reset()
+    lp.replay()
+    _, x2 = small_inputs(77)
+    for key, val in loop_rows(x2).items():
+        lp.inputs[0][key].copy_(val)
+    lp.replay()
+    torch.cuda.synchronize()
+    K = x2["drafts"].shape[2]
+    ref = oracle.spec_counterfactual_gamma(x2["target"][:, :K], x2["drafts"], x2["traj"])
+    np.testing.assert_allclose(to_np(lp.out["gamma"]), ref["gamma"], rtol=1e-5)
+    sel = to_np(lp.sel_hist)[1]
+    draft = np.stack([x2["drafts"][sel[b], b] for b in range(x2["target"].shape[0])])
+    vref = oracle.spec_verify(x2["target"], draft, x2["draft_tokens"], x2["r"], x2["u"])
+    ok = vref["margin_r"].min(axis=1) >= 1e-6
+    assert np.array_equal(to_np(lp.out["accepted_len"])[ok], vref["accepted_len"][ok])
+
+
+def test_loop_refuses_inputs_it_would_copy(binding):
+    """An input the library cannot read in place (another dtype, a misaligned row base) would
+    be copied once and the copy captured: the loop refuses it instead."""
+    from speculative_sampling_verification_row_amd.loop import HedgeSpecLoop
+    w, x = small_inputs(3)
+    rows = loop_rows(x)
+    v = dev_f32(np.full((4, w.B), 0.5, dtype=np.float32))
+    with pytest.raises(ValueError):
+        HedgeSpecLoop(dict(rows, traj=rows["traj"].to(torch.int64)), v, 1.0 / w.K)
+    # rows of V = 2999 on a pitch of 3000: the drafts can be read in place, a target starting
+    # one element in (2-byte offset) cannot
+    shifted = dict(rows, target=rows["target"][..., 1:], drafts=rows["drafts"][..., :2999])
+    with pytest.raises(ValueError):
+        HedgeSpecLoop(shifted, v, 1.0 / w.K)
+    HedgeSpecLoop(dict(rows, target=rows["target"][..., :2999], drafts=rows["drafts"][..., :2999]), v, 1.0 / w.K)
+
+
+def test_fault_word_is_surfaced_and_cleared(binding):
+    """A set fault word (a wait between workgroups that timed out) makes the synchronisation
+    point raise, and leaves the workspace zeroed for reuse.  The word is set from the host."""
+    banner("fault word surfaced")
+    from speculative_sampling_verification_row_amd.binding import WorkspaceFault
+    lp, _, _, _ = small_loop(binding, 4, seed=4)
+    lp.step()
+    lp.check()
+    lp.ws[binding.FAULT_WORD_OFFSET] = 1
+    with pytest.raises(WorkspaceFault):
+        lp.check()
+    assert int(lp.ws.count_nonzero().item()) == 0
+    lp.step()
+    lp.check()

@@ -204,14 +204,14 @@ def test_full_llama_vocab_config(B):
 
 
 def test_repeat_deterministic_one_workspace(B):
-    """20 back-to-back calls on one workspace (its counters must return to zero each
-    time) give bit-identical results; then the same workspace serves another V."""
-    banner("repeat 20x on one workspace")
+    """100 back-to-back calls on one workspace (its words must return to zero each time)
+    give bit-identical results; then the same workspace serves another V."""
+    banner("repeat 100x on one workspace")
     from speculative_sampling_verification_row_amd import binding
     x = sps_case(16, 5, 9000, seed=19)
     ws = binding.make_workspace(16, 5, 1)
     first = run_verify(B, x, ws=ws)
-    for _ in range(19):
+    for _ in range(99):
         again = run_verify(B, x, ws=ws)
         for a, b in zip(first[:3], again[:3]):
             np.testing.assert_array_equal(a, b)
@@ -248,18 +248,6 @@ def test_cactus_parity(B, delta):
     compare_verify(ref, A, o, m, f"cactus {delta}")
     valid = x["draft_tokens"] >= 0
     assert_rel(g[valid], ref["gamma_star"][valid], label="gamma*")
-
-
-def test_cactus_full_qwen_vocab_sampled(B):
-    """Full launch B=64, m=20, V=151936 at delta=1.0; the oracle checks 8 sequences."""
-    banner("cactus full B=64 m=20 V=151936 delta=1")
-    x = gen.make_sps_inputs(gen.QWEN_CACTUS)
-    A, o, m, g = run_verify(B, x, delta=1.0)
-    pick = np.array([0, 9, 17, 25, 33, 41, 52, 63])
-    sub = {k: (v[pick] if isinstance(v, np.ndarray) else v) for k, v in x.items()}
-    ref = oracle_verify(sub, delta=1.0)
-    print(compare_verify(ref, A[pick], o[pick], m[pick], "cactus full"))
-    assert_rel(g[pick], ref["gamma_star"], label="gamma* full")
 
 
 # ---------------------------------------------------------------------------
@@ -307,18 +295,6 @@ def test_cactus_kl_not_below_taylor_where_corollary6_applies(B):
     sel = gt <= 0.5
     assert sel.sum() > 100
     assert np.all(gk[sel] >= gt[sel] * (1 - 1e-6))
-
-
-def test_cactus_kl_full_qwen_vocab_sampled(B):
-    """Full launch B=64, m=20, V=151936 at delta=1.0; the oracle checks 8 sequences."""
-    banner("cactus-kl full B=64 m=20 V=151936 delta=1")
-    x = gen.make_sps_inputs(gen.QWEN_CACTUS)
-    A, o, m, g = run_verify(B, x, delta=1.0, kl=True)
-    pick = np.array([0, 7, 19, 28, 36, 44, 55, 62])
-    sub = {k: (v[pick] if isinstance(v, np.ndarray) else v) for k, v in x.items()}
-    ref = oracle_verify(sub, delta=1.0, kl=True)
-    print(compare_verify(ref, A[pick], o[pick], m[pick], "cactus-kl full"))
-    assert_rel(g[pick], ref["gamma_star"], label="gamma* kl full")
 
 
 @pytest.mark.parametrize("delta", [1e-6, 40.0])
