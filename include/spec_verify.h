@@ -69,7 +69,8 @@ enum {
   SPEC_ERR_PARAM = -3,     /* temperature, delta or loss_scale not finite / out of range */
   SPEC_ERR_ALIGN = -4,     /* a logits base pointer is not 16-byte aligned */
   SPEC_ERR_WORKSPACE = -5, /* workspace NULL, misaligned or smaller than spec_workspace_bytes() */
-  SPEC_ERR_HIP = -6        /* the HIP launch failed */
+  SPEC_ERR_HIP = -6,       /* the HIP launch failed */
+  SPEC_ERR_TOO_LARGE = -7  /* spec_verify_noalloc: the call needs more than SPEC_NOALLOC_MAX_BYTES of scratch */
 };
 
 /* Learners of hedge_censored_update. */
@@ -80,6 +81,7 @@ enum { SPEC_LEARNER_NORMALHEDGE = 0, SPEC_LEARNER_HEDGE = 1 };
 #define SPEC_MAX_V (1 << 20)   /* vocabulary size */
 #define SPEC_MAX_K 64          /* draft positions per sequence */
 #define SPEC_MAX_N 64          /* drafters */
+#define SPEC_NOALLOC_MAX_BYTES (16u << 20)  /* scratch of spec_verify_noalloc, per device */
 
 /* Human-readable text for a status code (static storage). */
 const char* spec_status_str(int status);
@@ -128,6 +130,27 @@ int spec_verify(const spec_bf16* target, int64_t target_row_stride,
                 int B, int K, int V, float temperature,
                 int32_t* accepted_len, int32_t* out_token, uint8_t* accept_mask,
                 void* workspace, size_t workspace_bytes, spec_stream_t stream);
+
+/*
+ * spec_verify_noalloc -- spec_verify for callers that cannot allocate device
+ * memory: code under graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same computation, arguments, outputs and status codes as
+ * spec_verify, without the workspace: the call uses a device array inside the
+ * library (SPEC_NOALLOC_MAX_BYTES, one per device, held until the process ends)
+ * and calls no allocating routine.  Its first call on a device looks up that
+ * device's copy (hipGetSymbolAddress): make it outside graph capture.  Every
+ * call clears the part of the array it uses with a fill kernel on `stream`, then
+ * verifies.  A call whose layout (spec_workspace_bytes(B, K, 1)) exceeds the
+ * array returns SPEC_ERR_TOO_LARGE and launches nothing.  All calls on one
+ * device share the array: calls that overlap on one device (different streams
+ * or threads without ordering) race and give unspecified results.
+ */
+int spec_verify_noalloc(const spec_bf16* target, int64_t target_row_stride,
+                        const spec_bf16* draft, int64_t draft_row_stride,
+                        const int32_t* draft_tokens, const float* r_accept, const float* u_resample,
+                        int B, int K, int V, float temperature,
+                        int32_t* accepted_len, int32_t* out_token, uint8_t* accept_mask,
+                        spec_stream_t stream);
 
 /*
  * spec_cactus_verify -- Cactus constrained acceptance, m drafts per sequence.

@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 
 SPEC_OK = 0
 STATUS = {0: "SPEC_OK", -1: "SPEC_ERR_NULL", -2: "SPEC_ERR_SHAPE", -3: "SPEC_ERR_PARAM",
-          -4: "SPEC_ERR_ALIGN", -5: "SPEC_ERR_WORKSPACE", -6: "SPEC_ERR_HIP"}
+          -4: "SPEC_ERR_ALIGN", -5: "SPEC_ERR_WORKSPACE", -6: "SPEC_ERR_HIP", -7: "SPEC_ERR_TOO_LARGE"}
 LEARNER_NORMALHEDGE = 0
 LEARNER_HEDGE = 1
 FAULT_WORD_OFFSET = 12  # byte offset of the workspace's fault word

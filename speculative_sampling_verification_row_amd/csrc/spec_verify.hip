@@ -52,6 +52,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "spec_device.hpp"
 #include "spec_verify.h"
 
@@ -2460,6 +2462,29 @@ static int verify_common(const spec_bf16* target, int64_t ts, const spec_bf16* d
   return launch_flow(p, s, stream);
 }
 
+// The workspace of spec_verify_noalloc: a device array of the library, one copy
+// per device, zero when the code object is loaded.  Host code never passes its
+// name to a kernel (on the host it is only a stand-in for the symbol); each
+// device's address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kNoAllocBytes = static_cast<size_t>(SPEC_NOALLOC_MAX_BYTES);
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+static std::mutex g_scratch_mutex;
+static void* g_scratch_ptr[64] = {nullptr};
+
+// This device's copy of `scratch` (nullptr on failure).
+static void* scratch_on_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace specv
 
 using namespace specv;
@@ -2475,6 +2500,7 @@ const char* spec_status_str(int status) {
     case SPEC_ERR_ALIGN: return "logits base pointer not 16-byte aligned";
     case SPEC_ERR_WORKSPACE: return "workspace NULL, misaligned or too small";
     case SPEC_ERR_HIP: return "HIP launch failed";
+    case SPEC_ERR_TOO_LARGE: return "call needs more scratch than SPEC_NOALLOC_MAX_BYTES";
     default: return "unknown status";
   }
 }
@@ -2502,6 +2528,26 @@ int spec_verify(const spec_bf16* target, int64_t target_row_stride, const spec_b
   return verify_common(target, target_row_stride, draft, draft_row_stride, draft_tokens, r_accept, u_resample, B, K,
                        V, 0.0, 0, temperature, accepted_len, out_token, accept_mask, nullptr, workspace,
                        workspace_bytes, stream);
+}
+
+int spec_verify_noalloc(const spec_bf16* target, int64_t target_row_stride, const spec_bf16* draft,
+                        int64_t draft_row_stride, const int32_t* draft_tokens, const float* r_accept,
+                        const float* u_resample, int B, int K, int V, float temperature, int32_t* accepted_len,
+                        int32_t* out_token, uint8_t* accept_mask, spec_stream_t stream) {
+  int st = check_common(B, K, V, temperature);
+  if (st != SPEC_OK) return st;
+  const size_t need = ws_layout(make_shape(B, K, 1, V, MODE_VERIFY, 0)).total;
+  if (need > kNoAllocBytes) return SPEC_ERR_TOO_LARGE;
+  void* ws = scratch_on_current_device();
+  if (ws == nullptr) return SPEC_ERR_HIP;
+  // clear what this call reads as unpublished: the regions of its layout (a kernel
+  // node, never a memset node, so that the call can be captured in a graph)
+  const size_t words = need / 4;
+  const int grid = static_cast<int>(words / 256 + 1 < 1024 ? words / 256 + 1 : 1024);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(256), 0, stream, static_cast<uint32_t*>(ws), words);
+  if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
+  return verify_common(target, target_row_stride, draft, draft_row_stride, draft_tokens, r_accept, u_resample, B, K,
+                       V, 0.0, 0, temperature, accepted_len, out_token, accept_mask, nullptr, ws, need, stream);
 }
 
 int spec_cactus_verify(const spec_bf16* verifier, int64_t verifier_row_stride, const spec_bf16* draft,
