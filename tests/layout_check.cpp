@@ -30,8 +30,10 @@ int main() {
               const bool ok = L.flags == 0 && L.done >= 16 && L.done + 4 * static_cast<size_t>(B) <= L.part &&
                               L.part + 8 * part_words <= L.tot &&
                               L.tot + 8 * static_cast<size_t>(B) * kMaxSlices * kMaxSlices <= L.gpart &&
-                              L.gpart + 8 * gpart_words <= L.total && L.total <= total && s.nsub <= kMaxSub &&
-                              s.S <= kMaxSlices;
+                              L.gpart + 8 * gpart_words <= L.cand && L.cand <= L.pstat &&
+                              L.pstat + (mode == MODE_GAMMA ? 8 * static_cast<size_t>(kMaxGrid) * kWaves : 0) <= L.pdone &&
+                              L.pdone + (mode == MODE_GAMMA ? 4 * static_cast<size_t>(kMaxGrid) : 0) <= L.total &&
+                              L.total <= total && s.nsub <= kMaxSub && s.S <= kMaxSlices;
               if (!ok) {
                 ++bad;
                 if (bad < 10)
@@ -98,5 +100,65 @@ int main() {
           }
         }
   printf("checked %d schedules, %d violations\n", sched_checked, sched_bad);
-  return (bad || sched_bad) ? 1 : 0;
+  // gamma row chunks: every row of every group is a regular job of exactly one
+  // slot; a drafter row's target row comes earlier in the same slot's jobs; a
+  // prefix job is the target row of the group its chunk starts inside; the
+  // weights grow by each slot's share and weigh a slot by its last member
+  int chunk_bad = 0, chunk_checked = 0;
+  const int nGs[] = {1, 2, 5, 160, 512, 777};
+  const int R1s[] = {2, 3, 8, 22, 65};
+  const int Qs[] = {1, 2, 7, 51, 64, 300, 4096};
+  // (members S, compute units, dispatch slots P)
+  const int SPs[][3] = {{8, 256, 2}, {10, 256, 2}, {3, 7, 3}, {1, 1, 1}, {5, 64, 4}, {7, 256, 1}};
+  std::vector<int> regular;
+  for (const auto& sp3 : SPs) {
+    const int S = sp3[0], ncu = sp3[1], P = sp3[2];
+    for (int q = 0; q < 600; ++q) {
+      const int c_last = std::min(P - 1, ((q + 1) * S - 1) / ncu);
+      const int64_t want = P == 1 ? kShareDen : slot_share(P, c_last);
+      if (slot_weights(q + 1, S, ncu, P) - slot_weights(q, S, ncu, P) != want) {
+        ++chunk_bad;
+        if (chunk_bad < 10) printf("slot weight violation S=%d ncu=%d P=%d q=%d\n", S, ncu, P, q);
+        break;
+      }
+    }
+  }
+  for (const auto& sp3 : SPs)
+  for (int nG : nGs)
+    for (int R1 : R1s)
+      for (int Q : Qs) {
+        const int S = sp3[0], ncu = sp3[1], P = sp3[2];
+        const int64_t J = static_cast<int64_t>(nG) * R1;
+        regular.assign(J, 0);
+        bool ok = true;
+        for (int slot = 0; slot < Q && ok; ++slot) {
+          const RowChunk c = row_chunk(J, R1, Q, slot, S, ncu, P);
+          int have_target = -1;
+          for (int n = 0; n < c.njobs && ok; ++n) {
+            int q, r;
+            bool priv;
+            chunk_job(c, R1, nG, n, q, r, priv);
+            if (q < 0 || q >= nG || r < 0 || r >= R1) { ok = false; break; }
+            if (priv) {
+              ok = n == 0 && r == 0 && c.prefix && q == c.j0 / R1;
+            } else {
+              ++regular[static_cast<int64_t>(q) * R1 + r];
+            }
+            if (r == 0) have_target = q;
+            else if (have_target != q) ok = false;
+          }
+          int q, r;
+          bool priv;
+          chunk_job(c, R1, nG, c.njobs, q, r, priv);
+          if (q != nG) ok = false;
+        }
+        for (int64_t j = 0; j < J && ok; ++j) ok = regular[j] == 1;
+        ++chunk_checked;
+        if (!ok) {
+          ++chunk_bad;
+          if (chunk_bad < 10) printf("row chunk violation nG=%d R1=%d Q=%d S=%d ncu=%d P=%d\n", nG, R1, Q, S, ncu, P);
+        }
+      }
+  printf("checked %d row-chunk partitions, %d violations\n", chunk_checked, chunk_bad);
+  return (bad || sched_bad || chunk_bad) ? 1 : 0;
 }

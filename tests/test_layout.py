@@ -1,7 +1,9 @@
 """Workspace-layout invariant, checked on the host (no GPU): every region a call
 indexes with its own slice and sub-tile counts stays inside its region, regions do
 not overlap, and the layout fits in spec_workspace_bytes for every V.  (A region
-sized by V once let one call read another call's leftovers.)"""
+sized by V once let one call read another call's leftovers.)  Also the static
+schedules: the phase-0 split deals each slice once, and the gamma row chunks make
+every row a job of exactly one slot with its target row before it."""
 
 import os
 import shutil
@@ -27,3 +29,4 @@ def test_workspace_regions_fit_every_shape(tmp_path):
     assert out.returncode == 0, out.stdout + out.stderr
     assert "layouts, 0 violations" in out.stdout
     assert "schedules, 0 violations" in out.stdout
+    assert "row-chunk partitions, 0 violations" in out.stdout

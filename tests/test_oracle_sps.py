@@ -290,3 +290,14 @@ def test_spec_verify_batched_matches_sequences_and_widens_bf16():
     # bf16 widening is exact: 1.0 is 0x3F80, -2.5 is 0xC020
     np.testing.assert_array_equal(oracle.widen_bf16(np.array([0x3F80, 0xC020, 0xFF80], dtype=np.uint16)),
                                   [1.0, -2.5, -np.inf])
+
+
+def test_cdf_neighbours_hand_cases():
+    """The positive-mass tokens just before and after a drawn token, skipping zero mass."""
+    w = [0.0, 0.2, 0.0, 0.0, 0.5, 0.3, 0.0]
+    assert oracle.cdf_neighbours(w, 4) == (1, 5)
+    assert oracle.cdf_neighbours(w, 1) == (-1, 4)
+    assert oracle.cdf_neighbours(w, 5) == (4, -1)
+    # a draw whose threshold sits just below a CDF step lands on the next token: the neighbour
+    j, margin = oracle.inverse_cdf(w, 0.2 / 1.0 - 1e-9)
+    assert j == 1 and margin < 1e-6 and 4 in oracle.cdf_neighbours(w, j)
