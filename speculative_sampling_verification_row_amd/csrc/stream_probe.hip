@@ -6,7 +6,8 @@
 // persistent grid of G workgroups streams slices g, g + G, g + 2G, ... in order,
 // each lane issuing kLoads 128-bit buffer loads per slice, with the next slice's
 // loads in flight while the current one is folded -- the same two-deep pipeline,
-// load width and descriptor-based addressing as the statistics slices.
+// load width, descriptor-based addressing and non-temporal cache policy as the
+// statistics slices.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -17,6 +18,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kLoads = 8;
 constexpr uint32_t kSliceBytes = kThreads * kLoads * 16u;
+constexpr int kPolicy = 2;  // bit 1 of the buffer load's cache-policy operand: non-temporal
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_buffer(const unsigned char* base, uint64_t off,
                                                                uint64_t bytes) {
@@ -31,7 +33,7 @@ __device__ __forceinline__ void slice_issue(__amdgpu_buffer_rsrc_t r, uint4 v[kL
 #pragma unroll
   for (int t = 0; t < kLoads; ++t) {
     const auto w = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(threadIdx.x * 16u),
-                                                         static_cast<int>(t * kThreads * 16u), 0);
+                                                         static_cast<int>(t * kThreads * 16u), kPolicy);
     v[t] = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
