@@ -57,11 +57,14 @@ def log(msg: str) -> None:
 
 
 def source_hash() -> str:
-    """Hash of the kernel sources' code: comments and whitespace are left out, so that
-    only a change of the code itself makes recorded counters stale."""
+    """Hash of the verification library's sources' code: comments and whitespace are
+    left out, so that only a change of the code itself makes recorded counters stale.
+    The streaming-read probe is a library of its own and is left out too."""
     csrc = os.path.join(ROOT, "speculative_sampling_verification_row_amd", "csrc")
     h = hashlib.sha256()
     for name in sorted(os.listdir(csrc)):
+        if name.startswith("stream_probe"):
+            continue
         if name.endswith((".hip", ".hpp", ".h", ".cpp")):
             with open(os.path.join(csrc, name), "r") as f:
                 text = f.read()
