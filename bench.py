@@ -473,6 +473,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="llama_sps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline (0: skip)")
     ap.add_argument("--copies-gib", type=float, default=1.0)
+    ap.add_argument("--reps", type=int, default=200,
+                    help="launches after the timed steps for the spread of the launch duration (0: skip)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (PMC calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -541,6 +543,25 @@ def main(argv=None):
     achieved = wl.algo_bytes / mean_launch_s / 1e9
     log(f"launch ms: mean {mean_launch_s * 1e3:.4f} (HIP events around {K} back-to-back launches); "
         f"wall/step {ms_step:.4f} ms; {achieved:.0f} GB/s algorithmic; host enqueue {t_enq * 1e6 / K:.1f} us/step")
+    # The spread, after the timed steps: args.reps more launches in back-to-back
+    # batches of 10, each batch between its own pair of events (a sample is a batch's
+    # mean launch duration).
+    dist = None
+    if args.reps >= 10:
+        nb = args.reps // 10
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nb)]
+        torch.cuda.synchronize()
+        for j in range(nb):
+            evs[j][0].record()
+            for i in range(10):
+                wl.launch(args.warmup + K + 10 * j + i)
+            evs[j][1].record()
+        torch.cuda.synchronize()
+        per = np.array([a.elapsed_time(b) / 10.0 for a, b in evs])
+        dist = {"reps": nb * 10, "batch": 10, "median_ms": float(np.median(per)),
+                "p10_ms": float(np.percentile(per, 10)), "p90_ms": float(np.percentile(per, 90))}
+        log(f"launch ms over {nb * 10} more launches (batches of 10): median {dist['median_ms']:.4f} "
+            f"p10 {dist['p10_ms']:.4f} p90 {dist['p90_ms']:.4f}")
 
     traffic = load_traffic(wl.key, wl.algo_bytes)
 
@@ -570,7 +591,7 @@ def main(argv=None):
                           "config": {"workload": wl.desc, "bytes_per_step": wl.algo_bytes},
                           "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                        "frac": achieved / HBM_PEAK_GBS, "kernel": kernel_of(wl.key),
-                                       "mean_launch_ms": mean_launch_s * 1e3}}), flush=True)
+                                       "mean_launch_ms": mean_launch_s * 1e3, "launch_spread": dist}}), flush=True)
         return 0
 
     out = {
@@ -590,7 +611,8 @@ def main(argv=None):
                    "algorithmic_bytes_per_step": wl.algo_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": kernel_of(args.workload), "mean_launch_ms": mean_launch_s * 1e3},
+                     "kernel": kernel_of(args.workload), "mean_launch_ms": mean_launch_s * 1e3,
+                     "launch_spread": dist},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
