@@ -8,12 +8,14 @@ B=64 sequences x K=5 drafts over the Llama-3.1 vocabulary (V=128256, 1% of
 target rows peaked); the other workloads (--workload) are available for
 measurement and profiling.
 
-Timing: W untimed warm-up steps, then K timed steps bracketed by device
-synchronisation; every launch is also bracketed by HIP events on the launch
-stream, whose mean is the kernel duration used for the roofline.  To keep the
-256 MB Infinity Cache from serving the inputs, steps rotate over enough
-identical copies of the inputs (>= 1 GiB in total) that each launch reads
-lines no earlier launch left in the cache.
+Timing: untimed warm-up steps (at least W, and whole steps until 100 ms have
+passed, so that the GPU's clocks have settled; the JSON reports how many), then
+K timed steps back to back, bracketed by device synchronisation and by one pair
+of HIP events on the launch stream, whose span / K is the mean launch duration
+used for the roofline.  200 more launches, in batches of 10, give its spread
+(median, p10, p90).  To keep the 256 MB Infinity Cache from serving the inputs,
+steps rotate over enough identical copies of the inputs (>= 1 GiB in total)
+that each launch reads lines no earlier launch left in the cache.
 
 Output: one JSON line on stdout (progress goes to stderr) with the metric,
 the roofline of the dominant kernel (algorithmic bytes per launch / mean
@@ -470,6 +472,9 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup-ms", type=float, default=100.0,
+                    help="keep warming up (whole steps) until this much GPU time has passed, so that the "
+                         "clocks have settled before the timed steps")
     ap.add_argument("--workload", default="llama_sps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline (0: skip)")
     ap.add_argument("--copies-gib", type=float, default=1.0)
@@ -519,9 +524,16 @@ def main(argv=None):
         torch.cuda.synchronize()
         log(f"calibration copy: {args.copy_calib_mib} MiB x 3")
 
-    for i in range(args.warmup):
-        wl.launch(i)
-    torch.cuda.synchronize()
+    # Warm-up: at least W steps, and whole steps until --warmup-ms have passed: with
+    # 10 steps (0.5 ms on llama_sps) the timed steps ran while the GPU's clocks were
+    # still rising and measured 4-12% slower than the steady state.
+    warm = 0
+    t_w = time.perf_counter()
+    while warm < args.warmup or (time.perf_counter() - t_w) * 1e3 < args.warmup_ms:
+        for _ in range(max(1, args.warmup) if warm < args.warmup else 10):
+            wl.launch(warm)
+            warm += 1
+        torch.cuda.synchronize()
 
     # The K launches run back to back between one pair of HIP events recorded on the
     # launching stream (torch's current stream, which the binding launches on): the
@@ -533,7 +545,7 @@ def main(argv=None):
     t0 = time.perf_counter()
     ev0.record()
     for i in range(K):
-        wl.launch(args.warmup + i)
+        wl.launch(warm + i)
     ev1.record()
     t_enq = time.perf_counter() - t0
     torch.cuda.synchronize()
@@ -554,7 +566,7 @@ def main(argv=None):
         for j in range(nb):
             evs[j][0].record()
             for i in range(10):
-                wl.launch(args.warmup + K + 10 * j + i)
+                wl.launch(warm + K + 10 * j + i)
             evs[j][1].record()
         torch.cuda.synchronize()
         per = np.array([a.elapsed_time(b) / 10.0 for a, b in evs])
@@ -600,7 +612,7 @@ def main(argv=None):
         "unit": "positions/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": warm,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
