@@ -104,7 +104,7 @@ struct Params {
   int B, K, N, V;
   float c;  // log2(e) / T
   double delta;
-  int kl_exact;  // Cactus gamma*: 0 the Taylor form, 1 the exact root of the KL budget (verify_kernel<true>)
+  int kl_exact;  // Cactus gamma*: 0 the Taylor form, 1 the exact root of the KL budget (verify_kernel<true, *>)
   int mode;
   int fused;
   // schedule
@@ -855,16 +855,32 @@ __device__ __forceinline__ int crossing_slice(double t, double u, double& x_rel)
 
 constexpr int kSliceSub = kTilesPerSlice * kWaves;  // 512-token sub-tiles of a slice
 
-// Draw unit x publishes its slice total (the wave scan of its sub-tile masses
-// L.subsum[0..kSliceSub)) to each unit y of its sequence as word tot[b][y][x],
-// reads the words addressed to it (clearing them: it is their only reader), and
-// returns the crossing slice of the sequence's draw (-1 for none).
+// Draw unit x of a sequence takes slices x, x + P1, x + 2 P1, ... < S (P1 the
+// sequence's draw units: S when the grid holds a unit per slice, fewer
+// otherwise, so that no workgroup runs two units one after the other).
+__device__ __forceinline__ int unit_slices(const Params& p, int x) {
+  return p.P1 == p.S ? 1 : (p.S - x + p.P1 - 1) / p.P1;
+}
+// The draw unit that takes slice s.
+__device__ __forceinline__ int slice_unit(const Params& p, int s) { return p.P1 == p.S ? s : s % p.P1; }
+
+// Draw unit x publishes the total of each of its slices s (the wave scan of the
+// slice's sub-tile masses, L.subsum[j kSliceSub ..] for its j-th slice) to each
+// unit y of its sequence as word tot[b][y][s], reads the S words addressed to it
+// (clearing them: it is their only reader), and returns the crossing slice of
+// the sequence's draw (-1 for none).
+template <bool MULTI = false>
 __device__ __forceinline__ int exchange_totals(const Params& p, int b, int x, double u, double& x_rel, Lds& L) {
   const int tid = threadIdx.x;
   unsigned long long* tw = p.tot + static_cast<size_t>(b) * kMaxSlices * kMaxSlices;
   if (tid < 64) {  // wave 0
-    const double T = readlane_f64(wave_incl_scan(tid < kSliceSub ? L.subsum[tid] : 0.0), 63);
-    if (tid < p.S) st_agent_u64(tw + tid * kMaxSlices + x, pack_f64(T));
+    auto publish = [&](int j) {
+      const double T = readlane_f64(wave_incl_scan(tid < kSliceSub ? L.subsum[j * kSliceSub + tid] : 0.0), 63);
+      if (tid < p.P1) st_agent_u64(tw + tid * kMaxSlices + x + j * p.P1, pack_f64(T));
+    };
+    publish(0);
+    if (MULTI)
+      for (int j = 1; j < unit_slices(p, x); ++j) publish(j);
   }
   if (tid < p.S) {
     unsigned long long* src = tw + x * kMaxSlices + tid;
@@ -896,7 +912,9 @@ __device__ __forceinline__ double kl_positions(const Params& p, int b, bool writ
 
 // With KL (exact-KL Cactus, delta > 0), the residual's gamma* is found here, while
 // the slice's loads are in flight, and completes d.w.
-template <int MODE, bool SPECIAL, bool KL = false>
+// MULTI: the unit may take several slices (P1 < S); without it, slice x only,
+// in straight-line code.
+template <int MODE, bool SPECIAL, bool KL = false, bool MULTI = false>
 __device__ __forceinline__ int draw_slice(const Params& p, int b, int x, Decision& d, Lds& L) {
   const int tid = threadIdx.x, wave = wave_id();
   const uint16_t* trow = target_row(p, b, d.draw_row);
@@ -904,45 +922,63 @@ __device__ __forceinline__ int draw_slice(const Params& p, int b, int x, Decisio
   const uint32_t row_bytes = static_cast<uint32_t>((p.V + kVec - 1) / kVec) * 16u;
   const __amdgpu_buffer_rsrc_t tr = row_buffer(trow, row_bytes);
   const __amdgpu_buffer_rsrc_t dr = row_buffer(drow, row_bytes);
-  const int c0 = x * kTilesPerSlice * kThreads + tid;  // this lane's chunk of the slice's first tile
-  // chunks past the row's end read zero and weigh nothing (chunk_weights)
+  // the unit's slices one after another; the last one's rows stay in registers
+  const int ns = MULTI ? unit_slices(p, x) : 1;
   uint4 vt[kTilesPerSlice], vd[kTilesPerSlice];
+  auto slice_masses = [&](int j) {
+    const int sl = x + j * p.P1;
+    const int c0 = sl * kTilesPerSlice * kThreads + tid;  // this lane's chunk of the slice's first tile
+    // chunks past the row's end read zero and weigh nothing (chunk_weights)
 #pragma unroll
-  for (int q = 0; q < kTilesPerSlice; ++q) {
-    const uint32_t uo = static_cast<uint32_t>((x * kTilesPerSlice + q) * kThreads) * 16u;
-    vt[q] = buffer_load16(tr, tid * 16u, uo);
-    vd[q] = MODE == W_RESID ? buffer_load16(dr, tid * 16u, uo) : make_uint4(0u, 0u, 0u, 0u);
-  }
-  if (KL && MODE == W_RESID && SPECIAL) {
-    const double gsA = kl_positions(p, b, x == 0, d.A, L);
-    const double ctA = L.dl.ct[d.A];
-    d.w.s_scale = ctA < 1.0 ? (1.0 - gsA) / (1.0 - ctA) : 0.0;
-    d.w.hn = gsA * L.m.rs[d.A];
-  }
+    for (int q = 0; q < kTilesPerSlice; ++q) {
+      const uint32_t uo = static_cast<uint32_t>((sl * kTilesPerSlice + q) * kThreads) * 16u;
+      vt[q] = buffer_load16(tr, tid * 16u, uo);
+      vd[q] = MODE == W_RESID ? buffer_load16(dr, tid * 16u, uo) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    if (KL && MODE == W_RESID && SPECIAL && j == 0) {
+      const double gsA = kl_positions(p, b, x == 0, d.A, L);
+      const double ctA = L.dl.ct[d.A];
+      d.w.s_scale = ctA < 1.0 ? (1.0 - gsA) / (1.0 - ctA) : 0.0;
+      d.w.hn = gsA * L.m.rs[d.A];
+    }
 #pragma unroll
-  for (int q = 0; q < kTilesPerSlice; ++q) {
-    double wv[8];
-    const double ls = chunk_weights<MODE, SPECIAL>(vt[q], vd[q], c0 + q * kThreads, p.V, d.w, wv);
-    const double incl = wave_incl_scan(ls);
-    if (lane_id() == 63) L.subsum[q * kWaves + wave] = incl;
-  }
+    for (int q = 0; q < kTilesPerSlice; ++q) {
+      double wv[8];
+      const double ls = chunk_weights<MODE, SPECIAL>(vt[q], vd[q], c0 + q * kThreads, p.V, d.w, wv);
+      const double incl = wave_incl_scan(ls);
+      if (lane_id() == 63) L.subsum[j * kSliceSub + q * kWaves + wave] = incl;
+    }
+  };
+  // the first slice as straight-line code (the only one when the grid holds a
+  // unit per slice), the others, if any, in a loop
+  slice_masses(0);
+  if (MULTI)
+    for (int j = 1; j < ns; ++j) slice_masses(j);
   __syncthreads();
   double x_rel = 0.0;
-  const int xs = exchange_totals(p, b, x, static_cast<double>(p.u[b * (p.K + 1) + d.draw_row]), x_rel, L);
-  if (xs != x) return xs;
-  // this slice's total is positive, so one of its sub-tiles has mass; the scan is
-  // the one that formed the total
-  const double m = lane_id() < kSliceSub ? L.subsum[lane_id()] : 0.0;
+  const int xs = exchange_totals<MULTI>(p, b, x, static_cast<double>(p.u[b * (p.K + 1) + d.draw_row]), x_rel, L);
+  if (xs < 0 || (MULTI ? slice_unit(p, xs) : xs) != x) return xs;
+  // the crossing slice is this unit's j-th; its total is positive, so one of its
+  // sub-tiles has mass; the scan is the one that formed the total
+  const int js = (xs - x) / p.P1;
+  const double m = lane_id() < kSliceSub ? L.subsum[js * kSliceSub + lane_id()] : 0.0;
   const int ss = wave_crossing(m, wave_incl_scan(m), x_rel);
   const int qs = ss / kWaves;
   if (wave == ss - qs * kWaves) {
+    const int c0 = xs * kTilesPerSlice * kThreads + tid;
     uint4 ct = vt[0], cd = vd[0];
+    if (!MULTI || js == ns - 1) {  // the last slice: its rows are still in registers
 #pragma unroll
-    for (int q = 1; q < kTilesPerSlice; ++q)
-      if (q == qs) {
-        ct = vt[q];
-        cd = vd[q];
-      }
+      for (int q = 1; q < kTilesPerSlice; ++q)
+        if (q == qs) {
+          ct = vt[q];
+          cd = vd[q];
+        }
+    } else {  // an earlier slice: its crossing tile is read again
+      const uint32_t uo = static_cast<uint32_t>((xs * kTilesPerSlice + qs) * kThreads) * 16u;
+      ct = buffer_load16(tr, tid * 16u, uo);
+      cd = MODE == W_RESID ? buffer_load16(dr, tid * 16u, uo) : make_uint4(0u, 0u, 0u, 0u);
+    }
     const int tok = subtile_token<MODE, SPECIAL>(ct, cd, c0 + qs * kThreads, p.V, d.w, x_rel);
     if (lane_id() == 0) {
       p.accepted_len[b] = tok >= 0 ? d.A : -1;
@@ -979,8 +1015,9 @@ __device__ __forceinline__ void target_h_draw(const Params& p, int b, const Deci
 // Draw unit x of sequence b.  Unit 0 also writes the per-position outputs, the
 // outputs of a sequence with no valid draw, and the outputs of a draw with no
 // mass.  `pre_n`: the drafted token of position threadIdx.x, loaded ahead of
-// time, or kNoToken.
-template <bool KL = false>
+// time, or kNoToken.  MULTI: units of several slices (a kernel instance of its
+// own, so that the other launches keep the single-slice code alone).
+template <bool KL = false, bool MULTI = false>
 __device__ __forceinline__ void unit_draw(const Params& p, int b, int x, int pre_n, Lds& L) {
   decide<KL>(p, b, x == 0, pre_n, L);
   Decision d = L.dl.d;
@@ -989,18 +1026,18 @@ __device__ __forceinline__ void unit_draw(const Params& p, int b, int x, int pre
   int xs;
   if (d.A < 0) {
     // no draw: the totals are still exchanged, so that unit 0 knows when to clear
-    if (threadIdx.x < kSliceSub) L.subsum[threadIdx.x] = 0.0;
+    for (int q = threadIdx.x; q < (MULTI ? unit_slices(p, x) : 1) * kSliceSub; q += kThreads) L.subsum[q] = 0.0;
     __syncthreads();
     double x_rel = 0.0;
-    xs = exchange_totals(p, b, x, 0.0, x_rel, L);
+    xs = exchange_totals<MULTI>(p, b, x, 0.0, x_rel, L);
     if (x == 0 && threadIdx.x == 0) {
       p.accepted_len[b] = -1;
       p.out_token[b] = -1;
     }
   } else {
-    xs = !d.pair       ? draw_slice<W_TARGET, false>(p, b, x, d, L)
-         : d.w.special ? draw_slice<W_RESID, true, KL>(p, b, x, d, L)
-                       : draw_slice<W_RESID, false>(p, b, x, d, L);
+    xs = !d.pair       ? draw_slice<W_TARGET, false, false, MULTI>(p, b, x, d, L)
+         : d.w.special ? draw_slice<W_RESID, true, KL, MULTI>(p, b, x, d, L)
+                       : draw_slice<W_RESID, false, false, MULTI>(p, b, x, d, L);
     if (xs < 0 && x == 0) {
       if (d.w.special)
         target_h_draw<true>(p, b, d, L);
@@ -1008,7 +1045,9 @@ __device__ __forceinline__ void unit_draw(const Params& p, int b, int x, int pre
         target_h_draw<false>(p, b, d, L);
     }
   }
-  finish_sequence(p, b, (xs < 0 ? 0 : xs) == x, L);
+  // the unit that holds the crossing slice (unit 0 when there is none) has read
+  // every unit's totals
+  finish_sequence(p, b, (xs < 0 ? 0 : MULTI ? slice_unit(p, xs) : xs) == x, L);
 }
 
 // ---------------------------------------------------------------------------
@@ -1469,9 +1508,10 @@ __device__ __forceinline__ void unit_estimate(const Params& p, int b, Lds& L) {
 
 __device__ __forceinline__ bool is_draw_unit(const Params& p, int u) { return p.P1 > 0; }
 
+template <bool MULTI>
 __device__ __forceinline__ void run_unit1(const Params& p, int u, int pre_n, Lds& L) {
   const int b = u / p.P1;
-  unit_draw(p, b, u - b * p.P1, pre_n, L);
+  unit_draw<false, MULTI>(p, b, u - b * p.P1, pre_n, L);
 }
 
 __device__ __forceinline__ void run_unit2(const Params& p, int v, Lds& L) { unit_estimate(p, v / p.P2, L); }
@@ -1574,6 +1614,8 @@ union KernelLds {
   GammaLds gamma;
 };
 
+// MULTI: draw units of several slices (fused calls whose B S exceeds the grid).
+template <bool MULTI>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gamma_kernel(Params p) {
   __shared__ KernelLds KL;
   Lds& L = KL.units;
@@ -1588,7 +1630,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   static_phase(p, G, g);
   for (int u = g; u < T1; u += G) {
     __syncthreads();
-    run_unit1(p, u, u == g ? pre_n : kNoToken, L);
+    run_unit1<MULTI>(p, u, u == g ? pre_n : kNoToken, L);
   }
   const int T2 = p.B * p.P2;
   for (int v = g; v < T2; v += G) {
@@ -1601,8 +1643,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // g, g + G, ...  It is the gamma kernel without the groups and the estimator, so
 // it holds less LDS and fewer registers.
 // KL: Cactus gamma* as the exact root of the KL budget (spec_cactus_kl_verify), a
-// separate instance so that the other calls keep the leaner code.
-template <bool KL>
+// separate instance so that the other calls keep the leaner code.  MULTI: draw
+// units of several slices, for calls whose B S exceeds the grid (an instance of
+// its own too: the single-slice code measured 1% slower beside it).
+template <bool KL, bool MULTI>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void verify_kernel(Params p) {
   __shared__ Lds L;
   const int G = gridDim.x, g = blockIdx.x;
@@ -1615,7 +1659,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int u = g; u < T1; u += G) {
     __syncthreads();
     const int b = u / p.P1;
-    unit_draw<KL>(p, b, u - b * p.P1, u == g ? pre_n : kNoToken, L);
+    unit_draw<KL, MULTI>(p, b, u - b * p.P1, u == g ? pre_n : kNoToken, L);
   }
 }
 
@@ -2457,7 +2501,7 @@ static int compute_units() {
 
 template <class Kernel>
 static int resident_workgroups(Kernel kernel, int which) {
-  static int cache[4][64] = {{0}};
+  static int cache[8][64] = {{0}};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (dev >= 0 && dev < 64 && cache[which][dev] > 0) return cache[which][dev];
@@ -2491,9 +2535,9 @@ static int launch_flow(Params& p, const Shape& s, hipStream_t stream) {
   const bool verify = s.mode == MODE_VERIFY;
   const bool tree = s.mode == MODE_TREE;
   int grid = tree     ? resident_workgroups(tree_kernel, 3)
-             : verify ? (p.kl_exact ? resident_workgroups(verify_kernel<true>, 2)
-                                    : resident_workgroups(verify_kernel<false>, 0))
-                      : resident_workgroups(gamma_kernel, 1);
+             : verify ? (p.kl_exact ? resident_workgroups(verify_kernel<true, false>, 2)
+                                    : resident_workgroups(verify_kernel<false, false>, 0))
+                      : resident_workgroups(gamma_kernel<false>, 1);
   if (grid <= 0) return SPEC_ERR_HIP;
   const int ncu = compute_units();
   const int slots = ncu > 0 && grid % ncu == 0 ? grid / ncu : 1;
@@ -2507,20 +2551,33 @@ static int launch_flow(Params& p, const Shape& s, hipStream_t stream) {
   if (tree_units > want) want = tree_units;
   if (grid > want) grid = static_cast<int>(want);
   // every workgroup is resident at once (the schedule's waits rely on it); a gamma
-  // slot and a sequence's draw units need S workgroups at once
-  if ((s.mode == MODE_GAMMA || s.P1 > 0) && grid < s.S) return SPEC_ERR_SHAPE;
+  // slot needs S workgroups at once
+  if (s.mode == MODE_GAMMA && grid < s.S) return SPEC_ERR_SHAPE;
   if (grid > kMaxGrid) grid = kMaxGrid;  // the workspace's per-workgroup regions are sized for it
   plan_units(p, s);
+  // draw units: one per slice of a sequence when the grid holds them all; else as
+  // many per sequence as the grid holds (each taking several slices), so that no
+  // workgroup runs a second draw unit after its first
+  const bool multi = s.P1 > 0 && static_cast<int64_t>(s.B) * s.P1 > grid;
+  if (multi) {
+    // the instance with units of several slices holds as many workgroups
+    const int g2 = verify ? (p.kl_exact ? resident_workgroups(verify_kernel<true, true>, 6)
+                                        : resident_workgroups(verify_kernel<false, true>, 4))
+                          : resident_workgroups(gamma_kernel<true>, 5);
+    if (g2 <= 0) return SPEC_ERR_HIP;
+    if (g2 < grid) grid = g2;
+    if (s.mode == MODE_GAMMA && grid < s.S) return SPEC_ERR_SHAPE;
+    p.P1 = grid / s.B > 1 ? grid / s.B : 1;
+    if (p.P1 > s.P1) p.P1 = s.P1;
+    if (s.mode != MODE_VERIFY) p.nlast = p.P1 + p.P2;
+  }
   p.ncu = ncu;
   p.slots = slots;  // make_split weights the slots only when the grid is all of them
-  if (tree)
-    hipLaunchKernelGGL(tree_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
-  else if (verify && p.kl_exact)
-    hipLaunchKernelGGL(verify_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, p);
-  else if (verify)
-    hipLaunchKernelGGL(verify_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(gamma_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
+  void (*kernel)(Params) = tree                  ? tree_kernel
+                           : verify && p.kl_exact ? (multi ? verify_kernel<true, true> : verify_kernel<true, false>)
+                           : verify               ? (multi ? verify_kernel<false, true> : verify_kernel<false, false>)
+                                                  : (multi ? gamma_kernel<true> : gamma_kernel<false>);
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 

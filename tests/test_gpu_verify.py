@@ -203,6 +203,28 @@ def test_full_llama_vocab_config(B):
     print(compare_verify(ref, A, o, m, "full c2"))
 
 
+@pytest.mark.parametrize("Bn,V,delta", [(16, 1 << 20, None), (64, 400000, None), (64, 400000, 0.5)])
+def test_units_of_several_slices(B, Bn, V, delta):
+    """More sequence slices than the grid has workgroups (B S > 512 on MI355X): a
+    sequence gets fewer draw units than slices, each streaming several slices (V = 2^20:
+    S = 64, 16 sequences, units of 2 slices; V = 400,000: S = 25, 64 sequences, units of
+    3-4 slices), and a crossing in a unit's earlier slice is found from a re-read tile.
+    Every sequence is checked, for SpS and for Cactus."""
+    banner(f"several slices per draw unit B={Bn} V={V} delta={delta}")
+    x = sps_case(Bn, 3, V, seed=31 + Bn, peak=0.0)
+    A, o, m, g = run_verify(B, x, delta=delta)
+    ref = oracle_verify(x, delta=delta)
+    print(compare_verify(ref, A, o, m, f"several slices B={Bn} V={V}"))
+    if delta is not None:
+        valid = x["draft_tokens"] >= 0
+        assert_rel(g[valid], ref["gamma_star"][valid], label="gamma* (several slices)")
+    # where the tokens fell, with the draw units a 512-workgroup grid gives
+    S = -(-V // 16384)
+    P1 = max(1, min(S, 512 // Bn))
+    earlier = sum(1 for t in o if t >= 0 and (t // 16384) + P1 < S)
+    print(f"tokens in a slice that is not its unit's last: {earlier} of {Bn}")
+
+
 def test_repeat_deterministic_one_workspace(B):
     """100 back-to-back calls on one workspace (its words must return to zero each time)
     give bit-identical results; then the same workspace serves another V."""
