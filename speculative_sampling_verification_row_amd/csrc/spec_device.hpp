@@ -169,6 +169,21 @@ __device__ __forceinline__ int wave_max_i(int v) {
              max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 
+// Maximum and sum over each row of 16 lanes (every lane of the row gets its row's):
+// the first four steps of the wave reductions, without the readlanes.
+__device__ __forceinline__ int row16_max_i(int v) {
+  v = max(v, dpp_i32<kDppQuadXor1>(v));
+  v = max(v, dpp_i32<kDppQuadXor2>(v));
+  v = max(v, dpp_i32<kDppRowHalfMirror>(v));
+  return max(v, dpp_i32<kDppRowMirror>(v));
+}
+__device__ __forceinline__ double row16_sum(double v) {
+  v += dpp_f64<kDppQuadXor1>(v);
+  v += dpp_f64<kDppQuadXor2>(v);
+  v += dpp_f64<kDppRowHalfMirror>(v);
+  return v + dpp_f64<kDppRowMirror>(v);
+}
+
 // Sum over the 64 lanes in a fixed order (every lane gets it).
 __device__ __forceinline__ double wave_sum(double v) {
   v += dpp_f64<kDppQuadXor1>(v);

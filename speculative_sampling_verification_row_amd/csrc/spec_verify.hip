@@ -362,18 +362,25 @@ __device__ __forceinline__ void merge_rows(const Params& p, int b, int nrows, Ro
         if (M.stage[q] == 0ull) M.stage[q] = poll_word(p.flags, part_row(p, b, row_of(i0 + q / W)) + q % W);
     }
     __syncthreads();
-    for (int i = wave_id(); i < nb; i += kWaves) {
-      const unsigned long long* st = M.stage + i * W;
+    // four rows per wave at once, one per row of 16 lanes (lane l16 of it taking
+    // words l16, l16 + 16, ...)
+    const int r16 = lane_id() >> 4, l16 = lane_id() & 15;
+    for (int j0 = wave_id() * 4; j0 < nb; j0 += kWaves * 4) {
+      const int i = j0 + r16;
+      const bool valid = i < nb;
+      const unsigned long long* st = M.stage + (valid ? i : 0) * W;
       int km = kNoK;
-      for (int q = lane_id(); q < W; q += 64) km = max(km, stats_k(st[q]));
-      km = wave_max_i(km);
+      if (valid)
+        for (int q = l16; q < W; q += 16) km = max(km, stats_k(st[q]));
+      km = row16_max_i(km);
       double s = 0.0;
-      for (int q = lane_id(); q < W; q += 64) {
-        const int kq = stats_k(st[q]);
-        if (kq != kNoK) s += ldexp(stats_s(st[q]), max(kq - km, -2000));
-      }
-      s = wave_sum(s);
-      if (lane_id() == 0) {
+      if (valid)
+        for (int q = l16; q < W; q += 16) {
+          const int kq = stats_k(st[q]);
+          if (kq != kNoK) s += ldexp(stats_s(st[q]), max(kq - km, -2000));
+        }
+      s = row16_sum(s);
+      if (valid && l16 == 0) {
         M.rk[i0 + i] = km == kNoK ? kNoRef : static_cast<float>(km);
         M.rs[i0 + i] = s;
       }
