@@ -1160,10 +1160,13 @@ __device__ __forceinline__ float lane_scale(float kl, const RowStats& r) {
   return static_cast<float>(ldexp(1.0 / r.s, static_cast<int>(fmaxf(kl - r.k, -2000.0f))));
 }
 
-// The target slice's 64 terms per lane, in LDS (conflict-free: consecutive lanes,
-// consecutive words), while the drafters' slices stream through registers.
+// The target slice's 64 terms per lane, in LDS as 16 float4 per lane (terms
+// 4j .. 4j + 3 in pt[j][lane]: conflict-free, consecutive lanes reading
+// consecutive 16-byte words), while the drafters' slices stream through
+// registers.  Four terms per read keep few reads in flight for the registers
+// the step leaves free.
 struct GammaLds {
-  float pt[kTilesPerSlice * 8][kThreads];
+  float4 pt[kTilesPerSlice * 2][kThreads];
   int last;  // the member that clears its slot's private words
 };
 
@@ -1262,8 +1265,10 @@ __host__ __device__ inline void chunk_job(const RowChunk& c, int R1, int nG, int
   priv = c.prefix && n == 0;
 }
 
+// FULL: the member's slice lies inside the row (every member but the last of a
+// ragged row), so its loop carries no masking.
+template <bool FULL>
 __device__ __forceinline__ void gamma_member(const Params& p, GammaLds& GL, int slot, int x) {
-  const bool full = (x + 1) * kSliceTok <= p.V;
   const int S = p.S, Q = gridDim.x / S;
   const int K = p.K, N = p.N, R1 = N + 1, nG = p.ngroups;
   const int ci0 = x * kSliceChunks + static_cast<int>(threadIdx.x);
@@ -1329,15 +1334,31 @@ __device__ __forceinline__ void gamma_member(const Params& p, GammaLds& GL, int 
     const float sc = lane_scale(pkl, rs);
     if (pr == 0) {  // the target's terms become probabilities
 #pragma unroll
-      for (int j = 0; j < kTilesPerSlice * 8; ++j) GL.pt[j][tid] *= sc;
+      for (int j = 0; j < kTilesPerSlice * 2; ++j) {
+        float4 a = GL.pt[j][tid];
+        a.x *= sc;
+        a.y *= sc;
+        a.z *= sc;
+        a.w *= sc;
+        GL.pt[j][tid] = a;
+      }
       return;
     }
     double gs = 0.0;
+    // the next tile's terms are read before this tile's are used, so that two
+    // tiles' reads are in flight rather than one
+    float4 na = GL.pt[0][tid], nb = GL.pt[1][tid];
 #pragma unroll
     for (int t = 0; t < kTilesPerSlice; ++t) {
+      const float4 a = na, b = nb;
+      if (t + 1 < kTilesPerSlice) {
+        na = GL.pt[2 * t + 2][tid];
+        nb = GL.pt[2 * t + 3][tid];
+      }
+      const float pt8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
       float mn[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) mn[i] = min_nonneg(GL.pt[t * 8 + i][tid], ep[t][i] * sc);
+      for (int i = 0; i < 8; ++i) mn[i] = min_nonneg(pt8[i], ep[t][i] * sc);
       gs += static_cast<double>(((mn[0] + mn[1]) + (mn[2] + mn[3])) + ((mn[4] + mn[5]) + (mn[6] + mn[7])));
     }
     gs = wave_sum(gs);
@@ -1362,7 +1383,7 @@ __device__ __forceinline__ void gamma_member(const Params& p, GammaLds& GL, int 
     unsigned long long wv[kRowWordsPerLane];
     if (pq >= 0) wave_row_issue(p, pw, wv);
     load(q1, r1, nxt);  // unconditional (no job: a buffer of no bytes), as in static_phase
-    if (!full) mask_tail(cur, ci0, p.V);
+    if (!FULL) mask_tail(cur, ci0, p.V);
     double sl;
     const float kl = lane_exps(p, cur, ec, sl);
     unsigned long long* words = words_of(q, r, priv);
@@ -1370,9 +1391,10 @@ __device__ __forceinline__ void gamma_member(const Params& p, GammaLds& GL, int 
     if (pq >= 0) finish_prev(wave_row_finish(p, pw, wv), ep);
     if (r == 0) {  // the target's terms wait in LDS for the row's normaliser
 #pragma unroll
-      for (int t = 0; t < kTilesPerSlice; ++t)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) GL.pt[t * 8 + i][tid] = ec[t][i];
+      for (int t = 0; t < kTilesPerSlice; ++t) {
+        GL.pt[2 * t][tid] = make_float4(ec[t][0], ec[t][1], ec[t][2], ec[t][3]);
+        GL.pt[2 * t + 1][tid] = make_float4(ec[t][4], ec[t][5], ec[t][6], ec[t][7]);
+      }
     }
     pq = q;
     pr = r;
@@ -1429,7 +1451,11 @@ __device__ __forceinline__ void gamma_member(const Params& p, GammaLds& GL, int 
 __device__ __forceinline__ void gamma_groups(const Params& p, GammaLds& GL) {
   const int S = p.S, Q = gridDim.x / S, g = blockIdx.x;
   if (g >= Q * S) return;
-  gamma_member(p, GL, g / S, g % S);
+  const int x = g % S;
+  if ((x + 1) * kSliceTok <= p.V)
+    gamma_member<true>(p, GL, g / S, x);
+  else
+    gamma_member<false>(p, GL, g / S, x);
 }
 
 
