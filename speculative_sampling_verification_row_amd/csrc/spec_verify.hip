@@ -1728,9 +1728,8 @@ constexpr int kWaveCand = 512;                          // a piece's candidates 
 
 struct TreeLds {
   MergeLds m;
-  uint32_t cand[kWaves][kWaveCand + 4];  // (+4: zeros after the last, for 16-byte reads)
-  uint32_t ranked[kWaves][kMaxTopk];     // a piece's best keys in rank order
-  float lmax[kWaves][64];                // the lanes' best logits
+  uint32_t cand[kWaves][kWaveCand + 16];  // (+16: zeros after the last, for reads of 16 keys)
+  uint32_t ranked[kWaves][kMaxTopk];      // a piece's best keys in rank order
   int ncand[kWaves];
   unsigned long long rec[kMaxTopk * kMaxSlices];
   uint32_t tau[2 * kWaves];
@@ -1753,6 +1752,26 @@ __device__ __forceinline__ void chunk_keys(const uint4 w, int off0, int valid, u
     const uint32_t b = (h[e >> 1] >> (16 * (e & 1))) & 0xffffu;
     k[e] = e < valid ? (bf16_key(b) << 16) | (0xffffu - static_cast<uint32_t>(off0 + e)) : 0u;
   }
+}
+
+// The same key of a bf16 value held as a float (low 16 bits zero), and back.
+__device__ __forceinline__ uint32_t float_key16(float f) { return bf16_key(__float_as_uint(f) >> 16); }
+__device__ __forceinline__ float key16_float(uint32_t k) {
+  const uint32_t b = (k & 0x8000u) ? (k & 0x7fffu) : (~k & 0xffffu);
+  return __uint_as_float(b << 16);
+}
+
+// The kk-th largest (1 <= kk <= 64) of the wave's 16-bit keys, one per lane, by
+// radix selection from the top bit: the largest T with at least kk keys >= T.
+// Ballots and scalar counts only (no LDS round trip).
+__device__ __forceinline__ uint32_t wave_kth_largest16(uint32_t key, int kk) {
+  uint32_t T = 0u;
+#pragma unroll
+  for (int b = 15; b >= 0; --b) {
+    const uint32_t c = T | (1u << b);
+    if (__popcll(__ballot(key >= c)) >= kk) T = c;
+  }
+  return T;
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
@@ -1845,16 +1864,11 @@ __device__ __forceinline__ PieceRecords piece_unit(const Params& p, int row, int
     unpack8(v[t], z, valid_of((t * 64 + lane) * kVec));
     m = max3f(max3f(z[0], z[1], z[2]), max3f(z[3], z[4], z[5]), max3f(z[6], z[7], m));
   }
-  L.lmax[w][lane] = m;
+  // tau: the topk-th best lane maximum (lanes without a token inside the row hold
+  // -inf, which only lowers it), selected on the maxima's exact bf16 keys
+  const float tau = key16_float(wave_kth_largest16(float_key16(m), kk));
   if (lane == 0) L.ncand[w] = 0;
   wave_lds_sync();
-  int rank = 0;  // lanes with a larger maximum
-#pragma unroll
-  for (int j = 0; j < 64; j += 4) {
-    const float4 o = *reinterpret_cast<const float4*>(&L.lmax[w][j]);
-    rank += (o.x > m ? 1 : 0) + (o.y > m ? 1 : 0) + (o.z > m ? 1 : 0) + (o.w > m ? 1 : 0);
-  }
-  const float tau = -wave_max(rank < kk ? -m : -__builtin_inff());
   // candidates (logit >= tau, inside the row) to LDS, with their exact keys; a
   // load without any in the wave (nearly all of them) costs one ballot
 #pragma unroll
@@ -1905,16 +1919,23 @@ __device__ __forceinline__ PieceRecords piece_unit(const Params& p, int row, int
     wave_lds_sync();
     C = L.ncand[w];
   }
-  if (lane < 4) cand[C + lane] = 0u;  // below every key
+  if (lane < 16) cand[C + lane] = 0u;  // below every key
   wave_lds_sync();
   // rank of each candidate among them; the topk best go to `ranked` in rank order
+  // (16 keys per round: four 16-byte broadcast reads issued together)
   for (int q0 = 0; q0 < C; q0 += 64) {
     const int q = q0 + lane;
     const uint32_t me = q < C ? cand[q] : 0u;
     int r = 0;
-    for (int j = 0; j < C; j += 4) {
-      const uint4 o = *reinterpret_cast<const uint4*>(cand + j);
-      r += (o.x > me ? 1 : 0) + (o.y > me ? 1 : 0) + (o.z > me ? 1 : 0) + (o.w > me ? 1 : 0);
+    for (int j = 0; j < C; j += 16) {
+      const uint4 o0 = *reinterpret_cast<const uint4*>(cand + j);
+      const uint4 o1 = *reinterpret_cast<const uint4*>(cand + j + 4);
+      const uint4 o2 = *reinterpret_cast<const uint4*>(cand + j + 8);
+      const uint4 o3 = *reinterpret_cast<const uint4*>(cand + j + 12);
+      r += (o0.x > me ? 1 : 0) + (o0.y > me ? 1 : 0) + (o0.z > me ? 1 : 0) + (o0.w > me ? 1 : 0);
+      r += (o1.x > me ? 1 : 0) + (o1.y > me ? 1 : 0) + (o1.z > me ? 1 : 0) + (o1.w > me ? 1 : 0);
+      r += (o2.x > me ? 1 : 0) + (o2.y > me ? 1 : 0) + (o2.z > me ? 1 : 0) + (o2.w > me ? 1 : 0);
+      r += (o3.x > me ? 1 : 0) + (o3.y > me ? 1 : 0) + (o3.z > me ? 1 : 0) + (o3.w > me ? 1 : 0);
     }
     if (q < C && r < kk) L.ranked[w][r] = me;
   }
