@@ -109,7 +109,11 @@ __device__ __forceinline__ void row_acc_add8(RowAcc& a, const float z[8], float 
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// The wave's index in the workgroup, as a scalar (the compiler cannot tell that
+// threadIdx.x >> 6 is the same in every lane of a wave: without readfirstlane,
+// addresses derived from it become per-lane values, and a buffer descriptor built
+// from them is issued through a loop over the lanes' distinct values).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // Cross-lane moves use DPP (data-parallel primitives of the VALU) rather than
 // LDS permutes: quad permutations and row mirrors combine lanes within a row of

@@ -1807,12 +1807,13 @@ __device__ __forceinline__ int wave_count_at_least(const uint4 v[kTilesPerSlice]
 }
 
 // Piece x of row (b K + k) N + i: loads of its 4096 tokens (lane l, load t:
-// tokens (64 t + l) 8 .. + 8 of the piece).  A row past the last (none) reads a
-// buffer of no bytes (zero, without touching memory).
+// tokens (64 t + l) 8 .. + 8 of the piece).  none: a unit past the last, whose
+// loads read a buffer of no bytes (zero, without touching memory); row and x are
+// then any valid piece, and only the byte count is a select.
 __device__ __forceinline__ void piece_load(const Params& p, int row, int x, bool none, uint4 v[kTilesPerSlice]) {
   const int i = row % p.N, bk = row / p.N, k = bk % p.K, b = bk / p.K;
   const uint32_t row_bytes = none ? 0u : static_cast<uint32_t>((p.V + kVec - 1) / kVec) * 16u;
-  const __amdgpu_buffer_rsrc_t dr = row_buffer(draft_row(p, none ? 0 : b, none ? 0 : i, none ? 0 : k), row_bytes);
+  const __amdgpu_buffer_rsrc_t dr = row_buffer(draft_row(p, b, i, k), row_bytes);
 #pragma unroll
   for (int t = 0; t < kTilesPerSlice; ++t)
     v[t] = stream_load16(dr, lane_id() * 16u, static_cast<uint32_t>(x * kPieceChunks + t * 64) * 16u);
@@ -2116,11 +2117,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   uint4 va[kTilesPerSlice], vb[kTilesPerSlice];
   int u = g * kWaves + wave_id();
   PieceRecords rec = no_records(p);
+  // (a unit past the last loads the last unit's descriptor with no bytes: no
+  // branch around the division, whose join would keep a flag in a register that
+  // the in-order load counter then makes wait for the loads in flight)
   auto load_unit = [&](int uu, uint4 (&v)[kTilesPerSlice]) {
-    const bool none = uu >= T1;
-    piece_load(p, none ? 0 : uu / Pw, none ? 0 : uu % Pw, none, v);
+    const int uc = min(uu, T1 - 1);
+    piece_load(p, uc / Pw, uc % Pw, uu >= T1, v);
   };
-  load_unit(u, va);
+  if (T1 > 0) load_unit(u, va);
   while (u < T1) {
     load_unit(u + GW, vb);
     store_records(rec);
