@@ -1868,33 +1868,67 @@ __device__ __forceinline__ PieceRecords piece_unit(const Params& p, int row, int
   // tau: the topk-th best lane maximum (lanes without a token inside the row hold
   // -inf, which only lowers it), selected on the maxima's exact bf16 keys
   const float tau = key16_float(wave_kth_largest16(float_key16(m), kk));
-  if (lane == 0) L.ncand[w] = 0;
-  wave_lds_sync();
-  // candidates (logit >= tau, inside the row) to LDS, with their exact keys; a
-  // load without any in the wave (nearly all of them) costs one ballot
+  int C;
+  if (FULL && tau > 0.0f) {
+    // Candidates (logit >= tau) element position by element position, on the raw
+    // words: one compare per bf16 value gives the wave's mask of lanes holding a
+    // candidate there, and nearly every mask is empty.  The high half of a word
+    // needs no unpacking: read as a float, the word is its high bf16 value plus
+    // less than one bf16 step of that value's size (the low half's bits extend
+    // the mantissa), so for tau > 0, a bf16 value itself, it reaches tau exactly
+    // when the high value does.  A lane writes its candidate at the running count
+    // plus its rank in the mask: no atomics, no LDS round trip.
+    C = 0;
+    auto put = [&](unsigned long long mask, int t, int e, uint32_t bits) {
+      if ((mask >> lane) & 1ull) {
+        const int q = C + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                              static_cast<uint32_t>(mask >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u)));
+        if (q < kWaveCand)
+          cand[q] = (bf16_key(bits) << 16) | (0xffffu - static_cast<uint32_t>((t * 64 + lane) * kVec + e));
+      }
+      C += __popcll(mask);
+    };
 #pragma unroll
-  for (int t = 0; t < kTilesPerSlice; ++t) {
-    const int off0 = (t * 64 + lane) * kVec;
-    const int valid = valid_of(off0);
-    float z[8];
-    unpack8(v[t], z, 8);
-    uint32_t hit = 0u;
+    for (int t = 0; t < kTilesPerSlice; ++t) {
+      const uint32_t wd[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) hit |= ((FULL || e < valid) && z[e] >= tau) ? (1u << e) : 0u;
-    if (__builtin_amdgcn_ballot_w64(hit != 0u) == 0ull) continue;
-    const uint4 wv = v[t];
-    while (hit != 0u) {
-      const int e = __builtin_ctz(hit);
-      hit &= hit - 1u;
-      // element e's bf16 bits by selects (an index into z would put z in scratch)
-      const uint32_t word = e < 4 ? (e < 2 ? wv.x : wv.y) : (e < 6 ? wv.z : wv.w);
-      const uint32_t bits = (e & 1) ? (word >> 16) : (word & 0xffffu);
-      const int q = atomicAdd(&L.ncand[w], 1);
-      if (q < kWaveCand) cand[q] = (bf16_key(bits) << 16) | (0xffffu - static_cast<uint32_t>(off0 + e));
+      for (int d = 0; d < 4; ++d) {
+        const unsigned long long mlo = __builtin_amdgcn_ballot_w64(__uint_as_float(wd[d] << 16) >= tau);
+        const unsigned long long mhi = __builtin_amdgcn_ballot_w64(__uint_as_float(wd[d]) >= tau);
+        if ((mlo | mhi) == 0ull) continue;
+        if (mlo != 0ull) put(mlo, t, 2 * d, wd[d] & 0xffffu);
+        if (mhi != 0ull) put(mhi, t, 2 * d + 1, wd[d] >> 16);
+      }
     }
+  } else {
+    if (lane == 0) L.ncand[w] = 0;
+    wave_lds_sync();
+    // candidates (logit >= tau, inside the row) to LDS, with their exact keys; a
+    // load without any in the wave costs one ballot
+#pragma unroll
+    for (int t = 0; t < kTilesPerSlice; ++t) {
+      const int off0 = (t * 64 + lane) * kVec;
+      const int valid = valid_of(off0);
+      float z[8];
+      unpack8(v[t], z, 8);
+      uint32_t hit = 0u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hit |= ((FULL || e < valid) && z[e] >= tau) ? (1u << e) : 0u;
+      if (__builtin_amdgcn_ballot_w64(hit != 0u) == 0ull) continue;
+      const uint4 wv = v[t];
+      while (hit != 0u) {
+        const int e = __builtin_ctz(hit);
+        hit &= hit - 1u;
+        // element e's bf16 bits by selects (an index into z would put z in scratch)
+        const uint32_t word = e < 4 ? (e < 2 ? wv.x : wv.y) : (e < 6 ? wv.z : wv.w);
+        const uint32_t bits = (e & 1) ? (word >> 16) : (word & 0xffffu);
+        const int q = atomicAdd(&L.ncand[w], 1);
+        if (q < kWaveCand) cand[q] = (bf16_key(bits) << 16) | (0xffffu - static_cast<uint32_t>(off0 + e));
+      }
+    }
+    wave_lds_sync();
+    C = L.ncand[w];
   }
-  wave_lds_sync();
-  int C = L.ncand[w];
   if (C > kWaveCand) {
     // rare: the exact topk-th best key by bisection (C > kWaveCand >= topk keys reach
     // tau), then its candidates again

@@ -68,6 +68,26 @@ def test_tree_ties_go_to_smaller_id(binding, quant, topk):
     assert_rel(got, ref, label="tree gamma ties")
 
 
+@pytest.mark.parametrize("case,topk", [("negative", 8), ("negative", 64), ("zero", 8), ("zero", 33)])
+def test_tree_nonpositive_threshold(binding, case, topk):
+    """Pieces whose threshold (the topk-th best lane maximum) is negative or zero, on
+    quantised logits so that many tie with it, and with -0 beside +0 in the zero case: the
+    kernel ranks such pieces on unpacked values rather than on the raw words."""
+    banner(f"tree threshold {case} topk={topk}")
+    rng = np.random.default_rng(topk + (1 if case == "zero" else 2))
+    B, K, N, V = 2, 2, 3, 20000
+    t = bf16_bits_from_f64(rng.normal(0, 4, (B, K + 1, V)))
+    if case == "negative":
+        d = bf16_bits_from_f64(-np.round(np.abs(rng.normal(0, 2, (N, B, K, V))) / 0.25) * 0.25 - 0.5)
+    else:
+        d = bf16_bits_from_f64(np.minimum(0.0, np.round(rng.normal(-6, 2, (N, B, K, V)))))
+        zeros = d == 0
+        d[zeros & (rng.random(d.shape) < 0.5)] = 0x8000  # -0
+    got = run_tree(binding, t, d, topk)
+    ref = oracle.spec_tree_gamma(t, d, topk)
+    assert_rel(got, ref, label=f"tree {case} threshold")
+
+
 def test_tree_all_equal_drafter_logits(binding):
     """Every logit tied: the children are the first topk ids of the row."""
     banner("tree all-equal drafter rows")
