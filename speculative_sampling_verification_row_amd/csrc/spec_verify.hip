@@ -1200,13 +1200,19 @@ __device__ __forceinline__ void mask_tail(uint4 v[kTilesPerSlice], int ci0, int 
 // dispatched first win the arbitration for the compute unit's issue slots and
 // memory, so slot 0 runs fastest.  Slot c >= 1 takes slot_share(slots, c) / 11 of
 // an even share of the work and slot 0 the rest, so that the slots finish
-// together.  Both kernels run two slots (measured: the second takes 9/11, in phase
-// 0 and in the gamma groups alike); the shares of three and four slots are
-// rougher measurements, kept for devices where more fit.
+// together.  Both kernels run two slots (measured: the second takes 9/11 of
+// phase 0, and 8/11 of the gamma groups' rows below); the shares of three and four
+// slots are rougher measurements, kept for devices where more fit.
 constexpr int kMaxSlots = 4;
 constexpr int kShareDen = 11;
 __host__ __device__ constexpr int slot_share(int P, int c) {
   return P == 2 ? (c == 1 ? 9 : 11) : P == 3 ? (c == 1 ? 11 : c == 2 ? 9 : 11) : P == 4 ? 11 - c : 11;
+}
+// The gamma groups' shares: with two slots the second takes 8/11 (measured: its
+// members' steps run about a quarter slower than the first slot's, since they
+// also wait longer for the other members' words); other slot counts as above.
+__host__ __device__ constexpr int gamma_share(int P, int c) {
+  return P == 2 ? (c == 1 ? 8 : 11) : slot_share(P, c);
 }
 
 // The rows of all groups, group by group (row 0 the target row k, row 1 + i
@@ -1234,7 +1240,7 @@ __host__ __device__ inline int64_t slot_weights(int q, int S, int ncu, int P) {
     // slots whose last member lies in dispatch slot c or before: (q' + 1) S <= (c + 1) ncu
     const int upto = c == P - 1 ? q : min(q, static_cast<int>(static_cast<int64_t>(c + 1) * ncu / S));
     if (upto > done) {
-      w += static_cast<int64_t>(upto - done) * slot_share(P, c);
+      w += static_cast<int64_t>(upto - done) * gamma_share(P, c);
       done = upto;
     }
   }

@@ -115,7 +115,7 @@ int main() {
     const int S = sp3[0], ncu = sp3[1], P = sp3[2];
     for (int q = 0; q < 600; ++q) {
       const int c_last = std::min(P - 1, ((q + 1) * S - 1) / ncu);
-      const int64_t want = P == 1 ? kShareDen : slot_share(P, c_last);
+      const int64_t want = P == 1 ? kShareDen : gamma_share(P, c_last);
       if (slot_weights(q + 1, S, ncu, P) - slot_weights(q, S, ncu, P) != want) {
         ++chunk_bad;
         if (chunk_bad < 10) printf("slot weight violation S=%d ncu=%d P=%d q=%d\n", S, ncu, P, q);
