@@ -1732,15 +1732,14 @@ constexpr int kPieceChunks = kPieceTok / kVec;
 constexpr int kMaxPieces = kMaxV / kPieceTok;
 constexpr int kWaveCand = 512;                          // a piece's candidates held in LDS
 
+constexpr int kWaveRec = 1024;   // records a merge wave gathers in LDS (beyond: the exact pass)
+constexpr int kRecPerLane = 8;  // rows with at most 64 x this many records keep them in registers
+
 struct TreeLds {
-  MergeLds m;
   uint32_t cand[kWaves][kWaveCand + 16];  // (+16: zeros after the last, for reads of 16 keys)
   uint32_t ranked[kWaves][kMaxTopk];      // a piece's best keys in rank order
   int ncand[kWaves];
-  unsigned long long rec[kMaxTopk * kMaxSlices];
-  uint32_t tau[2 * kWaves];
-  double red[kWaves];
-  int nrec;
+  unsigned long long rec[kWaves][kWaveRec];  // a merge wave's records at or above its bound
 };
 
 // Order-preserving 16-bit key of a bf16 logit; -0 counts as +0.
@@ -1997,150 +1996,166 @@ __device__ __forceinline__ int piece_records(const Params& p, int x) {
   return min(p.topk, min(kPieceTok, p.V - x * kPieceTok));
 }
 
-// Merge unit v = (b K + k) N + i.
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long x) {
+  const uint32_t h = wave_max_u32(static_cast<uint32_t>(x >> 32));
+  const uint32_t l = wave_max_u32(static_cast<uint32_t>(x >> 32) == h ? static_cast<uint32_t>(x) : 0u);
+  return (static_cast<unsigned long long>(h) << 32) | l;
+}
+
+// Bits of a record that can differ: the 16-bit logit key (bits 32..47) and the
+// token id's complement below 2^20 (bits 0..19); bits 20..31 are all ones and
+// 48..63 zero in every record of a row of at most 2^20 tokens.
+__device__ __forceinline__ int record_bit(int j) { return j < 16 ? 47 - j : 19 - (j - 16); }
+constexpr int kRecordBits = 36;
+
+// The kk-th best of a set of distinct records, by radix selection from the top
+// bit: the largest T with at least kk records >= T (0 when the set holds at most
+// kk).  count_ge(T) counts the set's records >= T over the wave.
+template <class CountGe>
+__device__ __forceinline__ unsigned long long kth_best_record(int kk, CountGe count_ge) {
+  unsigned long long T = 0x00000000fff00000ull;  // the bits every record holds
+  if (count_ge(T) <= kk) return 0ull;
+#pragma unroll 1
+  for (int j = 0; j < kRecordBits; ++j) {
+    const unsigned long long c = T | (1ull << record_bit(j));
+    if (count_ge(c) >= kk) T = c;
+  }
+  return T;
+}
+
+// Merge unit v = (b K + k) N + i, one wave (no workgroup barrier): the row's topk
+// best records over its pieces, and gamma = the target probability of their
+// tokens.  A bound at or below the row's topk-th best record is the best topk-th
+// record of the pieces with topk records; the records at or above it (1-2 topk on
+// these rows) go to LDS, and the exact topk-th best among them is selected bit by
+// bit with ballots.  Too many records at or above the bound (ties over many
+// pieces) select over all the row's records instead.
 __device__ __forceinline__ void tree_merge(const Params& p, int v, TreeLds& L) {
-  const int S = p.S, K = p.K, N = p.N, kk = p.topk;
+  const int K = p.K, N = p.N, kk = p.topk;
   const int P = (p.V + kPieceTok - 1) / kPieceTok;
-  const int i = v % N, bk = v / N, k = bk % K, b = bk / K;
-  const int tid = threadIdx.x;
+  const int bk = v / N, k = bk % K, b = bk / K;
+  const int w = wave_id(), lane = lane_id();
   unsigned long long* recs = p.cand + static_cast<size_t>(v) * P * static_cast<size_t>(kk);
-  // the target row's statistics (phase 0)
-  merge_rows(p, b, 1, [&](int) { return k; }, L.m);
-  // a bound at or below the row's kk-th best record: the best kk-th record of the
-  // pieces with kk records
-  uint32_t tlo = 0u, thi = 0u;
-  for (int x = tid; x < P; x += kThreads) {
-    if (piece_records(p, x) != kk) continue;
-    const unsigned long long w = poll_word(p.flags, recs + static_cast<size_t>(x) * kk + (kk - 1));
-    const uint32_t h = static_cast<uint32_t>(w >> 32), l = static_cast<uint32_t>(w);
-    if (h > thi || (h == thi && l > tlo)) {
-      thi = h;
-      tlo = l;
-    }
-  }
-  // 64-bit maximum over the block, as (high, low) words
-  unsigned long long tw = (static_cast<unsigned long long>(thi) << 32) | tlo;
-  {
-    uint32_t h = wave_max_u32(thi);
-    uint32_t l = wave_max_u32(thi == h ? tlo : 0u);
-    if (lane_id() == 0) {
-      L.tau[wave_id()] = h;
-      L.tau[kWaves + wave_id()] = l;
-    }
-    if (tid == 0) L.nrec = 0;
-    __syncthreads();
-    tw = 0ull;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      tw = max(tw, (static_cast<unsigned long long>(L.tau[w]) << 32) | L.tau[kWaves + w]);
-  }
-  // the records at or above the bound, to LDS (every expected record is read)
-  constexpr int kRecCap = kMaxTopk * kMaxSlices;
-  auto gather = [&](unsigned long long bound) {
-    for (int q = tid; q < P * kk; q += kThreads) {
-      const int x = q / kk, j = q - x * kk;
-      if (j >= piece_records(p, x)) continue;
-      const unsigned long long w = poll_word(p.flags, recs + static_cast<size_t>(x) * kk + j);
-      if (w >= bound && w != 0ull) {
-        const int c = atomicAdd(&L.nrec, 1);
-        if (c < kRecCap) L.rec[c] = w;
-      }
-    }
-    __syncthreads();
-  };
-  gather(tw);
-  if (L.nrec > kRecCap) {
-    // rare: pieces other than the bound's may each hold up to kk - 1 records above
-    // it.  The kk-th best of the pieces' best records is a bound too, and only the
-    // kk pieces whose best reaches it hold records at or above it: kk^2 <= kRecCap.
-    __syncthreads();
-    for (int x = tid; x < P; x += kThreads) L.rec[x] = poll_word(p.flags, recs + static_cast<size_t>(x) * kk);
-    if (tid == 0) L.nrec = 0;
-    __syncthreads();
-    unsigned long long t2 = 0ull;
-    for (int x0 = wave_id() * 64; x0 < P; x0 += kThreads) {
-      const int x = x0 + lane_id();
-      const unsigned long long me = x < P ? L.rec[x] : 0ull;
-      int r = 0;
-      for (int c0 = 0; c0 < P; c0 += 64) {
-        const unsigned long long o = c0 + lane_id() < P ? L.rec[c0 + lane_id()] : 0ull;
-        const uint32_t ohi = static_cast<uint32_t>(o >> 32), olo = static_cast<uint32_t>(o);
-#pragma unroll
-        for (int j = 0; j < 64; ++j)
-          r += ((static_cast<unsigned long long>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ohi), j))) << 32) |
-                static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(olo), j))) > me ? 1 : 0;
-      }
-      if (x < P && r == kk - 1) t2 = me;
-    }
-    // the one piece best of rank kk - 1, to every thread
-    const uint32_t h = wave_max_u32(static_cast<uint32_t>(t2 >> 32));
-    const uint32_t l = wave_max_u32(static_cast<uint32_t>(t2 >> 32) == h ? static_cast<uint32_t>(t2) : 0u);
-    if (lane_id() == 0) {
-      L.tau[wave_id()] = h;
-      L.tau[kWaves + wave_id()] = l;
-    }
-    __syncthreads();
-    unsigned long long b2 = 0ull;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) b2 = max(b2, (static_cast<unsigned long long>(L.tau[w]) << 32) | L.tau[kWaves + w]);
-    __syncthreads();
-    gather(max(tw, b2));
-  }
-  const int C = min(L.nrec, kRecCap);
-  if (tid == 0 && L.nrec > C) st_agent(&p.flags[3], 1u);  // cannot happen: a fault word, never an overrun
-  const RowStats st{L.m.rk[0], L.m.rs[0]};
+  unsigned long long* wrec = L.rec[w];
+  // the target row's statistics words, issued first (phase 0)
+  unsigned long long* row_words = part_row(p, b, k);
+  unsigned long long wv[kRowWordsPerLane];
+  wave_row_issue(p, row_words, wv);
+  const int nall = P * kk;
   const uint16_t* trow = target_row(p, b, k);
+  RowStats st{};
   double s = 0.0;
-  for (int q0 = wave_id() * 64; q0 < C; q0 += kThreads) {
-    const int q = q0 + lane_id();
-    const unsigned long long me = q < C ? L.rec[q] : 0ull;
-    int r = 0;
-    for (int c0 = 0; c0 < C; c0 += 64) {
-      const unsigned long long other = c0 + lane_id() < C ? L.rec[c0 + lane_id()] : 0ull;  // 0: below every record
-      const uint32_t ohi = static_cast<uint32_t>(other >> 32), olo = static_cast<uint32_t>(other);
+  auto add_token = [&](unsigned long long r) {
+    const uint32_t tok = 0xffffffffu - static_cast<uint32_t>(r);
+    if (tok < static_cast<uint32_t>(p.V))
+      s += token_prob(bf16_at(trow, static_cast<int>(tok)), p.c, st);
+    else
+      st_agent(&p.flags[3], 1u);  // not a record of this call: the fault word, never an index
+  };
+  // a record slot q of the row that its piece writes (piece x = q / kk, rank q % kk)
+  auto written = [&](int q) { return q < nall && q - (q / kk) * kk < piece_records(p, q / kk); };
+  if (nall <= 64 * kRecPerLane) {
+    // every record of the row in registers, loaded together (a slot no piece
+    // writes reads slot 0 and counts as none), then the exact topk-th best
+    unsigned long long rr[kRecPerLane];
 #pragma unroll
-      for (int j = 0; j < 64; ++j) {
-        const unsigned long long o =
-            (static_cast<unsigned long long>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ohi), j))) << 32) |
-            static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(olo), j));
-        r += o > me ? 1 : 0;
-      }
+    for (int j = 0; j < kRecPerLane; ++j) {
+      const int q = j * 64 + lane;
+      rr[j] = ld_agent_u64(recs + (written(q) ? q : 0));
     }
-    if (q < C && r < kk) {
-      const uint32_t tok = 0xffffffffu - static_cast<uint32_t>(me);
-      if (tok < static_cast<uint32_t>(p.V))
-        s += token_prob(bf16_at(trow, static_cast<int>(tok)), p.c, st);
-      else
-        st_agent(&p.flags[3], 1u);  // not a record of this call: the fault word, never an index
+#pragma unroll
+    for (int j = 0; j < kRecPerLane; ++j) {
+      const int q = j * 64 + lane;
+      if (!written(q))
+        rr[j] = 0ull;
+      else if (rr[j] == 0ull)
+        rr[j] = poll_word(p.flags, recs + q);
+    }
+    st = wave_row_finish(p, row_words, wv);
+    const int nrl = (nall + 63) / 64;
+    const unsigned long long T = kth_best_record(kk, [&](unsigned long long t) {
+      int c = 0;
+#pragma unroll
+      for (int j = 0; j < kRecPerLane; ++j)
+        if (j < nrl) c += __popcll(__builtin_amdgcn_ballot_w64(rr[j] != 0ull && rr[j] >= t));
+      return c;
+    });
+#pragma unroll
+    for (int j = 0; j < kRecPerLane; ++j)
+      if (rr[j] != 0ull && rr[j] >= T) add_token(rr[j]);
+  } else {
+    // the bound: the best topk-th record of the pieces with topk records
+    unsigned long long tw = 0ull;
+    for (int x = lane; x < P; x += 64)
+      if (piece_records(p, x) == kk) tw = max(tw, poll_word(p.flags, recs + static_cast<size_t>(x) * kk + (kk - 1)));
+    tw = wave_max_u64(tw);
+    // the records at or above it, compacted to LDS in lane order (every record the
+    // pieces write is read)
+    int C = 0;
+    for (int q0 = 0; q0 < nall; q0 += 64) {
+      const int q = q0 + lane;
+      unsigned long long r = 0ull;
+      if (written(q)) r = poll_word(p.flags, recs + q);
+      const bool in = r != 0ull && r >= tw;
+      const unsigned long long m = __builtin_amdgcn_ballot_w64(in);
+      if (in) {
+        const int at = C + static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                                       __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
+        if (at < kWaveRec) wrec[at] = r;
+      }
+      C += __popcll(m);
+    }
+    st = wave_row_finish(p, row_words, wv);
+    if (C <= kWaveRec) {
+      wave_lds_sync();
+      // the gathered records, up to 16 per lane, in registers for the selection
+      constexpr int kPer = kWaveRec / 64;
+      unsigned long long g[kPer];
+      const int nper = (C + 63) / 64;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) g[j] = (j < nper && j * 64 + lane < C) ? wrec[j * 64 + lane] : 0ull;
+      const unsigned long long T = kth_best_record(kk, [&](unsigned long long t) {
+        int c = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+          if (j < nper) c += __popcll(__builtin_amdgcn_ballot_w64(g[j] >= t));
+        return c;
+      });
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (j < nper && g[j] != 0ull && g[j] >= T) add_token(g[j]);
+    } else {
+      // rare: select over every record of the row, read again from memory (each is
+      // published: all were read above)
+      auto rec_at = [&](int q) -> unsigned long long { return written(q) ? ld_agent_u64(recs + q) : 0ull; };
+      const unsigned long long T = kth_best_record(kk, [&](unsigned long long t) {
+        int c = 0;
+        for (int q0 = 0; q0 < nall; q0 += 64) {
+          const unsigned long long r = rec_at(q0 + lane);
+          c += __popcll(__builtin_amdgcn_ballot_w64(r != 0ull && r >= t));
+        }
+        return c;
+      });
+      for (int q0 = 0; q0 < nall; q0 += 64) {
+        const unsigned long long r = rec_at(q0 + lane);
+        if (r != 0ull && r >= T) add_token(r);
+      }
     }
   }
   s = wave_sum(s);
-  if (lane_id() == 0) L.red[wave_id()] = s;
-  __syncthreads();
-  if (tid == 0) {
-    double g = 0.0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) g += L.red[w];
-    p.gamma[v] = static_cast<float>(g);
-  }
+  if (lane == 0) p.gamma[v] = static_cast<float>(s);
   // every record of the row back to zero
-  for (int q = tid; q < P * kk; q += kThreads) {
-    const int x = q / kk, j = q - x * kk;
-    if (j < piece_records(p, x)) st_agent_u64(recs + static_cast<size_t>(x) * kk + j, 0ull);
-  }
+  for (int q = lane; q < nall; q += 64)
+    if (written(q)) st_agent_u64(recs + q, 0ull);
   // the last of the row's N merge units clears its statistics words
   stores_complete();
-  __syncthreads();
-  if (tid == 0) {
-    const int last = ticket(&p.done[bk]) == static_cast<uint32_t>(N - 1) ? 1 : 0;
+  int last = 0;
+  if (lane == 0) {
+    last = ticket(&p.done[bk]) == static_cast<uint32_t>(N - 1) ? 1 : 0;
     if (last) st_agent(&p.done[bk], 0u);
-    L.nrec = last;
   }
-  __syncthreads();
-  if (L.nrec) {
-    unsigned long long* w = part_row(p, b, k);
-    for (int q = tid; q < S * kWaves; q += kThreads) st_agent_u64(w + q, 0ull);
-  }
+  if (__builtin_amdgcn_readfirstlane(last))
+    for (int q = lane; q < p.S * kWaves; q += 64) st_agent_u64(row_words + q, 0ull);
 }
 
 // Draft-tree calls (spec_tree_gamma): phase 0 over the target rows, then the piece
@@ -2184,11 +2199,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       store_records(piece_unit<false>(p, r, Pw, va, L));
     }
   }
+  // merge units: one per wave, v = g kWaves + w, + G kWaves, ...
   const int T2 = p.B * p.K * p.N;
-  for (int v = g; v < T2; v += G) {
-    __syncthreads();
-    tree_merge(p, v, L);
-  }
+  for (int v = g * kWaves + wave_id(); v < T2; v += GW) tree_merge(p, v, L);
 }
 
 // ---------------------------------------------------------------------------
