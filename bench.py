@@ -147,7 +147,15 @@ class Workload:
     key = ""
     desc = ""
     positions = 0          # verified draft positions per launch
-    algo_bytes = 0         # bytes the method must move per launch (every logit once + small arrays)
+    algo_bytes = 0         # bytes the method must move per launch (every logit it needs once + small arrays)
+    bonus_rows = None      # bonus target rows among them: sequences that accepted every draft
+
+    def count_bonus(self, accepted_len, K: int, B: int, V: int) -> None:
+        """The bonus row K of a sequence is needed (and read) only when it accepted all K
+        drafts: count those in the launch's own outputs and add their rows."""
+        self.bonus_rows = int((accepted_len == K).sum().item())
+        self.algo_bytes = self.base_bytes + 2 * V * self.bonus_rows
+        log(f"bonus rows read: {self.bonus_rows} of {B} sequences accepted every draft")
 
     def setup(self, copies_min_bytes: int):
         raise NotImplementedError
@@ -173,9 +181,10 @@ class SpsLike(Workload):
         B, K, V = w.B, w.K, w.V
         self.desc = w.name + ("" if delta is None else f" delta={delta}") + (" exact-KL gamma*" if exact_kl else "")
         self.positions = B * K
-        rows = B * (K + 1) + B * K
+        # target and draft rows of positions 0..K-1; bonus rows are added once counted
+        rows = 2 * B * K
         small = B * K * 4 * 2 + B * (K + 1) * 4 + B * 4 * 2 + B * K + (B * K * 4 if delta is not None else 0)
-        self.algo_bytes = 2 * V * rows + small
+        self.base_bytes = self.algo_bytes = 2 * V * rows + small
 
     def setup(self, copies_min_bytes):
         import torch
@@ -202,6 +211,7 @@ class SpsLike(Workload):
                                                         exact_kl=self.exact_kl)
                           for t, d in self.copies]
         log(f"{len(self.copies)} input copies of {2 * (t.numel() + d.numel()) / 1e6:.1f} MB")
+        self.count_bonus(self.calls[0].run()[0], self.w.K, self.w.B, self.w.V)
 
     def launch(self, i):
         self.calls[i % len(self.calls)].launch()
@@ -236,12 +246,12 @@ class GammaLike(Workload):
         B, K, N, V = w.B, w.K, w.N, w.V
         self.desc = w.name
         self.positions = B * K
-        trows = B * (K + 1) if w.fused else B * K
-        rows = trows + N * B * K
+        # target rows 0..K-1 and every drafter's rows; a fused call's bonus rows are added once counted
+        rows = B * K + N * B * K
         small = B * K * 4 + B * K * N * 4 + 2 * B * N * 4
         if w.fused:
             small += B * 4 + B * K * 4 * 2 + B * (K + 1) * 4 + B * 4 * 2 + B * K
-        self.algo_bytes = 2 * V * rows + small
+        self.base_bytes = self.algo_bytes = 2 * V * rows + small
 
     def setup(self, copies_min_bytes):
         import torch
@@ -266,6 +276,8 @@ class GammaLike(Workload):
         self.calls = [binding.prepare_counterfactual_gamma(t, d, self.traj, self.w.temperature, workspace=self.ws,
                                                            **self.kw) for t, d in self.copies]
         log(f"{len(self.copies)} input copies of {per / 1e6:.1f} MB")
+        if self.w.fused:
+            self.count_bonus(self.calls[0].run()["accepted_len"], self.w.K, self.w.B, self.w.V)
 
     def launch(self, i):
         self.calls[i % len(self.calls)].launch()
@@ -372,6 +384,15 @@ class LoopLike(GammaLike):
         torch.cuda.synchronize()
         self.loop.reset()
         self.loop.capture()
+        # bonus rows: the mean over the first rounds (each round selects its own drafters)
+        self.loop.reset()
+        full, nr = 0, 64
+        for _ in range(nr):
+            self.loop.replay()
+            full += int((self.loop.out["accepted_len"] == self.w.K).sum().item())
+        self.bonus_rows = full / nr
+        self.algo_bytes = int(round(self.base_bytes + 2 * self.w.V * self.bonus_rows))
+        log(f"bonus rows read: {self.bonus_rows:.2f} of {self.w.B} sequences per round (mean of {nr} rounds)")
         self.loop.reset()
         log(f"captured a round per row copy ({n} copies of {per / 1e6:.1f} MB) as graphs")
 
@@ -620,7 +641,7 @@ def main(argv=None):
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.desc, "positions_per_step": wl.positions,
-                   "algorithmic_bytes_per_step": wl.algo_bytes},
+                   "algorithmic_bytes_per_step": wl.algo_bytes, "bonus_rows_per_step": wl.bonus_rows},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": kernel_of(args.workload), "mean_launch_ms": mean_launch_s * 1e3,

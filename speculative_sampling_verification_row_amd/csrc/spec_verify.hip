@@ -12,23 +12,25 @@
 //
 //   gamma groups -- (gamma calls) slots of S workgroups stream a position's
 //       target row and its N drafter rows once (gamma_groups).
-//   phase 0 -- statistics slices of the call's slice list, dealt to the
-//       workgroups on a fixed schedule weighted by how fast the hardware serves
-//       each dispatch slot of them (static_phase).  A slice is 16384 tokens of one row,
-//       streamed once from HBM with 128-bit loads while the next slice's loads
-//       are in flight.  Each wave reduces its share to an exact base-2 softmax
-//       pair (reference k, sum s) and publishes it as one 64-bit word.  The list
-//       is sequence-major, so sequences finish their statistics one after
-//       another.
+//   phase 0 -- (verify and draft-tree calls) statistics slices of the call's
+//       slice list, dealt to the workgroups on a fixed schedule weighted by how
+//       fast the hardware serves each dispatch slot of them (static_phase).  A
+//       slice is 16384 tokens of one row, streamed once from HBM with 128-bit
+//       loads while the next slice's loads are in flight.  Each wave reduces its
+//       share to an exact base-2 softmax pair (reference k, sum s) and publishes
+//       it as one 64-bit word.  The list is sequence-major, so sequences finish
+//       their statistics one after another.  It holds the rows the decisions
+//       need (target and draft rows of positions 0..K-1): the bonus row K is
+//       read only by the draw units of a sequence that accepts every draft.
 //   phase 1 -- units g, g + G, ... of the draw list, one per slice of a
 //       sequence's rows.  A draw unit merges the sequence's statistics, takes
 //       every accept decision ([LT] §5.1, [CA] Key design 3), finds the first
 //       rejection A and computes per-512-token sub-tile masses of the sampling
 //       weights of its slice of the row pair A ((pt - pd)+, Cactus's (h - pd)+)
-//       or of the bonus row pt.  It publishes its slice's total, reads the
-//       other slices' totals, and the unit whose slice holds the inverse-CDF
-//       crossing ([LT] §9.1) finds the token in the rows it still holds in
-//       registers.
+//       or of the bonus row pt (at references of its own, since that row has no
+//       statistics).  It publishes its slice's total, reads the other slices'
+//       totals, and the unit whose slice holds the inverse-CDF crossing ([LT]
+//       §9.1) finds the token in the rows it still holds in registers.
 //   phase 2 -- (gamma calls) units g, g + G, ... of the HedgeSpec estimator and
 //       loss ([NB] Key designs 1-3).
 //
@@ -116,7 +118,7 @@ struct Params {
   int P2;      // phase-2 (estimator) units per sequence
   int nlast;   // gamma calls: steps per sequence that read its statistics (0: verify calls)
   int RS;      // statistics slices per sequence (R * S)
-  int total0;  // slices of the statistics list (verify: B * R * S; gamma: the fused bonus rows, B * S or 0)
+  int total0;  // slices of the statistics list (verify and draft-tree calls: B * R * S; gamma calls: 0)
   int ngroups; // gamma groups (B * K): a position's target row and its N drafter rows
   int ncu;     // compute units; workgroup g sits in dispatch slot g / ncu
   int slots;   // workgroups per compute unit in this launch (1: no weighting)
@@ -158,20 +160,13 @@ __device__ __forceinline__ unsigned long long* part_row(const Params& p, int b, 
   return p.part + (static_cast<size_t>(b) * p.R + r) * static_cast<size_t>(p.S) * kWaves;
 }
 
-// Statistic row streamed i-th within a sequence.  Verify calls: target 0, draft 0,
-// target 1, draft 1, ..., then the bonus target row K.  Gamma calls: position by
-// position, target row k then every drafter's row k; the fused bonus row last.
+// Statistic row streamed i-th within a sequence of the phase-0 list.  Verify
+// calls: target 0, draft 0, target 1, draft 1, ...  Draft-tree calls: target rows
+// 0..K-1.  (Gamma calls have no list: their groups stream every row.)
 __device__ __forceinline__ int order_row(const Params& p, int i) {
-  if (p.mode == MODE_TREE) return i;  // draft-tree calls: target rows 0..K-1 only
-  if (p.mode == MODE_VERIFY) {
-    if (i >= 2 * p.K) return p.K;
-    const int k = i >> 1;
-    return (i & 1) ? p.RT + k : k;
-  }
-  const int g1 = p.N + 1;
-  if (i >= p.K * g1) return p.K;
-  const int k = i / g1, m = i - k * g1;
-  return m == 0 ? k : p.RT + (m - 1) * p.K + k;
+  if (p.mode == MODE_TREE) return i;
+  const int k = i >> 1;
+  return (i & 1) ? p.RT + k : k;
 }
 
 // ---------------------------------------------------------------------------
@@ -241,19 +236,12 @@ __device__ __forceinline__ SliceLoc slice_loc(const Params& p, int sig) {
     none.out = nullptr;
     return none;
   }
-  int b, x, r;
-  if (p.mode == MODE_GAMMA) {  // the list holds only the fused bonus rows (the groups do the rest)
-    b = sig / p.S;
-    x = sig - b * p.S;
-    r = p.K;
-  } else {
-    b = sig / p.RS;
-    const int q = sig - b * p.RS;
-    const int i = q / p.S;
-    x = q - i * p.S + i % p.S;
-    if (x >= p.S) x -= p.S;
-    r = order_row(p, i);
-  }
+  const int b = sig / p.RS;
+  const int q = sig - b * p.RS;
+  const int i = q / p.S;
+  int x = q - i * p.S + i % p.S;
+  if (x >= p.S) x -= p.S;
+  const int r = order_row(p, i);
   SliceLoc L;
   L.row = row_buffer(stat_row(p, b, r), static_cast<uint32_t>((p.V + kVec - 1) / kVec) * 16u);
   L.c0 = x * kSliceChunks;
@@ -613,7 +601,9 @@ struct Lds {
   MergeLds m;
   DecideLds dl;
   double subsum[kMaxSub];
+  float wref[kMaxSub / kTilesPerSlice];  // bonus draws: each wave's reference, per slice of the unit
   double tot[kMaxSlices];
+  int tk[kMaxSlices];                    // bonus draws: each slice's reference
   double gsum[kRowCap];
   double arat[kRowCap];
   int flag;
@@ -691,8 +681,9 @@ __host__ __device__ inline double kl_divergence(double g, double c) {
   return kl_share(c, x, g * l1 - d) + kl_share(c1, y, (1.0 - g) * log1p(y) + d);
 }
 
-// Merge the statistics of target rows 0..K and drafter `drafter`'s rows 0..K-1,
-// take every accept decision, and describe the draw.  Writes accept_mask and
+// Merge the statistics of target rows 0..K-1 and drafter `drafter`'s rows 0..K-1,
+// take every accept decision, and describe the draw (the bonus row K has no
+// statistics: its draw finds its own references).  Writes accept_mask and
 // gamma_star when `write_outputs`.  The result is in L.dl.d after the call.
 template <bool KL = false>
 __device__ __forceinline__ void decide(const Params& p, int b, bool write_outputs, int pre_n, Lds& L) {
@@ -715,8 +706,8 @@ __device__ __forceinline__ void decide(const Params& p, int b, bool write_output
       zd = bf16_at(draft_row(p, b, drafter, t), n);
     }
   }
-  // rows 0..K: target rows 0..K; rows K+1..2K: the drafter's rows 0..K-1
-  merge_rows(p, b, 2 * K + 1, [&](int i) { return i <= K ? i : p.RT + dsafe * K + (i - K - 1); }, L.m);
+  // rows 0..K-1: target rows 0..K-1; rows K..2K-1: the drafter's rows 0..K-1
+  merge_rows(p, b, 2 * K, [&](int i) { return i < K ? i : p.RT + dsafe * K + (i - K); }, L.m);
   // threads t < K (all in wave 0): the accept test of position t
   uint32_t state = ST_INVALID;
   double ct = 0.0, gs = 0.0;
@@ -724,7 +715,7 @@ __device__ __forceinline__ void decide(const Params& p, int b, bool write_output
     bool acc = false;
     if (tok_ok) {
       const RowStats st{L.m.rk[t], L.m.rs[t]};
-      const RowStats sd{L.m.rk[K + 1 + t], L.m.rs[K + 1 + t]};
+      const RowStats sd{L.m.rk[K + t], L.m.rs[K + t]};
       // [CA] Key design 3 with the verifier's probability c of the candidate; delta = 0 is SpS.
       ct = fmin(token_prob(zt, p.c, st), 1.0);
       const double cd = token_prob(zd, p.c, sd);
@@ -777,8 +768,8 @@ __device__ __forceinline__ void decide(const Params& p, int b, bool write_output
         d.pair = 1;
         w.mode = W_RESID;
         w.kt = L.m.rk[A];
-        w.kd = L.m.rk[K + 1 + A];
-        w.r = L.m.rs[A] / L.m.rs[K + 1 + A];
+        w.kd = L.m.rk[K + A];
+        w.r = L.m.rs[A] / L.m.rs[K + A];
         // [CA] Key design 2 (1.0 exactly at delta = 0); with the exact-KL gamma*
         // the draw sets both once it has gamma* (kl_positions)
         w.s_scale = ctA < 1.0 ? (1.0 - gsA) / (1.0 - ctA) : 0.0;
@@ -786,12 +777,12 @@ __device__ __forceinline__ void decide(const Params& p, int b, bool write_output
         w.n = nA;
         w.special = p.delta > 0.0 ? 1 : 0;
       } else {
-        // every draft kept: bonus token from target row K
+        // every draft kept: bonus token from target row K (the draw sets the references)
         d.A = K;
         d.draw_row = K;
         d.pair = 0;
         w.mode = W_TARGET;
-        w.kt = L.m.rk[K];
+        w.kt = 0.0f;
       }
       d.w = w;
       L.dl.d = d;
@@ -875,15 +866,30 @@ __device__ __forceinline__ int slice_unit(const Params& p, int s) { return p.P1 
 // slice's sub-tile masses, L.subsum[j kSliceSub ..] for its j-th slice) to each
 // unit y of its sequence as word tot[b][y][s], reads the S words addressed to it
 // (clearing them: it is their only reader), and returns the crossing slice of
-// the sequence's draw (-1 for none).
-template <bool MULTI = false>
-__device__ __forceinline__ int exchange_totals(const Params& p, int b, int x, double u, double& x_rel, Lds& L) {
+// the sequence's draw (-1 for none), with x_rel the draw's point relative to the
+// mass before that slice.
+// REF (bonus draws, whose row has no merged statistics): a wave's sub-tile masses
+// are in units of 2^-k_w, k_w its own reference (L.wref), so a slice's total is
+// published as a statistics word at the slice's reference (the largest of its
+// waves'), the reader brings the totals to the largest slice reference before
+// the scan, and x_rel is returned in units of the crossing slice's reference
+// (kx, from the crossing slice's word).
+template <bool MULTI = false, bool REF = false>
+__device__ __forceinline__ int exchange_totals(const Params& p, int b, int x, double u, double& x_rel, Lds& L,
+                                               int& kx) {
   const int tid = threadIdx.x;
   unsigned long long* tw = p.tot + static_cast<size_t>(b) * kMaxSlices * kMaxSlices;
   if (tid < 64) {  // wave 0
     auto publish = [&](int j) {
-      const double T = readlane_f64(wave_incl_scan(tid < kSliceSub ? L.subsum[j * kSliceSub + tid] : 0.0), 63);
-      if (tid < p.P1) st_agent_u64(tw + tid * kMaxSlices + x + j * p.P1, pack_f64(T));
+      double m = tid < kSliceSub ? L.subsum[j * kSliceSub + tid] : 0.0;
+      float ks = 0.0f;
+      if (REF) {
+        const float* wr = L.wref + j * kWaves;
+        ks = fmaxf(fmaxf(wr[0], wr[1]), fmaxf(wr[2], wr[3]));
+        if (tid < kSliceSub) m = ldexp(m, static_cast<int>(fmaxf(wr[tid & (kWaves - 1)] - ks, -2000.0f)));
+      }
+      const double T = readlane_f64(wave_incl_scan(m), 63);
+      if (tid < p.P1) st_agent_u64(tw + tid * kMaxSlices + x + j * p.P1, REF ? pack_stats(ks, T) : pack_f64(T));
     };
     publish(0);
     if (MULTI)
@@ -893,12 +899,26 @@ __device__ __forceinline__ int exchange_totals(const Params& p, int b, int x, do
     unsigned long long* src = tw + x * kMaxSlices + tid;
     unsigned long long w = ld_agent_u64(src);
     if (w == 0ull) w = poll_word(p.flags, src);
-    L.tot[tid] = unpack_f64(w);
+    if (REF) {
+      L.tk[tid] = stats_k(w);
+      L.tot[tid] = stats_s(w);
+    } else {
+      L.tot[tid] = unpack_f64(w);
+    }
     st_agent_u64(src, 0ull);
   }
   __syncthreads();
   const int lane = lane_id();
-  return crossing_slice(lane < p.S ? L.tot[lane] : 0.0, u, x_rel);
+  if (!REF) return crossing_slice(lane < p.S ? L.tot[lane] : 0.0, u, x_rel);
+  const int kq = lane < p.S ? L.tk[lane] : kNoK;
+  const int km = wave_max_i(kq);
+  const double t = kq != kNoK ? ldexp(L.tot[lane], max(kq - km, -2000)) : 0.0;
+  const int xs = crossing_slice(t, u, x_rel);
+  if (xs >= 0) {
+    kx = L.tk[xs];
+    x_rel = ldexp(x_rel, min(km - kx, 2000));
+  }
+  return xs;
 }
 
 // Draw unit x of sequence b, decision d made: the sub-tile masses of slice x of
@@ -921,6 +941,9 @@ __device__ __forceinline__ double kl_positions(const Params& p, int b, bool writ
 // the slice's loads are in flight, and completes d.w.
 // MULTI: the unit may take several slices (P1 < S); without it, slice x only,
 // in straight-line code.
+// W_TARGET (the bonus row, which has no merged statistics): each wave weighs its
+// share of a slice at its own reference k_w = ceil(max z c) over that share
+// (L.wref), and exchange_totals brings the slices to a common one.
 template <int MODE, bool SPECIAL, bool KL = false, bool MULTI = false>
 __device__ __forceinline__ int draw_slice(const Params& p, int b, int x, Decision& d, Lds& L) {
   const int tid = threadIdx.x, wave = wave_id();
@@ -948,6 +971,19 @@ __device__ __forceinline__ int draw_slice(const Params& p, int b, int x, Decisio
       d.w.s_scale = ctA < 1.0 ? (1.0 - gsA) / (1.0 - ctA) : 0.0;
       d.w.hn = gsA * L.m.rs[d.A];
     }
+    if (MODE == W_TARGET) {
+      const int nchunks = (p.V + kVec - 1) / kVec;
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int q = 0; q < kTilesPerSlice; ++q) {
+        const int ci = c0 + q * kThreads;
+        float z[8];
+        unpack8(vt[q], z, ci < nchunks ? p.V - ci * kVec : 0);
+        mx = max3f(max3f(z[0], z[1], z[2]), max3f(z[3], z[4], z[5]), max3f(z[6], z[7], mx));
+      }
+      d.w.kt = fmaxf(kNoRef, ceilf(wave_max(mx) * p.c));
+      if (lane_id() == 0) L.wref[j * kWaves + wave] = d.w.kt;
+    }
 #pragma unroll
     for (int q = 0; q < kTilesPerSlice; ++q) {
       double wv[8];
@@ -963,15 +999,27 @@ __device__ __forceinline__ int draw_slice(const Params& p, int b, int x, Decisio
     for (int j = 1; j < ns; ++j) slice_masses(j);
   __syncthreads();
   double x_rel = 0.0;
-  const int xs = exchange_totals<MULTI>(p, b, x, static_cast<double>(p.u[b * (p.K + 1) + d.draw_row]), x_rel, L);
+  int kx = 0;
+  const int xs = exchange_totals<MULTI, MODE == W_TARGET>(p, b, x, static_cast<double>(p.u[b * (p.K + 1) + d.draw_row]),
+                                                         x_rel, L, kx);
   if (xs < 0 || (MULTI ? slice_unit(p, xs) : xs) != x) return xs;
   // the crossing slice is this unit's j-th; its total is positive, so one of its
   // sub-tiles has mass; the scan is the one that formed the total
   const int js = (xs - x) / p.P1;
-  const double m = lane_id() < kSliceSub ? L.subsum[js * kSliceSub + lane_id()] : 0.0;
+  double m = lane_id() < kSliceSub ? L.subsum[js * kSliceSub + lane_id()] : 0.0;
+  float kw = 0.0f;
+  if (MODE == W_TARGET) {  // every sub-tile at the slice's reference kx, as its published total
+    const float* wr = L.wref + js * kWaves;
+    m = ldexp(m, static_cast<int>(fmaxf(wr[lane_id() & (kWaves - 1)] - static_cast<float>(kx), -2000.0f)));
+    kw = wr[wave];
+  }
   const int ss = wave_crossing(m, wave_incl_scan(m), x_rel);
   const int qs = ss / kWaves;
   if (wave == ss - qs * kWaves) {
+    if (MODE == W_TARGET) {  // this wave's own units
+      d.w.kt = kw;
+      x_rel = ldexp(x_rel, static_cast<int>(fminf(static_cast<float>(kx) - kw, 2000.0f)));
+    }
     const int c0 = xs * kTilesPerSlice * kThreads + tid;
     uint4 ct = vt[0], cd = vd[0];
     if (!MULTI || js == ns - 1) {  // the last slice: its rows are still in registers
@@ -1036,7 +1084,8 @@ __device__ __forceinline__ void unit_draw(const Params& p, int b, int x, int pre
     for (int q = threadIdx.x; q < (MULTI ? unit_slices(p, x) : 1) * kSliceSub; q += kThreads) L.subsum[q] = 0.0;
     __syncthreads();
     double x_rel = 0.0;
-    xs = exchange_totals<MULTI>(p, b, x, 0.0, x_rel, L);
+    int kx = 0;
+    xs = exchange_totals<MULTI>(p, b, x, 0.0, x_rel, L, kx);
     if (x == 0 && threadIdx.x == 0) {
       p.accepted_len[b] = -1;
       p.out_token[b] = -1;
@@ -2517,7 +2566,10 @@ static Shape make_shape(int B, int K, int N, int V, int mode, int fused) {
   s.mode = mode;
   s.fused = fused;
   s.topk = 0;
-  s.RT = mode == MODE_VERIFY ? K + 1 : K + fused;
+  // statistics rows: the target rows 0..K-1 and the drafters' rows; the bonus row K
+  // (needed only when every draft is accepted) is read by the draw units of such
+  // a sequence alone
+  s.RT = K;
   s.R = s.RT + N * K;
   if (mode == MODE_TREE) s.R = s.RT = K;  // the statistics list holds the target rows only
   s.S = (V + kSliceTok - 1) / kSliceTok;
@@ -2530,8 +2582,8 @@ static Shape make_shape(int B, int K, int N, int V, int mode, int fused) {
     s.nlast = N;  // merge units per target row (tickets per row)
   }
   s.RS = static_cast<int64_t>(s.R) * s.S;
-  // gamma calls: the groups take the rows of positions 0..K-1; the list holds the bonus rows
-  s.total0 = mode == MODE_VERIFY ? static_cast<int64_t>(B) * s.RS : (fused ? static_cast<int64_t>(B) * s.S : 0);
+  // gamma calls: the groups take every statistics row, so the list is empty
+  s.total0 = mode == MODE_VERIFY ? static_cast<int64_t>(B) * s.RS : 0;
   s.ngroups = mode == MODE_VERIFY ? 0 : static_cast<int64_t>(B) * K;
   if (mode == MODE_TREE) {
     s.total0 = static_cast<int64_t>(B) * s.RS;
