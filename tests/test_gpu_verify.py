@@ -225,6 +225,50 @@ def test_units_of_several_slices(B, Bn, V, delta):
     print(f"tokens in a slice that is not its unit's last: {earlier} of {Bn}")
 
 
+@pytest.mark.parametrize("Bn,V", [(64, 128256), (16, 1 << 20), (64, 400000)])
+def test_bonus_row_at_references_of_its_own(B, Bn, V):
+    """Every draft accepted (draft rows equal to the target's), so every sequence draws
+    its bonus from target row K, a row with no statistics of its own: each wave of a draw
+    unit weighs its share of a slice at its own reference and the slices meet at a common
+    one ([LT] §9.1: the bonus token from the target's last row).  Each bonus row puts two
+    slices 40 above the rest, so that the mass splits between them, every other slice 200
+    below (about 290 binary orders, past fp32's range), one wave's share of a top slice
+    30 below its slice, and a run of masked (-inf) tokens in the other top slice.  Units of
+    one slice (V = 128,256) and of several (V = 2^20 and 400,000); every sequence checked."""
+    banner(f"bonus draws at their own references B={Bn} V={V}")
+    K = 4
+    x = sps_case(Bn, K, V, seed=41 + Bn, peak=0.0)
+    x["draft"] = x["target"][:, :K].copy()
+    x["draft_tokens"] = gen.sample_tokens(x["draft"], 1.0, seed=42, config_id=94)
+    rng = np.random.default_rng(43 + Bn)
+    S = -(-V // 16384)
+    tops = []
+    for b in range(Bn):
+        z = oracle.widen_bf16(x["target"][b, K]).astype(np.float64)
+        top = rng.choice(S, size=2, replace=False)
+        off = np.full(S, -200.0)
+        off[top] = 40.0 + 0.5 * rng.random(2)
+        z = z + np.repeat(off, 16384)[:V]
+        for q in range(8):  # wave 2's share of the first top slice: 512 tokens of each tile
+            lo = int(top[0]) * 16384 + q * 2048 + 2 * 512
+            z[lo:min(lo + 512, V)] -= 30.0
+        bits = bf16_bits_from_f64(z)
+        lo = int(top[1]) * 16384 + 300
+        bits[lo:min(lo + 700, V)] = np.uint16(0xFF80)
+        x["target"][b, K] = bits
+        tops.append(sorted(int(t) for t in top))
+    A, o, m, _ = run_verify(B, x)
+    assert np.all(A == K) and np.all(m == 1)
+    ref = oracle_verify(x)
+    print(compare_verify(ref, A, o, m, f"bonus B={Bn} V={V}"))
+    # the draws did land in both top slices across the batch
+    slices = [int(t) // 16384 for t in o]
+    assert all(s in tp for s, tp in zip(slices, tops))
+    first = sum(1 for s, tp in zip(slices, tops) if s == tp[0])
+    print(f"tokens in the lower-indexed top slice: {first} of {Bn}")
+    assert 0 < first < Bn
+
+
 def test_repeat_deterministic_one_workspace(B):
     """100 back-to-back calls on one workspace (its words must return to zero each time)
     give bit-identical results; then the same workspace serves another V."""
