@@ -1519,53 +1519,74 @@ __device__ __forceinline__ void gamma_groups(const Params& p, GammaLds& GL) {
 __device__ __forceinline__ void unit_estimate(const Params& p, int b, Lds& L) {
   const int tid = threadIdx.x, K = p.K, N = p.N;
   const int J = max(1, min(K, kRowCap / (N + 1)));
+  const int nw = p.S * kWaves;  // gamma words of a (position, drafter) pair: one per (slice, wave)
   // [NB] Key design 2 (reading: L = 1 + sum_k gamma_k prod_{j<k} a_j) and Key design 3 (f = K + 1 - L)
   double Lh = 1.0, prod = 1.0;
   for (int k0 = 0; k0 < K; k0 += J) {
     const int nk = min(J, K - k0);
-    // gamma of the chunk's (position, drafter) pairs: one pair per thread
-    if (tid < nk * N) {
-      const int kk = k0 + tid / N, i = tid % N;
-      const int nw = p.S * kWaves;  // one word per (slice, wave) of the group members
-      unsigned long long* src = p.gpart + ((static_cast<size_t>(b) * K + kk) * N + i) * nw;
-      double g = 0.0;
-      for (int x0 = 0; x0 < nw; x0 += 8) {
-        unsigned long long w[8];
+    const int npair = nk * N;  // pair tid = (position k0 + tid / N, drafter tid % N)
+    const int kl = tid / N, di = tid - kl * N, kk = k0 + kl;
+    // the pair's trajectory token and its two logits, issued first so that these
+    // loads overlap the words' below
+    const bool has_tok = tid < npair && kk < K - 1;
+    const int x = has_tok ? p.traj[b * K + kk] : 0;
+    const bool x_ok = x >= 0 && x < p.V;
+    uint32_t ztb = 0u, zdb = 0u;
+    if (has_tok && x_ok) {
+      ztb = target_row(p, b, kk)[x];
+      zdb = draft_row(p, b, di, kk)[x];
+    }
+    // gamma words of the chunk's pairs (contiguous: pair by pair, nw each), read by
+    // the whole workgroup through LDS, kStage at a time; thread tid < npair sums its
+    // pair's words in order
+    const unsigned long long* src = p.gpart + (static_cast<size_t>(b) * K + k0) * N * nw;
+    const int total = npair * nw;
+    double g = 0.0;
+    for (int q0 = 0; q0 < total; q0 += kStage) {
+      const int nq = min(kStage, total - q0);
+      unsigned long long w[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] = x0 + e < nw ? ld_agent_u64(src + x0 + e) : kValid;
-        bool missing = false;
+      for (int e = 0; e < 8; ++e) w[e] = ld_agent_u64(const_cast<unsigned long long*>(src) + q0 + min(tid + e * kThreads, nq - 1));
+      bool missing = false;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) missing |= w[e] == 0ull;
-        if (missing) {  // not yet published (rare): wait for each word of the batch in turn
-          for (int e = 0; e < 8 && x0 + e < nw; ++e) g += unpack_f64(poll_word(p.flags, src + x0 + e));
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) g += unpack_f64(w[e]);
-        }
+      for (int e = 0; e < 8; ++e) {
+        const int q = tid + e * kThreads;
+        if (q < nq) L.m.stage[q] = w[e];
+        missing |= q < nq && w[e] == 0ull;
       }
+      if (missing) {  // not yet published (rare): wait for each missing word
+        for (int q = tid; q < nq; q += kThreads)
+          if (L.m.stage[q] == 0ull) L.m.stage[q] = poll_word(p.flags, const_cast<unsigned long long*>(src) + q0 + q);
+      }
+      __syncthreads();
+      if (tid < npair) {
+        const int lo = max(tid * nw, q0), hi = min((tid + 1) * nw, q0 + nq);
+        for (int q = lo; q < hi; ++q) g += unpack_f64(L.m.stage[q - q0]);
+      }
+      __syncthreads();
+    }
+    if (tid < npair) {
       L.gsum[tid] = g;
-      p.gamma[(b * K + kk) * N + i] = static_cast<float>(g);
+      p.gamma[(b * K + kk) * N + di] = static_cast<float>(g);
     }
     // statistics of the chunk's rows: (target kk, drafter 0 kk, ..., drafter N-1 kk)
     merge_rows(p, b, nk * (N + 1),
                [&](int i) {
-                 const int kk = k0 + i / (N + 1), m = i % (N + 1);
-                 return m == 0 ? kk : p.RT + (m - 1) * K + kk;
+                 const int k2 = k0 + i / (N + 1), m = i % (N + 1);
+                 return m == 0 ? k2 : p.RT + (m - 1) * K + k2;
                },
                L.m);
     // realised-token acceptance a = min(1, pd(x)/pt(x)) at x = traj[kk]
-    if (tid < nk * N) {
-      const int kl = tid / N, i = tid % N, kk = k0 + kl;
+    if (tid < npair) {
       double a = 1.0;
       if (kk < K - 1) {
-        const int x = p.traj[b * K + kk];
-        if (x < 0 || x >= p.V) {
+        if (!x_ok) {
           a = __builtin_nan("");
         } else {
           const RowStats st{L.m.rk[kl * (N + 1)], L.m.rs[kl * (N + 1)]};
-          const RowStats sd{L.m.rk[kl * (N + 1) + 1 + i], L.m.rs[kl * (N + 1) + 1 + i]};
-          const double ptx = token_prob(bf16_at(target_row(p, b, kk), x), p.c, st);
-          const double pdx = token_prob(bf16_at(draft_row(p, b, i, kk), x), p.c, sd);
+          const RowStats sd{L.m.rk[kl * (N + 1) + 1 + di], L.m.rs[kl * (N + 1) + 1 + di]};
+          const double ptx = token_prob(__uint_as_float(ztb << 16), p.c, st);
+          const double pdx = token_prob(__uint_as_float(zdb << 16), p.c, sd);
           a = ptx > 0.0 ? fmin(1.0, pdx / ptx) : (pdx > 0.0 ? 1.0 : 0.0);
         }
       }
@@ -1573,9 +1594,9 @@ __device__ __forceinline__ void unit_estimate(const Params& p, int b, Lds& L) {
     }
     __syncthreads();
     if (tid < N) {
-      for (int kl = 0; kl < nk; ++kl) {
-        Lh += L.gsum[kl * N + tid] * prod;
-        prod *= L.arat[kl * N + tid];
+      for (int k1 = 0; k1 < nk; ++k1) {
+        Lh += L.gsum[k1 * N + tid] * prod;
+        prod *= L.arat[k1 * N + tid];
       }
     }
     __syncthreads();
@@ -1720,8 +1741,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __syncthreads();
     run_unit1<MULTI>(p, u, u == g ? pre_n : kNoToken, L);
   }
+  // the estimator units start on the workgroups after the draw units' (workgroup
+  // g takes units (g - T1) mod G, + G, ...), so that where the grid has room they
+  // run beside the draws rather than after them
   const int T2 = p.B * p.P2;
-  for (int v = g; v < T2; v += G) {
+  for (int v = (g + G - T1 % G) % G; v < T2; v += G) {
     __syncthreads();
     run_unit2(p, v, L);
   }
