@@ -693,19 +693,16 @@ __device__ __forceinline__ void decide(const Params& p, int b, bool write_output
   const bool bad_sel = drafter < 0 || drafter >= p.N;
   const int dsafe = bad_sel ? 0 : drafter;
   // thread t < K: the drafted token of position t, its uniform and its two logits,
-  // fetched first so that these loads overlap the statistics loads
-  int n = -1;
-  float rr = 0.0f, zt = 0.0f, zd = 0.0f;
-  bool tok_ok = false;
-  if (t < K) {
-    n = pre_n != kNoToken ? pre_n : p.tokens[b * K + t];
-    rr = p.r[b * K + t];
-    tok_ok = !bad_sel && n >= 0 && n < V;
-    if (tok_ok) {
-      zt = bf16_at(target_row(p, b, t), n);
-      zd = bf16_at(draft_row(p, b, drafter, t), n);
-    }
-  }
+  // loaded first so that these loads overlap the statistics words' (every thread
+  // loads, those past K position K - 1's, and the logits stay bf16 patterns until
+  // the decisions, so that no wait for them comes before the words' loads)
+  const int tc = min(t, K - 1);
+  const int n = pre_n != kNoToken ? pre_n : p.tokens[b * K + tc];
+  const bool tok_ok = t < K && !bad_sel && n >= 0 && n < V;
+  const int nc = min(max(n, 0), V - 1);
+  const float rr = p.r[b * K + tc];
+  const uint32_t zt_bits = target_row(p, b, tc)[nc];
+  const uint32_t zd_bits = draft_row(p, b, dsafe, tc)[nc];
   // rows 0..K-1: target rows 0..K-1; rows K..2K-1: the drafter's rows 0..K-1
   merge_rows(p, b, 2 * K, [&](int i) { return i < K ? i : p.RT + dsafe * K + (i - K); }, L.m);
   // threads t < K (all in wave 0): the accept test of position t
@@ -716,6 +713,7 @@ __device__ __forceinline__ void decide(const Params& p, int b, bool write_output
     if (tok_ok) {
       const RowStats st{L.m.rk[t], L.m.rs[t]};
       const RowStats sd{L.m.rk[K + t], L.m.rs[K + t]};
+      const float zt = __uint_as_float(zt_bits << 16), zd = __uint_as_float(zd_bits << 16);
       // [CA] Key design 3 with the verifier's probability c of the candidate; delta = 0 is SpS.
       ct = fmin(token_prob(zt, p.c, st), 1.0);
       const double cd = token_prob(zd, p.c, sd);
@@ -1069,7 +1067,7 @@ __device__ __forceinline__ void target_h_draw(const Params& p, int b, const Deci
 
 // Draw unit x of sequence b.  Unit 0 also writes the per-position outputs, the
 // outputs of a sequence with no valid draw, and the outputs of a draw with no
-// mass.  `pre_n`: the drafted token of position threadIdx.x, loaded ahead of
+// mass.  `pre_n`: the drafted token of position min(threadIdx.x, K - 1), loaded ahead of
 // time, or kNoToken.  MULTI: units of several slices (a kernel instance of its
 // own, so that the other launches keep the single-slice code alone).
 template <bool KL = false, bool MULTI = false>
@@ -1730,11 +1728,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   Lds& L = KL.units;
   const int G = gridDim.x, g = blockIdx.x;
   const int T1 = p.B * p.P1;
-  // the drafted token of this workgroup's first draw unit, loaded now so that the
-  // unit's decisions do not wait for it (nothing waits for the load here)
+  // the drafted token of this workgroup's first draw unit (position
+  // min(threadIdx.x, K - 1)), loaded now so that the unit's decisions do not wait
+  // for it (nothing waits for the load here)
   int pre_n = kNoToken;
-  if (g < T1 && is_draw_unit(p, g) && static_cast<int>(threadIdx.x) < p.K)
-    pre_n = p.tokens[(g / p.P1) * p.K + static_cast<int>(threadIdx.x)];
+  if (g < T1 && is_draw_unit(p, g)) pre_n = p.tokens[(g / p.P1) * p.K + min(static_cast<int>(threadIdx.x), p.K - 1)];
   if (p.mode == MODE_GAMMA) gamma_groups(p, KL.gamma);
   static_phase(p, G, g);
   for (int u = g; u < T1; u += G) {
@@ -1763,10 +1761,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ Lds L;
   const int G = gridDim.x, g = blockIdx.x;
   const int T1 = p.B * p.P1;
-  // the drafted token of this workgroup's first draw unit, loaded now so that the
-  // unit's decisions do not wait for it (nothing waits for the load here)
+  // the drafted token of this workgroup's first draw unit (position
+  // min(threadIdx.x, K - 1)), loaded now so that the unit's decisions do not wait
+  // for it (nothing waits for the load here)
   int pre_n = kNoToken;
-  if (g < T1 && static_cast<int>(threadIdx.x) < p.K) pre_n = p.tokens[(g / p.P1) * p.K + static_cast<int>(threadIdx.x)];
+  if (g < T1) pre_n = p.tokens[(g / p.P1) * p.K + min(static_cast<int>(threadIdx.x), p.K - 1)];
   static_phase(p, G, g);
   for (int u = g; u < T1; u += G) {
     __syncthreads();
