@@ -388,6 +388,35 @@ int hedge_censored_update(double* state, double* weights, double* queue_loss, in
                           int Q, int T, spec_stream_t stream);
 
 /*
+ * spec_hedgespec_round -- one whole HedgeSpec round in one launch ([NB] overall
+ * framework: the learner selects a drafter per sequence, that drafter's chunk is
+ * verified, and every drafter is evaluated on the verified trajectory; Key
+ * designs 1-3).  It computes exactly what hedge_censored_update (steps 1-4 above,
+ * with these state arguments) followed by the fused spec_counterfactual_gamma
+ * with sel = this round's selections computes, but the learner step runs inside
+ * the gamma launch: the first draw unit of each sequence takes it and hands the
+ * drafter to the sequence's other draw units, so a round is one kernel and no
+ * node gap.
+ *
+ * loss [B][N] and accepted_len [B] are both the previous round's outputs, which
+ * the learner reads, and this round's, which the launch writes (the estimator
+ * waits for the learner before it overwrites loss).  sel [B] receives this
+ * round's drafters.  Every other argument is as in spec_counterfactual_gamma
+ * (fused form: draft_tokens, r_accept, u_resample, accepted_len and out_token
+ * required) and hedge_censored_update; the workspace is a
+ * spec_workspace_bytes(B, K, N) one.  Status codes as there.
+ */
+int spec_hedgespec_round(const spec_bf16* target, int64_t target_row_stride, int target_rows_per_seq,
+                         const spec_bf16* drafts, int64_t draft_row_stride, int64_t drafter_stride,
+                         const int32_t* traj_tokens, int B, int K, int N, int V, float temperature, float* gamma,
+                         float* est_len, float* loss, const int32_t* draft_tokens, const float* r_accept,
+                         const float* u_resample, int32_t* accepted_len, int32_t* out_token, uint8_t* accept_mask,
+                         double* state, double* weights, double* queue_loss, int32_t* queue_tokens, int32_t* round,
+                         int learner, float eta, float loss_scale, const float* v_select, int32_t* sel,
+                         int32_t* sel_hist, int Q, int T, void* workspace, size_t workspace_bytes,
+                         spec_stream_t stream);
+
+/*
  * spec_acceptance_loss -- [NB] Key design 3's loss when the acceptance probability
  * is optimised: f = 1 - gamma at every position, a chunk's K positions summed:
  *   loss[b][i] = sum_k (1 - gamma[b][k][i])   (fp64 sum, stored as float32)

@@ -53,6 +53,8 @@ _SIGNATURES = {
                                        _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "hedge_update": (_I, [_P, _P, _P, _P, _F, _P, _P, _I, _I, _P]),
     "hedge_censored_update": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _F, _F, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "spec_hedgespec_round": (_I, [_P, _I64, _I, _P, _I64, _I64, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P,
+                                  _P, _P, _P, _P, _P, _P, _P, _P, _I, _F, _F, _P, _P, _P, _I, _I, _P, _SZ, _P]),
 }
 
 
@@ -381,6 +383,61 @@ def prepare_counterfactual_gamma(target, drafts, traj_tokens, temperature: float
     inputs = {"target": t, "drafts": d, "traj_tokens": traj, "sel": sel, "draft_tokens": draft_tokens,
               "r_accept": r_accept, "u_resample": u_resample}
     return Launcher("spec_counterfactual_gamma", args, out, keep, ws, inputs)
+
+
+def prepare_hedgespec_round(target, drafts, traj_tokens, temperature: float, learner, *, draft_tokens,
+                            r_accept, u_resample, workspace=None, with_mask: bool = True,
+                            outputs: Optional[dict] = None, strict: bool = False) -> Launcher:
+    """spec_hedgespec_round with its tensors fixed: one HedgeSpec round in one launch.
+    `learner` holds the censoring learner's device state (state, weights, queue_loss,
+    queue_tokens, round, sel, sel_hist, v, K, learner, eta, loss_scale: a
+    hedge.CensoredLearner); outputs["loss"] and outputs["accepted_len"] are the
+    previous round's for the learner and this round's after the launch."""
+    _need_cuda(target, drafts, traj_tokens, draft_tokens, r_accept, u_resample)
+    N, B, K, V = drafts.shape
+    if target.shape[0] != B or target.shape[2] != V:
+        raise ValueError("target must be [B, R, V]")
+    R = target.shape[1]
+    t, ts = _rows(target, strict, "target")
+    d, ds = _rows(drafts, strict, "drafts")
+    drafter_stride = ds * B * K
+    traj = _as(traj_tokens, torch.int32, strict, "traj_tokens")
+    dev = target.device
+    if outputs is None:
+        out = {
+            "gamma": torch.empty((B, K, N), dtype=torch.float32, device=dev),
+            "est_len": torch.empty((B, N), dtype=torch.float32, device=dev),
+            "loss": torch.zeros((B, N), dtype=torch.float32, device=dev),
+            "accepted_len": torch.zeros(B, dtype=torch.int32, device=dev),
+            "out_token": torch.empty(B, dtype=torch.int32, device=dev),
+            "accept_mask": torch.empty((B, K), dtype=torch.uint8, device=dev) if with_mask else None,
+        }
+    else:
+        out = outputs
+    draft_tokens = _as(draft_tokens, torch.int32, strict, "draft_tokens")
+    r_accept = _as(r_accept, torch.float32, strict, "r_accept")
+    u_resample = _as(u_resample, torch.float32, strict, "u_resample")
+    L = learner
+    for x, dt in ((L.state, torch.float64), (L.weights, torch.float64), (L.queue_loss, torch.float64),
+                  (L.queue_tokens, torch.int32), (L.round, torch.int32), (L.v, torch.float32),
+                  (L.sel, torch.int32), (L.sel_hist, torch.int32)):
+        if x.dtype != dt or not x.is_contiguous() or not x.is_cuda:
+            raise ValueError(f"learner state: expected a contiguous {dt} device tensor")
+    if int(L.K) != K or tuple(L.state.shape) != (B, N):
+        raise ValueError("the learner's shape does not match the round's")
+    Q = L.queue_tokens.shape[1]
+    T = L.v.shape[0]
+    ws = make_workspace(B, K, N, dev) if workspace is None else workspace
+    args = (_ptr(t), ts, R, _ptr(d), ds, drafter_stride, _ptr(traj), B, K, N, V, float(temperature),
+            _ptr(out["gamma"]), _ptr(out["est_len"]), _ptr(out["loss"]), _ptr(draft_tokens), _ptr(r_accept),
+            _ptr(u_resample), _ptr(out["accepted_len"]), _ptr(out["out_token"]), _ptr(out.get("accept_mask")),
+            _ptr(L.state), _ptr(L.weights), _ptr(L.queue_loss), _ptr(L.queue_tokens), _ptr(L.round),
+            int(L.learner), float(L.eta), float(L.loss_scale), _ptr(L.v), _ptr(L.sel), _ptr(L.sel_hist), Q, T,
+            _ptr(ws), ws.numel())
+    keep = (t, d, traj, draft_tokens, r_accept, u_resample, ws, out, L)
+    inputs = {"target": t, "drafts": d, "traj_tokens": traj, "draft_tokens": draft_tokens,
+              "r_accept": r_accept, "u_resample": u_resample}
+    return Launcher("spec_hedgespec_round", args, out, keep, ws, inputs)
 
 
 def hedge_update(cum_regret, weights, loss, loss_scale: float, *, has_loss=None, v_select=None,

@@ -76,6 +76,7 @@ constexpr int kStage = 8 * kThreads;  // statistics words staged in LDS at once
 constexpr int kRowCap = 256;          // merged rows held in LDS at once
 constexpr int kNoK = INT32_MIN;       // statistics word of a share with no finite logit
 constexpr int kNoToken = INT32_MIN;   // no preloaded drafted token
+constexpr int kMaxQueue = 256;        // slots of a learner's delayed-feedback queue
 
 // Everything a lane needs to turn logits into sampling weights.  Weights are kept
 // in units of 1/st (st the target row's sum): an inverse-CDF draw depends only on
@@ -89,6 +90,25 @@ struct WeightCtx {
   int n;           // candidate token
   int special;     // 1: token n carries gamma* (delta > 0)
   int mode;        // W_RESID, W_TARGET_H, W_TARGET
+};
+
+// The censoring learner's round (hedge_censored_update, and the learner step of a
+// fused HedgeSpec round): its state, the previous round's outputs it reads, and
+// the selections it writes.
+struct CensoredArgs {
+  double* S;          // [B][N] the learner's state (regret, or cumulative loss)
+  double* W;          // [B][N] weights
+  double* qloss;      // [B][Q][N] queued scaled losses
+  int32_t* qtok;      // [B][Q] tokens verified since each queued round (-1: empty slot)
+  int32_t* round;     // [B] rounds done
+  const float* loss;  // [B][N] the previous round's losses
+  const int32_t* alen;  // [B] the previous round's accepted lengths
+  int K, learner;
+  float eta, scale;
+  const float* v;     // [T][B] selection uniforms
+  int32_t* sel;       // [B] out: this round's drafters
+  int32_t* sel_hist;  // [T][B] out
+  int B, N, Q, T;
 };
 
 struct Params {
@@ -140,6 +160,11 @@ struct Params {
   unsigned long long* cand;   // draft-tree calls: [B][K][N][pieces][topk] piece records
   unsigned long long* pstat;  // gamma calls: [slots][S][kWaves] a slot's private statistics words (prefix target row)
   uint32_t* pdone;            // gamma calls: [slots] tickets of the members done with those words
+  // fused HedgeSpec rounds (spec_hedgespec_round): the learner step runs in each
+  // sequence's first draw unit; lrn.round == nullptr otherwise
+  CensoredArgs lrn;
+  unsigned long long* selw;  // [B] the round's drafter + 1, published by that unit to the sequence's others
+  unsigned long long* lrnw;  // [B] non-zero once the learner has read the previous round's loss
 };
 
 __device__ __forceinline__ const uint4* as_chunks(const uint16_t* row) { return reinterpret_cast<const uint4*>(row); }
@@ -209,6 +234,13 @@ __device__ __forceinline__ unsigned long long poll_word(uint32_t* flags, unsigne
       return 0ull;
     }
   }
+}
+
+// LDS written by some lanes of this wave is then read by others: the writes
+// complete first.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
 }
 
 // ---------------------------------------------------------------------------
@@ -587,6 +619,7 @@ __device__ __forceinline__ void row_subtiles(const uint16_t* trow, const uint16_
 
 struct Decision {
   WeightCtx w;
+  int drafter;   // the drafter whose rows are verified
   int A;         // accepted length; -1 invalid
   int draw_row;  // position of the draw row (A, or K for the bonus)
   int pair;      // 1: residual over (target A, draft A); 0: pt of target row K
@@ -607,9 +640,48 @@ struct Lds {
   double gsum[kRowCap];
   double arat[kRowCap];
   int flag;
+  int32_t qtok[kWaves][kMaxQueue];  // fused HedgeSpec rounds: each wave's learner queue counts
 };
 
 __device__ __forceinline__ int draw_drafter(const Params& p, int b) { return p.mode == MODE_VERIFY ? 0 : p.sel[b]; }
+
+__device__ __forceinline__ int censored_round(const CensoredArgs& a, int b, int32_t* tok);
+
+// The drafter whose rows unit x of sequence b verifies: 0 in verify calls, sel[b]
+// in gamma calls, and in a fused HedgeSpec round the learner's choice for this
+// round, which learner_steps published at the kernel's start.
+template <bool LEARN>
+__device__ __forceinline__ int unit_drafter(const Params& p, int b, int x, Lds& L) {
+  if (p.mode == MODE_VERIFY) return 0;
+  if (!LEARN) return p.sel[b];
+  if (threadIdx.x == 0) {
+    const unsigned long long w = poll_word(p.flags, &p.selw[b]);
+    L.flag = static_cast<int>(static_cast<uint32_t>(w)) - 1;  // a timeout leaves -1: no valid drafter
+  }
+  __syncthreads();
+  const int d = L.flag;
+  __syncthreads();
+  return d;
+}
+
+// Fused HedgeSpec rounds ([NB] overall framework: select, then verify): the
+// learner steps of every sequence, taken at the kernel's start by the waves of
+// gamma slot 0 (workgroups 0 .. S-1, which take no gamma rows: row_chunk with
+// skip0), wave w of workgroup g taking sequences g kWaves + w, + S kWaves, ...
+// Each publishes the sequence's drafter (+1) to its draw units and, once it has
+// read the previous round's loss, the word that lets the estimator overwrite it.
+__device__ __forceinline__ void learner_steps(const Params& p, Lds& L) {
+  const int S = p.S, g = blockIdx.x, w = wave_id();
+  const int span = (gridDim.x / S >= 2 ? S : static_cast<int>(gridDim.x)) * kWaves;
+  for (int b = g * kWaves + w; b < p.B; b += span) {
+    const int pick = censored_round(p.lrn, b, L.qtok[w]);
+    if (lane_id() == 0) {
+      st_agent_u64(&p.lrnw[b], 1ull);
+      st_agent_u64(&p.selw[b], static_cast<unsigned long long>(static_cast<uint32_t>(pick)) + 1ull);
+    }
+    wave_lds_sync();
+  }
+}
 
 // One outcome's part of a two-outcome KL divergence, c * phi(1 + x) with
 // phi(t) = t ln t - t + 1 >= 0 and x = (g - c) / c: `plain` is its direct form
@@ -681,15 +753,15 @@ __host__ __device__ inline double kl_divergence(double g, double c) {
   return kl_share(c, x, g * l1 - d) + kl_share(c1, y, (1.0 - g) * log1p(y) + d);
 }
 
-// Merge the statistics of target rows 0..K-1 and drafter `drafter`'s rows 0..K-1,
+// Merge the statistics of target rows 0..K-1 and drafter `drafter`'s rows 0..K-1
+// (0 for verify calls; a drafter id out of range makes the sequence invalid),
 // take every accept decision, and describe the draw (the bonus row K has no
 // statistics: its draw finds its own references).  Writes accept_mask and
 // gamma_star when `write_outputs`.  The result is in L.dl.d after the call.
 template <bool KL = false>
-__device__ __forceinline__ void decide(const Params& p, int b, bool write_outputs, int pre_n, Lds& L) {
+__device__ __forceinline__ void decide(const Params& p, int b, bool write_outputs, int pre_n, int drafter, Lds& L) {
   const int K = p.K, V = p.V;
   const int t = threadIdx.x;
-  const int drafter = draw_drafter(p, b);
   const bool bad_sel = drafter < 0 || drafter >= p.N;
   const int dsafe = bad_sel ? 0 : drafter;
   // thread t < K: the drafted token of position t, its uniform and its two logits,
@@ -745,6 +817,7 @@ __device__ __forceinline__ void decide(const Params& p, int b, bool write_output
     const int nA = __builtin_amdgcn_readlane(n, A < K ? A : 0);
     if (t == 0) {
       Decision d;
+      d.drafter = dsafe;
       WeightCtx w;
       w.c = p.c;
       w.kd = 0.0f;
@@ -818,6 +891,7 @@ __device__ __forceinline__ void finish_sequence(const Params& p, int b, bool cle
     unsigned long long* w = part_row(p, b, 0);
     const int n = p.R * p.S * kWaves;
     for (int q = threadIdx.x; q < n; q += kThreads) st_agent_u64(w + q, 0ull);
+    if (p.lrn.round != nullptr && threadIdx.x == 0) st_agent_u64(&p.selw[b], 0ull);  // every draw unit has read it
   }
   __syncthreads();
 }
@@ -946,7 +1020,7 @@ template <int MODE, bool SPECIAL, bool KL = false, bool MULTI = false>
 __device__ __forceinline__ int draw_slice(const Params& p, int b, int x, Decision& d, Lds& L) {
   const int tid = threadIdx.x, wave = wave_id();
   const uint16_t* trow = target_row(p, b, d.draw_row);
-  const uint16_t* drow = d.pair ? draft_row(p, b, draw_drafter(p, b), d.draw_row) : trow;
+  const uint16_t* drow = d.pair ? draft_row(p, b, d.drafter, d.draw_row) : trow;
   const uint32_t row_bytes = static_cast<uint32_t>((p.V + kVec - 1) / kVec) * 16u;
   const __amdgpu_buffer_rsrc_t tr = row_buffer(trow, row_bytes);
   const __amdgpu_buffer_rsrc_t dr = row_buffer(drow, row_bytes);
@@ -1070,9 +1144,10 @@ __device__ __forceinline__ void target_h_draw(const Params& p, int b, const Deci
 // mass.  `pre_n`: the drafted token of position min(threadIdx.x, K - 1), loaded ahead of
 // time, or kNoToken.  MULTI: units of several slices (a kernel instance of its
 // own, so that the other launches keep the single-slice code alone).
-template <bool KL = false, bool MULTI = false>
+// LEARN: a fused HedgeSpec round (the learner step in the sequence's first unit).
+template <bool KL = false, bool MULTI = false, bool LEARN = false>
 __device__ __forceinline__ void unit_draw(const Params& p, int b, int x, int pre_n, Lds& L) {
-  decide<KL>(p, b, x == 0, pre_n, L);
+  decide<KL>(p, b, x == 0, pre_n, unit_drafter<LEARN>(p, b, x, L), L);
   Decision d = L.dl.d;
   // exact-KL gamma* outputs where the draw does not find them (no residual draw)
   if (KL && x == 0 && p.delta > 0.0 && p.gamma_star && !(d.A >= 0 && d.pair)) kl_positions(p, b, true, -1, L);
@@ -1294,11 +1369,15 @@ __host__ __device__ inline int64_t slot_weights(int q, int S, int ncu, int P) {
   return w;
 }
 
-__host__ __device__ inline RowChunk row_chunk(int64_t J, int R1, int Q, int slot, int S, int ncu, int P) {
+// skip0 (Q >= 2): slot 0 takes no rows (in a fused HedgeSpec round its members
+// take the learner steps instead) and the other slots share them as above.
+__host__ __device__ inline RowChunk row_chunk(int64_t J, int R1, int Q, int slot, int S, int ncu, int P,
+                                              bool skip0 = false) {
   RowChunk c;
-  const int64_t WQ = slot_weights(Q, S, ncu, P);
-  c.j0 = J * slot_weights(slot, S, ncu, P) / WQ;
-  c.j1 = J * slot_weights(slot + 1, S, ncu, P) / WQ;
+  const int64_t w0 = skip0 && Q >= 2 ? slot_weights(1, S, ncu, P) : 0;
+  const int64_t WQ = slot_weights(Q, S, ncu, P) - w0;
+  c.j0 = J * max(slot_weights(slot, S, ncu, P) - w0, static_cast<int64_t>(0)) / WQ;
+  c.j1 = J * max(slot_weights(slot + 1, S, ncu, P) - w0, static_cast<int64_t>(0)) / WQ;
   c.prefix = c.j0 < c.j1 && (c.j0 % R1) != 0 ? 1 : 0;
   c.njobs = c.j0 < c.j1 ? static_cast<int>(c.j1 - c.j0) + c.prefix : 0;
   return c;
@@ -1329,7 +1408,7 @@ __device__ __forceinline__ void gamma_member(const Params& p, GammaLds& GL, int 
   const int tid = threadIdx.x;
   // dispatch slots as phase 0 counts them (all of them in the grid, else one)
   const int P = (p.slots >= 1 && p.slots <= kMaxSlots && p.ncu * p.slots == static_cast<int>(gridDim.x)) ? p.slots : 1;
-  const RowChunk ch = row_chunk(static_cast<int64_t>(nG) * R1, R1, Q, slot, S, p.ncu, P);
+  const RowChunk ch = row_chunk(static_cast<int64_t>(nG) * R1, R1, Q, slot, S, p.ncu, P, p.lrn.round != nullptr);
   if (ch.njobs == 0) return;
   const int prefix = ch.prefix, njobs = ch.njobs;
   unsigned long long* own_words = p.pstat + static_cast<size_t>(slot) * S * kWaves;
@@ -1599,6 +1678,16 @@ __device__ __forceinline__ void unit_estimate(const Params& p, int b, Lds& L) {
     }
     __syncthreads();
   }
+  if (p.lrn.round != nullptr) {
+    // fused HedgeSpec round: the learner reads the previous round's loss from the
+    // same buffer; overwrite it only once the learner is done with it (its only
+    // reader here: clear the word)
+    if (tid == 0) {
+      poll_word(p.flags, &p.lrnw[b]);
+      st_agent_u64(&p.lrnw[b], 0ull);
+    }
+    __syncthreads();
+  }
   if (tid < N) {
     p.est_len[b * N + tid] = static_cast<float>(Lh);
     p.loss[b * N + tid] = static_cast<float>(static_cast<double>(K + 1) - Lh);
@@ -1615,10 +1704,10 @@ __device__ __forceinline__ void unit_estimate(const Params& p, int b, Lds& L) {
 
 __device__ __forceinline__ bool is_draw_unit(const Params& p, int u) { return p.P1 > 0; }
 
-template <bool MULTI>
+template <bool MULTI, bool LEARN>
 __device__ __forceinline__ void run_unit1(const Params& p, int u, int pre_n, Lds& L) {
   const int b = u / p.P1;
-  unit_draw<false, MULTI>(p, b, u - b * p.P1, pre_n, L);
+  unit_draw<false, MULTI, LEARN>(p, b, u - b * p.P1, pre_n, L);
 }
 
 __device__ __forceinline__ void run_unit2(const Params& p, int v, Lds& L) { unit_estimate(p, v / p.P2, L); }
@@ -1722,7 +1811,9 @@ union KernelLds {
 };
 
 // MULTI: draw units of several slices (fused calls whose B S exceeds the grid).
-template <bool MULTI>
+// LEARN: fused HedgeSpec rounds (spec_hedgespec_round), an instance of its own so
+// that the other gamma calls keep the leaner code.
+template <bool MULTI, bool LEARN = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gamma_kernel(Params p) {
   __shared__ KernelLds KL;
   Lds& L = KL.units;
@@ -1733,11 +1824,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // for it (nothing waits for the load here)
   int pre_n = kNoToken;
   if (g < T1 && is_draw_unit(p, g)) pre_n = p.tokens[(g / p.P1) * p.K + min(static_cast<int>(threadIdx.x), p.K - 1)];
+  if (LEARN) {
+    // slot 0's workgroups (all of the grid's, when it holds one slot) take the
+    // learner steps first; their LDS is then handed to the groups
+    if (g < (gridDim.x / p.S >= 2 ? p.S : static_cast<int>(gridDim.x))) learner_steps(p, L);
+    __syncthreads();
+  }
   if (p.mode == MODE_GAMMA) gamma_groups(p, KL.gamma);
   static_phase(p, G, g);
   for (int u = g; u < T1; u += G) {
     __syncthreads();
-    run_unit1<MULTI>(p, u, u == g ? pre_n : kNoToken, L);
+    run_unit1<MULTI, LEARN>(p, u, u == g ? pre_n : kNoToken, L);
   }
   // the estimator units start on the workgroups after the draw units' (workgroup
   // g takes units (g - T1) mod G, + G, ...), so that where the grid has room they
@@ -1862,12 +1959,6 @@ __device__ __forceinline__ int wave_sum_i(int v) {
   return v;
 }
 
-// LDS written by some lanes of this wave is then read by others: the writes
-// complete first.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-}
 
 // The piece's keys at or above `tau` (nonzero), counted over the wave.
 __device__ __forceinline__ int wave_count_at_least(const uint4 v[kTilesPerSlice], int base, int V, uint32_t tau) {
@@ -2413,7 +2504,6 @@ __global__ __launch_bounds__(64) void hedge_exp_kernel(double* L, double* W, con
 // scaled loss (fp64) and the usable round (-1: free); the usable rounds are worked
 // on in LDS during the call.  Delays of at most Q - 2 rounds keep a slot from
 // being reused before its loss is applied (Q >= 2K + 2 covers the note's 2K).
-constexpr int kMaxQueue = 256;
 __global__ __launch_bounds__(64) void hedge_queue_kernel(double* R, double* W, double* qloss, int32_t* qdue,
                                                          int32_t* round, const float* loss, const int32_t* delays,
                                                          float scale, const float* v, int32_t* sel, int32_t* sel_hist,
@@ -2493,26 +2583,25 @@ __global__ __launch_bounds__(64) void hedge_queue_kernel(double* R, double* W, d
 // Hedge with rate eta (state: cumulative loss).
 enum : int { LEARNER_NORMALHEDGE = 0, LEARNER_HEDGE = 1 };
 
-__global__ __launch_bounds__(64) void hedge_censored_kernel(double* S, double* W, double* qloss, int32_t* qtok,
-                                                            int32_t* round, const float* loss, const int32_t* alen,
-                                                            int K, int learner, float eta, float scale, const float* v,
-                                                            int32_t* sel, int32_t* sel_hist, int B, int N, int Q, int T) {
-  const int b = blockIdx.x;
-  const int i = threadIdx.x;
+// One wave (lane i: drafter i), sequence b: one round of the censoring learner.
+// `tok` (LDS, Q entries) holds the queue's counts during the round.  Returns the
+// round's drafter (sel[b] as it stands once the schedules are exhausted).
+__device__ __forceinline__ int censored_round(const CensoredArgs& a, int b, int32_t* tok) {
+  const int i = lane_id();
+  const int N = a.N, Q = a.Q, K = a.K;
   const bool act = i < N;
   const int idx = b * N + i;
-  const int t = round[b];
-  if (t >= T) return;  // the schedules are exhausted: nothing more
-  __shared__ int32_t tok[kMaxQueue];
-  double Si = act ? S[idx] : 0.0, wi = act ? W[idx] : 0.0;
-  int32_t* gtok = qtok + static_cast<size_t>(b) * Q;
-  double* ql = qloss + static_cast<size_t>(b) * Q * N;
-  const int add = t > 0 && alen[b] >= 0 ? alen[b] + 1 : 0;
+  const int t = a.round[b];
+  if (t >= a.T) return a.sel[b];  // the schedules are exhausted: nothing more
+  double Si = act ? a.S[idx] : 0.0, wi = act ? a.W[idx] : 0.0;
+  int32_t* gtok = a.qtok + static_cast<size_t>(b) * Q;
+  double* ql = a.qloss + static_cast<size_t>(b) * Q * N;
+  const int add = t > 0 && a.alen[b] >= 0 ? a.alen[b] + 1 : 0;
   for (int q = i; q < Q; q += 64) {
     const int32_t c = gtok[q];
     tok[q] = c >= 0 ? min(c + add, K) : -1;  // counts stop at K: reaching it is all that matters
   }
-  __syncthreads();
+  wave_lds_sync();
   if (t > 0) {
     // queued slots hold rounds t - 1 - Q .. t - 2; slot q holds the latest r <= t - 2 with r % Q == q
     const int newest = ((t - 2) % Q + Q) % Q;  // slot of round t - 2 (when t = 1 nothing is queued)
@@ -2528,29 +2617,35 @@ __global__ __launch_bounds__(64) void hedge_censored_kernel(double* S, double* W
       }
       if (best < 0) break;
       const double l = act ? ql[best * N + i] : 0.0;
-      if (learner == LEARNER_NORMALHEDGE)
+      if (a.learner == LEARNER_NORMALHEDGE)
         normalhedge_step(Si, wi, l, act, N);
       else
-        hedge_exp_step(Si, wi, l, static_cast<double>(eta), act);
-      __syncthreads();
+        hedge_exp_step(Si, wi, l, static_cast<double>(a.eta), act);
+      wave_lds_sync();
       if (i == 0) tok[best] = -1;
-      __syncthreads();
+      wave_lds_sync();
     }
     const int pslot = (t - 1) % Q;
-    if (act) ql[pslot * N + i] = static_cast<double>(loss[idx]) * static_cast<double>(scale);
+    if (act) ql[pslot * N + i] = static_cast<double>(a.loss[idx]) * static_cast<double>(a.scale);
     if (i == 0) tok[pslot] = 0;
-    __syncthreads();
+    wave_lds_sync();
   }
   if (act) {
-    S[idx] = Si;
-    W[idx] = wi;
+    a.S[idx] = Si;
+    a.W[idx] = wi;
   }
   for (int q = i; q < Q; q += 64) gtok[q] = tok[q];
-  const int pick = hedge_select(wi, v + static_cast<size_t>(t) * B, sel, b, N);
+  const int pick = hedge_select(wi, a.v + static_cast<size_t>(t) * a.B, a.sel, b, N);
   if (i == 0) {
-    sel_hist[static_cast<size_t>(t) * B + b] = pick;
-    round[b] = t + 1;
+    a.sel_hist[static_cast<size_t>(t) * a.B + b] = pick;
+    a.round[b] = t + 1;
   }
+  return pick;
+}
+
+__global__ __launch_bounds__(64) void hedge_censored_kernel(CensoredArgs a) {
+  __shared__ int32_t tok[kMaxQueue];
+  censored_round(a, blockIdx.x, tok);
 }
 
 // [NB] Key design 3's acceptance-probability loss of a chunk: the sum over its K
@@ -2618,7 +2713,7 @@ static Shape make_shape(int B, int K, int N, int V, int mode, int fused) {
 // Byte offsets of the workspace regions.  They depend on (B, K, N, mode) only
 // (every region is sized for the longest row), so one workspace serves every V.
 struct WsLayout {
-  size_t flags, done, part, tot, gpart, cand, pstat, pdone, total;
+  size_t flags, done, part, tot, gpart, cand, pstat, pdone, selw, lrnw, total;
 };
 
 // Most workgroups of a gamma call (its slots' private words are sized for it).
@@ -2649,6 +2744,11 @@ static WsLayout ws_layout(const Shape& s) {
   o = align256(o + (s.mode == MODE_GAMMA ? 8 * static_cast<size_t>(kMaxGrid) * kWaves : 0));
   L.pdone = o;
   o = align256(o + (s.mode == MODE_GAMMA ? 4 * static_cast<size_t>(kMaxGrid) : 0));
+  // fused HedgeSpec rounds: each sequence's drafter word and learner word
+  L.selw = o;
+  o = align256(o + (s.mode == MODE_GAMMA ? 8 * B : 0));
+  L.lrnw = o;
+  o = align256(o + (s.mode == MODE_GAMMA ? 8 * B : 0));
   L.total = o;
   return L;
 }
@@ -2669,6 +2769,8 @@ static int bind_workspace(Params& p, const Shape& s, void* ws, size_t bytes) {
   p.cand = reinterpret_cast<unsigned long long*>(base + L.cand);
   p.pstat = reinterpret_cast<unsigned long long*>(base + L.pstat);
   p.pdone = reinterpret_cast<uint32_t*>(base + L.pdone);
+  p.selw = reinterpret_cast<unsigned long long*>(base + L.selw);
+  p.lrnw = reinterpret_cast<unsigned long long*>(base + L.lrnw);
   return SPEC_OK;
 }
 
@@ -2687,7 +2789,7 @@ static int compute_units() {
 
 template <class Kernel>
 static int resident_workgroups(Kernel kernel, int which) {
-  static int cache[8][64] = {{0}};
+  static int cache[10][64] = {{0}};  // [which kernel][device]
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (dev >= 0 && dev < 64 && cache[which][dev] > 0) return cache[which][dev];
@@ -2723,7 +2825,8 @@ static int launch_flow(Params& p, const Shape& s, hipStream_t stream) {
   int grid = tree     ? resident_workgroups(tree_kernel, 3)
              : verify ? (p.kl_exact ? resident_workgroups(verify_kernel<true, false>, 2)
                                     : resident_workgroups(verify_kernel<false, false>, 0))
-                      : resident_workgroups(gamma_kernel<false>, 1);
+                      : (p.lrn.round ? resident_workgroups(gamma_kernel<false, true>, 7)
+                                     : resident_workgroups(gamma_kernel<false>, 1));
   if (grid <= 0) return SPEC_ERR_HIP;
   const int ncu = compute_units();
   const int slots = ncu > 0 && grid % ncu == 0 ? grid / ncu : 1;
@@ -2749,7 +2852,8 @@ static int launch_flow(Params& p, const Shape& s, hipStream_t stream) {
     // the instance with units of several slices holds as many workgroups
     const int g2 = verify ? (p.kl_exact ? resident_workgroups(verify_kernel<true, true>, 6)
                                         : resident_workgroups(verify_kernel<false, true>, 4))
-                          : resident_workgroups(gamma_kernel<true>, 5);
+                          : (p.lrn.round ? resident_workgroups(gamma_kernel<true, true>, 8)
+                                         : resident_workgroups(gamma_kernel<true>, 5));
     if (g2 <= 0) return SPEC_ERR_HIP;
     if (g2 < grid) grid = g2;
     if (s.mode == MODE_GAMMA && grid < s.S) return SPEC_ERR_SHAPE;
@@ -2762,6 +2866,7 @@ static int launch_flow(Params& p, const Shape& s, hipStream_t stream) {
   void (*kernel)(Params) = tree                  ? tree_kernel
                            : verify && p.kl_exact ? (multi ? verify_kernel<true, true> : verify_kernel<true, false>)
                            : verify               ? (multi ? verify_kernel<false, true> : verify_kernel<false, false>)
+                           : p.lrn.round          ? (multi ? gamma_kernel<true, true> : gamma_kernel<false, true>)
                                                   : (multi ? gamma_kernel<true> : gamma_kernel<false>);
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
@@ -2923,13 +3028,13 @@ int spec_cactus_kl_verify(const spec_bf16* verifier, int64_t verifier_row_stride
                        gamma_star, workspace, workspace_bytes, stream);
 }
 
-int spec_counterfactual_gamma(const spec_bf16* target, int64_t target_row_stride, int target_rows_per_seq,
+static int gamma_call(const spec_bf16* target, int64_t target_row_stride, int target_rows_per_seq,
                               const spec_bf16* drafts, int64_t draft_row_stride, int64_t drafter_stride,
                               const int32_t* traj_tokens, int B, int K, int N, int V, float temperature, float* gamma,
                               float* est_len, float* loss, const int32_t* sel, const int32_t* draft_tokens,
                               const float* r_accept, const float* u_resample, int32_t* accepted_len,
                               int32_t* out_token, uint8_t* accept_mask, void* workspace, size_t workspace_bytes,
-                              spec_stream_t stream) {
+                              spec_stream_t stream, const CensoredArgs* lrn) {
   int st = check_common(B, K, V, temperature);
   if (st != SPEC_OK) return st;
   if (N < 1 || N > SPEC_MAX_N) return SPEC_ERR_SHAPE;
@@ -2969,7 +3074,43 @@ int spec_counterfactual_gamma(const spec_bf16* target, int64_t target_row_stride
   p.gamma = gamma;
   p.est_len = est_len;
   p.loss = loss;
+  if (lrn != nullptr) p.lrn = *lrn;  // else p.lrn.round stays nullptr: no learner step
   return launch_flow(p, s, stream);
+}
+
+int spec_counterfactual_gamma(const spec_bf16* target, int64_t target_row_stride, int target_rows_per_seq,
+                              const spec_bf16* drafts, int64_t draft_row_stride, int64_t drafter_stride,
+                              const int32_t* traj_tokens, int B, int K, int N, int V, float temperature, float* gamma,
+                              float* est_len, float* loss, const int32_t* sel, const int32_t* draft_tokens,
+                              const float* r_accept, const float* u_resample, int32_t* accepted_len,
+                              int32_t* out_token, uint8_t* accept_mask, void* workspace, size_t workspace_bytes,
+                              spec_stream_t stream) {
+  return gamma_call(target, target_row_stride, target_rows_per_seq, drafts, draft_row_stride, drafter_stride,
+                    traj_tokens, B, K, N, V, temperature, gamma, est_len, loss, sel, draft_tokens, r_accept,
+                    u_resample, accepted_len, out_token, accept_mask, workspace, workspace_bytes, stream, nullptr);
+}
+
+int spec_hedgespec_round(const spec_bf16* target, int64_t target_row_stride, int target_rows_per_seq,
+                         const spec_bf16* drafts, int64_t draft_row_stride, int64_t drafter_stride,
+                         const int32_t* traj_tokens, int B, int K, int N, int V, float temperature, float* gamma,
+                         float* est_len, float* loss, const int32_t* draft_tokens, const float* r_accept,
+                         const float* u_resample, int32_t* accepted_len, int32_t* out_token, uint8_t* accept_mask,
+                         double* state, double* weights, double* queue_loss, int32_t* queue_tokens, int32_t* round,
+                         int learner, float eta, float loss_scale, const float* v_select, int32_t* sel,
+                         int32_t* sel_hist, int Q, int T, void* workspace, size_t workspace_bytes,
+                         spec_stream_t stream) {
+  if (B < 1 || N < 1 || N > SPEC_MAX_N || K < 1 || K > SPEC_MAX_K || Q < K + 1 || Q > kMaxQueue || T < 1)
+    return SPEC_ERR_SHAPE;
+  if (!state || !weights || !queue_loss || !queue_tokens || !round || !v_select || !sel || !sel_hist || !accepted_len ||
+      !loss)
+    return SPEC_ERR_NULL;
+  if (learner != SPEC_LEARNER_NORMALHEDGE && learner != SPEC_LEARNER_HEDGE) return SPEC_ERR_PARAM;
+  if (!(loss_scale >= 0.0f) || !isfinite(loss_scale) || !(eta >= 0.0f) || !isfinite(eta)) return SPEC_ERR_PARAM;
+  const CensoredArgs a{state, weights, queue_loss, queue_tokens, round, loss, accepted_len, K, learner, eta,
+                       loss_scale, v_select, sel, sel_hist, B, N, Q, T};
+  return gamma_call(target, target_row_stride, target_rows_per_seq, drafts, draft_row_stride, drafter_stride,
+                    traj_tokens, B, K, N, V, temperature, gamma, est_len, loss, sel, draft_tokens, r_accept,
+                    u_resample, accepted_len, out_token, accept_mask, workspace, workspace_bytes, stream, &a);
 }
 
 size_t spec_tree_workspace_bytes(int B, int K, int N, int V, int topk) {
@@ -3051,8 +3192,9 @@ int hedge_censored_update(double* state, double* weights, double* queue_loss, in
     return SPEC_ERR_NULL;
   if (learner != SPEC_LEARNER_NORMALHEDGE && learner != SPEC_LEARNER_HEDGE) return SPEC_ERR_PARAM;
   if (!(loss_scale >= 0.0f) || !isfinite(loss_scale) || !(eta >= 0.0f) || !isfinite(eta)) return SPEC_ERR_PARAM;
-  hipLaunchKernelGGL(hedge_censored_kernel, dim3(B), dim3(64), 0, stream, state, weights, queue_loss, queue_tokens,
-                     round, loss, accepted_len, K, learner, eta, loss_scale, v_select, sel_out, sel_hist, B, N, Q, T);
+  const CensoredArgs a{state, weights, queue_loss, queue_tokens, round, loss, accepted_len, K, learner, eta,
+                       loss_scale, v_select, sel_out, sel_hist, B, N, Q, T};
+  hipLaunchKernelGGL(hedge_censored_kernel, dim3(B), dim3(64), 0, stream, a);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 

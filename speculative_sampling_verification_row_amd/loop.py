@@ -14,7 +14,10 @@ launches on one stream, with every pointer fixed in advance:
                              accepted length the next learner step counts
 
 so a round needs nothing from the host, and ``capture()`` records a round as a
-graph that ``replay()`` runs again, round after round.  Nothing is allocated
+graph that ``replay()`` runs again, round after round.  With the censoring
+learner the two are one launch by default (``spec_hedgespec_round``: the first
+draw unit of each sequence takes the learner step inside the gamma launch), so a
+round is one graph node; ``fused=False`` keeps the two launches.  Nothing is allocated
 after construction, and nothing in a round clears memory with a memset (the
 library's workspace is left zero by every call).
 
@@ -45,7 +48,7 @@ _ROW_KEYS = {"target": "target", "drafts": "drafts", "traj": "traj_tokens", "dra
 
 class HedgeSpecLoop:
     def __init__(self, rows, v_select, loss_scale: float, temperature: float = 1.0, *, delays=None, eta=None,
-                 queue_slots=None):
+                 queue_slots=None, fused: bool = True):
         sets = [rows] if isinstance(rows, dict) else list(rows)
         if not sets:
             raise ValueError("no rows")
@@ -62,13 +65,20 @@ class HedgeSpecLoop:
             self.learner = ScheduledLearner(B, N, K, T, loss_scale, v_select, delays, queue_slots=queue_slots,
                                             device=dev)
         self.ws = binding.make_workspace(B, K, N)
+        self.fused = bool(fused) and delays is None
         self.calls = []
         out = None
         for rs in sets:
-            call = binding.prepare_counterfactual_gamma(
-                rs["target"], rs["drafts"], rs["traj"], temperature, sel=self.learner.sel,
-                draft_tokens=rs["draft_tokens"], r_accept=rs["r_accept"], u_resample=rs["u_resample"],
-                workspace=self.ws, outputs=out, strict=True)
+            if self.fused:
+                call = binding.prepare_hedgespec_round(
+                    rs["target"], rs["drafts"], rs["traj"], temperature, self.learner,
+                    draft_tokens=rs["draft_tokens"], r_accept=rs["r_accept"], u_resample=rs["u_resample"],
+                    workspace=self.ws, outputs=out, strict=True)
+            else:
+                call = binding.prepare_counterfactual_gamma(
+                    rs["target"], rs["drafts"], rs["traj"], temperature, sel=self.learner.sel,
+                    draft_tokens=rs["draft_tokens"], r_accept=rs["r_accept"], u_resample=rs["u_resample"],
+                    workspace=self.ws, outputs=out, strict=True)
             out = call.outputs
             self.calls.append(call)
         self.out = out
@@ -86,7 +96,8 @@ class HedgeSpecLoop:
         self.t = 0
 
     def _round(self, j: int, stream=None) -> None:
-        self.learner.step(self.out["loss"], self.out["accepted_len"], stream)
+        if not self.fused:
+            self.learner.step(self.out["loss"], self.out["accepted_len"], stream)
         self.calls[j].launch(stream)
 
     def step(self, stream=None) -> None:

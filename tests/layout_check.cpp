@@ -32,7 +32,9 @@ int main() {
                               L.tot + 8 * static_cast<size_t>(B) * kMaxSlices * kMaxSlices <= L.gpart &&
                               L.gpart + 8 * gpart_words <= L.cand && L.cand <= L.pstat &&
                               L.pstat + (mode == MODE_GAMMA ? 8 * static_cast<size_t>(kMaxGrid) * kWaves : 0) <= L.pdone &&
-                              L.pdone + (mode == MODE_GAMMA ? 4 * static_cast<size_t>(kMaxGrid) : 0) <= L.total &&
+                              L.pdone + (mode == MODE_GAMMA ? 4 * static_cast<size_t>(kMaxGrid) : 0) <= L.selw &&
+                              L.selw + (mode == MODE_GAMMA ? 8 * static_cast<size_t>(B) : 0) <= L.lrnw &&
+                              L.lrnw + (mode == MODE_GAMMA ? 8 * static_cast<size_t>(B) : 0) <= L.total &&
                               L.total <= total && s.nsub <= kMaxSub && s.S <= kMaxSlices;
               if (!ok) {
                 ++bad;
@@ -123,6 +125,7 @@ int main() {
       }
     }
   }
+  for (int skip0 = 0; skip0 < 2; ++skip0)
   for (const auto& sp3 : SPs)
   for (int nG : nGs)
     for (int R1 : R1s)
@@ -131,8 +134,10 @@ int main() {
         const int64_t J = static_cast<int64_t>(nG) * R1;
         regular.assign(J, 0);
         bool ok = true;
+        // skip0 (fused HedgeSpec rounds, Q >= 2): slot 0 takes no rows
+        if (skip0 && Q >= 2 && row_chunk(J, R1, Q, 0, S, ncu, P, true).njobs != 0) ok = false;
         for (int slot = 0; slot < Q && ok; ++slot) {
-          const RowChunk c = row_chunk(J, R1, Q, slot, S, ncu, P);
+          const RowChunk c = row_chunk(J, R1, Q, slot, S, ncu, P, skip0 != 0);
           int have_target = -1;
           for (int n = 0; n < c.njobs && ok; ++n) {
             int q, r;

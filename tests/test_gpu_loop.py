@@ -72,7 +72,7 @@ def small_inputs(seed):
     return w, gen.make_gamma_inputs(w, seed=seed)
 
 
-def small_loop(binding, T=24, seed=0, scheduled=False, sets=1):
+def small_loop(binding, T=24, seed=0, scheduled=False, sets=1, fused=True, eta=None):
     from speculative_sampling_verification_row_amd.loop import HedgeSpecLoop
     w, x = small_inputs(seed)
     xs = [x] + [small_inputs(seed + 100 + j)[1] for j in range(sets - 1)]
@@ -81,7 +81,7 @@ def small_loop(binding, T=24, seed=0, scheduled=False, sets=1):
     v = rng.random((T, w.B), dtype=np.float32)
     rows = [loop_rows(xi) for xi in xs]
     lp = HedgeSpecLoop(rows if sets > 1 else rows[0], dev_f32(v), 1.0 / w.K,
-                       delays=dev_i32(delays) if scheduled else None)
+                       delays=dev_i32(delays) if scheduled else None, fused=fused, eta=eta)
     return lp, xs, delays, v
 
 
@@ -151,6 +151,26 @@ def check_selections_follow_oracle(hist, W_rounds, v, margin=1e-4):
             assert hist[t, b] == oracle.normalhedge_select(w, float(v[t, b])), (t, b)
             checked += 1
     return checked
+
+
+@pytest.mark.parametrize("eta", [None, 0.7])
+def test_fused_round_equals_two_launches(binding, eta):
+    """One launch per round (spec_hedgespec_round: the learner step inside the gamma
+    launch) gives, round after round, bit for bit what the learner's own launch
+    followed by the fused gamma launch gives: selections, learner state, gamma, losses,
+    accepted lengths and tokens (NormalHedge, and Hedge at rate eta; two row sets)."""
+    banner(f"fused round vs two launches eta={eta}")
+    T = 24
+    a = small_loop(binding, T, sets=2, fused=True, eta=eta)[0]
+    b = small_loop(binding, T, sets=2, fused=False, eta=eta)[0]
+    assert a.fused and not b.fused
+    for t in range(T):
+        a.step()
+        b.step()
+        for x, y in zip(snapshot(a), snapshot(b)):
+            np.testing.assert_array_equal(x, y, err_msg=f"round {t}")
+    assert int(a.ws.count_nonzero().item()) == 0 and int(b.ws.count_nonzero().item()) == 0
+    a.check()
 
 
 def test_loop_censored_rounds_match_oracle(binding):
