@@ -160,10 +160,9 @@ struct Params {
   unsigned long long* cand;   // draft-tree calls: [B][K][N][pieces][topk] piece records
   unsigned long long* pstat;  // gamma calls: [slots][S][kWaves] a slot's private statistics words (prefix target row)
   uint32_t* pdone;            // gamma calls: [slots] tickets of the members done with those words
-  // fused HedgeSpec rounds (spec_hedgespec_round): the learner step runs in each
-  // sequence's first draw unit; lrn.round == nullptr otherwise
-  CensoredArgs lrn;
-  unsigned long long* selw;  // [B] the round's drafter + 1, published by that unit to the sequence's others
+  // fused HedgeSpec rounds (spec_hedgespec_round), whose learner arguments come as
+  // the kernel's second argument; both nullptr in every other call
+  unsigned long long* selw;  // [B] the round's drafter + 1, published by the learner to the sequence's draw units
   unsigned long long* lrnw;  // [B] non-zero once the learner has read the previous round's loss
 };
 
@@ -619,7 +618,6 @@ __device__ __forceinline__ void row_subtiles(const uint16_t* trow, const uint16_
 
 struct Decision {
   WeightCtx w;
-  int drafter;   // the drafter whose rows are verified
   int A;         // accepted length; -1 invalid
   int draw_row;  // position of the draw row (A, or K for the bonus)
   int pair;      // 1: residual over (target A, draft A); 0: pt of target row K
@@ -659,7 +657,7 @@ __device__ __forceinline__ int unit_drafter(const Params& p, int b, int x, Lds& 
     L.flag = static_cast<int>(static_cast<uint32_t>(w)) - 1;  // a timeout leaves -1: no valid drafter
   }
   __syncthreads();
-  const int d = L.flag;
+  const int d = __builtin_amdgcn_readfirstlane(L.flag);  // the same in every lane: scalar for the row buffers
   __syncthreads();
   return d;
 }
@@ -670,11 +668,11 @@ __device__ __forceinline__ int unit_drafter(const Params& p, int b, int x, Lds& 
 // skip0), wave w of workgroup g taking sequences g kWaves + w, + S kWaves, ...
 // Each publishes the sequence's drafter (+1) to its draw units and, once it has
 // read the previous round's loss, the word that lets the estimator overwrite it.
-__device__ __forceinline__ void learner_steps(const Params& p, Lds& L) {
+__device__ __forceinline__ void learner_steps(const Params& p, const CensoredArgs& a, Lds& L) {
   const int S = p.S, g = blockIdx.x, w = wave_id();
   const int span = (gridDim.x / S >= 2 ? S : static_cast<int>(gridDim.x)) * kWaves;
   for (int b = g * kWaves + w; b < p.B; b += span) {
-    const int pick = censored_round(p.lrn, b, L.qtok[w]);
+    const int pick = censored_round(a, b, L.qtok[w]);
     if (lane_id() == 0) {
       st_agent_u64(&p.lrnw[b], 1ull);
       st_agent_u64(&p.selw[b], static_cast<unsigned long long>(static_cast<uint32_t>(pick)) + 1ull);
@@ -817,7 +815,6 @@ __device__ __forceinline__ void decide(const Params& p, int b, bool write_output
     const int nA = __builtin_amdgcn_readlane(n, A < K ? A : 0);
     if (t == 0) {
       Decision d;
-      d.drafter = dsafe;
       WeightCtx w;
       w.c = p.c;
       w.kd = 0.0f;
@@ -891,7 +888,7 @@ __device__ __forceinline__ void finish_sequence(const Params& p, int b, bool cle
     unsigned long long* w = part_row(p, b, 0);
     const int n = p.R * p.S * kWaves;
     for (int q = threadIdx.x; q < n; q += kThreads) st_agent_u64(w + q, 0ull);
-    if (p.lrn.round != nullptr && threadIdx.x == 0) st_agent_u64(&p.selw[b], 0ull);  // every draw unit has read it
+    if (p.selw != nullptr && threadIdx.x == 0) st_agent_u64(&p.selw[b], 0ull);  // every draw unit has read it
   }
   __syncthreads();
 }
@@ -1016,11 +1013,16 @@ __device__ __forceinline__ double kl_positions(const Params& p, int b, bool writ
 // W_TARGET (the bonus row, which has no merged statistics): each wave weighs its
 // share of a slice at its own reference k_w = ceil(max z c) over that share
 // (L.wref), and exchange_totals brings the slices to a common one.
-template <int MODE, bool SPECIAL, bool KL = false, bool MULTI = false>
-__device__ __forceinline__ int draw_slice(const Params& p, int b, int x, Decision& d, Lds& L) {
+// LEARN (fused HedgeSpec rounds): `drafter` is the learner's pick for the round;
+// the other calls look theirs up here (0, or sel[b]), each instance on its own,
+// which keeps the residual draws' row loads inside their own instances (a drafter
+// shared by both made the compiler hoist them above the choice between the two,
+// measured 2% slower).
+template <int MODE, bool SPECIAL, bool KL = false, bool MULTI = false, bool LEARN = false>
+__device__ __forceinline__ int draw_slice(const Params& p, int b, int x, Decision& d, int drafter, Lds& L) {
   const int tid = threadIdx.x, wave = wave_id();
   const uint16_t* trow = target_row(p, b, d.draw_row);
-  const uint16_t* drow = d.pair ? draft_row(p, b, d.drafter, d.draw_row) : trow;
+  const uint16_t* drow = d.pair ? draft_row(p, b, LEARN ? drafter : draw_drafter(p, b), d.draw_row) : trow;
   const uint32_t row_bytes = static_cast<uint32_t>((p.V + kVec - 1) / kVec) * 16u;
   const __amdgpu_buffer_rsrc_t tr = row_buffer(trow, row_bytes);
   const __amdgpu_buffer_rsrc_t dr = row_buffer(drow, row_bytes);
@@ -1147,7 +1149,8 @@ __device__ __forceinline__ void target_h_draw(const Params& p, int b, const Deci
 // LEARN: a fused HedgeSpec round (the learner step in the sequence's first unit).
 template <bool KL = false, bool MULTI = false, bool LEARN = false>
 __device__ __forceinline__ void unit_draw(const Params& p, int b, int x, int pre_n, Lds& L) {
-  decide<KL>(p, b, x == 0, pre_n, unit_drafter<LEARN>(p, b, x, L), L);
+  const int drafter = unit_drafter<LEARN>(p, b, x, L);
+  decide<KL>(p, b, x == 0, pre_n, drafter, L);
   Decision d = L.dl.d;
   // exact-KL gamma* outputs where the draw does not find them (no residual draw)
   if (KL && x == 0 && p.delta > 0.0 && p.gamma_star && !(d.A >= 0 && d.pair)) kl_positions(p, b, true, -1, L);
@@ -1164,9 +1167,9 @@ __device__ __forceinline__ void unit_draw(const Params& p, int b, int x, int pre
       p.out_token[b] = -1;
     }
   } else {
-    xs = !d.pair       ? draw_slice<W_TARGET, false, false, MULTI>(p, b, x, d, L)
-         : d.w.special ? draw_slice<W_RESID, true, KL, MULTI>(p, b, x, d, L)
-                       : draw_slice<W_RESID, false, false, MULTI>(p, b, x, d, L);
+    xs = !d.pair       ? draw_slice<W_TARGET, false, false, MULTI, LEARN>(p, b, x, d, drafter, L)
+         : d.w.special ? draw_slice<W_RESID, true, KL, MULTI, LEARN>(p, b, x, d, drafter, L)
+                       : draw_slice<W_RESID, false, false, MULTI, LEARN>(p, b, x, d, drafter, L);
     if (xs < 0 && x == 0) {
       if (d.w.special)
         target_h_draw<true>(p, b, d, L);
@@ -1408,7 +1411,7 @@ __device__ __forceinline__ void gamma_member(const Params& p, GammaLds& GL, int 
   const int tid = threadIdx.x;
   // dispatch slots as phase 0 counts them (all of them in the grid, else one)
   const int P = (p.slots >= 1 && p.slots <= kMaxSlots && p.ncu * p.slots == static_cast<int>(gridDim.x)) ? p.slots : 1;
-  const RowChunk ch = row_chunk(static_cast<int64_t>(nG) * R1, R1, Q, slot, S, p.ncu, P, p.lrn.round != nullptr);
+  const RowChunk ch = row_chunk(static_cast<int64_t>(nG) * R1, R1, Q, slot, S, p.ncu, P, p.selw != nullptr);
   if (ch.njobs == 0) return;
   const int prefix = ch.prefix, njobs = ch.njobs;
   unsigned long long* own_words = p.pstat + static_cast<size_t>(slot) * S * kWaves;
@@ -1678,7 +1681,7 @@ __device__ __forceinline__ void unit_estimate(const Params& p, int b, Lds& L) {
     }
     __syncthreads();
   }
-  if (p.lrn.round != nullptr) {
+  if (p.lrnw != nullptr) {
     // fused HedgeSpec round: the learner reads the previous round's loss from the
     // same buffer; overwrite it only once the learner is done with it (its only
     // reader here: clear the word)
@@ -1812,9 +1815,12 @@ union KernelLds {
 
 // MULTI: draw units of several slices (fused calls whose B S exceeds the grid).
 // LEARN: fused HedgeSpec rounds (spec_hedgespec_round), an instance of its own so
-// that the other gamma calls keep the leaner code.
+// that the other gamma calls keep the leaner code; the learner's arguments a are a
+// second kernel argument (unused by the other instances), which keeps them out of
+// the Params every kernel takes.
 template <bool MULTI, bool LEARN = false>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gamma_kernel(Params p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gamma_kernel(Params p,
+                                                                                                       CensoredArgs a) {
   __shared__ KernelLds KL;
   Lds& L = KL.units;
   const int G = gridDim.x, g = blockIdx.x;
@@ -1827,7 +1833,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   if (LEARN) {
     // slot 0's workgroups (all of the grid's, when it holds one slot) take the
     // learner steps first; their LDS is then handed to the groups
-    if (g < (gridDim.x / p.S >= 2 ? p.S : static_cast<int>(gridDim.x))) learner_steps(p, L);
+    if (g < (gridDim.x / p.S >= 2 ? p.S : static_cast<int>(gridDim.x))) learner_steps(p, a, L);
     __syncthreads();
   }
   if (p.mode == MODE_GAMMA) gamma_groups(p, KL.gamma);
@@ -2433,7 +2439,7 @@ __device__ __forceinline__ int hedge_select(double wcur, const float* v, int32_t
     if (pick < 0 && run > x) pick = q;
   }
   const int s = pick >= 0 ? pick : last_pos;
-  if (threadIdx.x == 0) sel[b] = s;
+  if (lane_id() == 0) sel[b] = s;
   return s;
 }
 
@@ -2769,8 +2775,10 @@ static int bind_workspace(Params& p, const Shape& s, void* ws, size_t bytes) {
   p.cand = reinterpret_cast<unsigned long long*>(base + L.cand);
   p.pstat = reinterpret_cast<unsigned long long*>(base + L.pstat);
   p.pdone = reinterpret_cast<uint32_t*>(base + L.pdone);
-  p.selw = reinterpret_cast<unsigned long long*>(base + L.selw);
-  p.lrnw = reinterpret_cast<unsigned long long*>(base + L.lrnw);
+  // the learner's words: gamma calls only (a verify or draft-tree layout has no room
+  // for them, and a null selw tells the kernels there is no learner)
+  p.selw = s.mode == MODE_GAMMA ? reinterpret_cast<unsigned long long*>(base + L.selw) : nullptr;
+  p.lrnw = s.mode == MODE_GAMMA ? reinterpret_cast<unsigned long long*>(base + L.lrnw) : nullptr;
   return SPEC_OK;
 }
 
@@ -2814,7 +2822,8 @@ static void plan_units(Params& p, const Shape& s) {
   p.ngroups = static_cast<int>(s.ngroups);
 }
 
-static int launch_flow(Params& p, const Shape& s, hipStream_t stream) {
+// lrn: the learner of a fused HedgeSpec round (gamma calls), else nullptr.
+static int launch_flow(Params& p, const Shape& s, hipStream_t stream, const CensoredArgs* lrn = nullptr) {
   // a slice is 32 KB of logits, so 2^31 slices exceed any device's memory; the
   // limit keeps the schedule in 32-bit arithmetic (with room for j * G + g)
   if (s.total0 > 0x3fffffffLL || static_cast<int64_t>(s.B) * s.P1 > 0x3fffffffLL || s.ngroups > 0x3fffffffLL ||
@@ -2825,7 +2834,7 @@ static int launch_flow(Params& p, const Shape& s, hipStream_t stream) {
   int grid = tree     ? resident_workgroups(tree_kernel, 3)
              : verify ? (p.kl_exact ? resident_workgroups(verify_kernel<true, false>, 2)
                                     : resident_workgroups(verify_kernel<false, false>, 0))
-                      : (p.lrn.round ? resident_workgroups(gamma_kernel<false, true>, 7)
+                      : (lrn ? resident_workgroups(gamma_kernel<false, true>, 7)
                                      : resident_workgroups(gamma_kernel<false>, 1));
   if (grid <= 0) return SPEC_ERR_HIP;
   const int ncu = compute_units();
@@ -2852,7 +2861,7 @@ static int launch_flow(Params& p, const Shape& s, hipStream_t stream) {
     // the instance with units of several slices holds as many workgroups
     const int g2 = verify ? (p.kl_exact ? resident_workgroups(verify_kernel<true, true>, 6)
                                         : resident_workgroups(verify_kernel<false, true>, 4))
-                          : (p.lrn.round ? resident_workgroups(gamma_kernel<true, true>, 8)
+                          : (lrn ? resident_workgroups(gamma_kernel<true, true>, 8)
                                          : resident_workgroups(gamma_kernel<true>, 5));
     if (g2 <= 0) return SPEC_ERR_HIP;
     if (g2 < grid) grid = g2;
@@ -2863,12 +2872,16 @@ static int launch_flow(Params& p, const Shape& s, hipStream_t stream) {
   }
   p.ncu = ncu;
   p.slots = slots;  // make_split weights the slots only when the grid is all of them
-  void (*kernel)(Params) = tree                  ? tree_kernel
-                           : verify && p.kl_exact ? (multi ? verify_kernel<true, true> : verify_kernel<true, false>)
-                           : verify               ? (multi ? verify_kernel<false, true> : verify_kernel<false, false>)
-                           : p.lrn.round          ? (multi ? gamma_kernel<true, true> : gamma_kernel<false, true>)
-                                                  : (multi ? gamma_kernel<true> : gamma_kernel<false>);
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, stream, p);
+  if (s.mode == MODE_GAMMA) {
+    void (*kernel)(Params, CensoredArgs) = lrn ? (multi ? gamma_kernel<true, true> : gamma_kernel<false, true>)
+                                               : (multi ? gamma_kernel<true> : gamma_kernel<false>);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, stream, p, lrn ? *lrn : CensoredArgs{});
+  } else {
+    void (*kernel)(Params) = tree                  ? tree_kernel
+                             : verify && p.kl_exact ? (multi ? verify_kernel<true, true> : verify_kernel<true, false>)
+                                                    : (multi ? verify_kernel<false, true> : verify_kernel<false, false>);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, stream, p);
+  }
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 
@@ -3074,8 +3087,8 @@ static int gamma_call(const spec_bf16* target, int64_t target_row_stride, int ta
   p.gamma = gamma;
   p.est_len = est_len;
   p.loss = loss;
-  if (lrn != nullptr) p.lrn = *lrn;  // else p.lrn.round stays nullptr: no learner step
-  return launch_flow(p, s, stream);
+  if (lrn == nullptr) p.selw = p.lrnw = nullptr;  // no learner step: the kernel reads neither word
+  return launch_flow(p, s, stream, lrn);
 }
 
 int spec_counterfactual_gamma(const spec_bf16* target, int64_t target_row_stride, int target_rows_per_seq,

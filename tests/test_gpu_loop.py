@@ -167,7 +167,8 @@ def test_fused_round_equals_two_launches(binding, eta):
     for t in range(T):
         a.step()
         b.step()
-        for x, y in zip(snapshot(a), snapshot(b)):
+        for x, y in zip(snapshot(a) + [to_np(a.learner.sel), to_np(a.learner.round)],
+                        snapshot(b) + [to_np(b.learner.sel), to_np(b.learner.round)]):
             np.testing.assert_array_equal(x, y, err_msg=f"round {t}")
     assert int(a.ws.count_nonzero().item()) == 0 and int(b.ws.count_nonzero().item()) == 0
     a.check()
