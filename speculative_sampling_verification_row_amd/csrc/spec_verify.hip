@@ -868,7 +868,9 @@ __device__ __forceinline__ void decide(const Params& p, int b, bool write_output
 // knows this, having read every draw unit's total (each unit publishes its total
 // after its last read of the words).  In a gamma call, the steps that read them
 // (nlast: the draw units of a fused call and the estimator) take a ticket and
-// the last one clears.
+// the last one clears.  LEARN: a fused HedgeSpec round, whose drafter word is
+// cleared with them.
+template <bool LEARN = false>
 __device__ __forceinline__ void finish_sequence(const Params& p, int b, bool clearer, Lds& L) {
   int last = clearer ? 1 : 0;
   if (p.nlast == 1) {
@@ -888,7 +890,7 @@ __device__ __forceinline__ void finish_sequence(const Params& p, int b, bool cle
     unsigned long long* w = part_row(p, b, 0);
     const int n = p.R * p.S * kWaves;
     for (int q = threadIdx.x; q < n; q += kThreads) st_agent_u64(w + q, 0ull);
-    if (p.selw != nullptr && threadIdx.x == 0) st_agent_u64(&p.selw[b], 0ull);  // every draw unit has read it
+    if (LEARN && threadIdx.x == 0) st_agent_u64(&p.selw[b], 0ull);  // every draw unit has read it
   }
   __syncthreads();
 }
@@ -1179,7 +1181,7 @@ __device__ __forceinline__ void unit_draw(const Params& p, int b, int x, int pre
   }
   // the unit that holds the crossing slice (unit 0 when there is none) has read
   // every unit's totals
-  finish_sequence(p, b, (xs < 0 ? 0 : MULTI ? slice_unit(p, xs) : xs) == x, L);
+  finish_sequence<LEARN>(p, b, (xs < 0 ? 0 : MULTI ? slice_unit(p, xs) : xs) == x, L);
 }
 
 // ---------------------------------------------------------------------------
@@ -1401,8 +1403,9 @@ __host__ __device__ inline void chunk_job(const RowChunk& c, int R1, int nG, int
 }
 
 // FULL: the member's slice lies inside the row (every member but the last of a
-// ragged row), so its loop carries no masking.
-template <bool FULL>
+// ragged row), so its loop carries no masking.  LEARN: a fused HedgeSpec round
+// (slot 0 takes no rows).
+template <bool FULL, bool LEARN>
 __device__ __forceinline__ void gamma_member(const Params& p, GammaLds& GL, int slot, int x) {
   const int S = p.S, Q = gridDim.x / S;
   const int K = p.K, N = p.N, R1 = N + 1, nG = p.ngroups;
@@ -1411,7 +1414,7 @@ __device__ __forceinline__ void gamma_member(const Params& p, GammaLds& GL, int 
   const int tid = threadIdx.x;
   // dispatch slots as phase 0 counts them (all of them in the grid, else one)
   const int P = (p.slots >= 1 && p.slots <= kMaxSlots && p.ncu * p.slots == static_cast<int>(gridDim.x)) ? p.slots : 1;
-  const RowChunk ch = row_chunk(static_cast<int64_t>(nG) * R1, R1, Q, slot, S, p.ncu, P, p.selw != nullptr);
+  const RowChunk ch = row_chunk(static_cast<int64_t>(nG) * R1, R1, Q, slot, S, p.ncu, P, LEARN);
   if (ch.njobs == 0) return;
   const int prefix = ch.prefix, njobs = ch.njobs;
   unsigned long long* own_words = p.pstat + static_cast<size_t>(slot) * S * kWaves;
@@ -1583,19 +1586,23 @@ __device__ __forceinline__ void gamma_member(const Params& p, GammaLds& GL, int 
 
 // Slot g / S of the workgroups, member g % S (workgroups beyond the last full slot
 // and slots beyond the last group have no group work).
+// LEARN: a fused HedgeSpec round, whose slot 0 takes no rows.
+template <bool LEARN>
 __device__ __forceinline__ void gamma_groups(const Params& p, GammaLds& GL) {
   const int S = p.S, Q = gridDim.x / S, g = blockIdx.x;
   if (g >= Q * S) return;
   const int x = g % S;
   if ((x + 1) * kSliceTok <= p.V)
-    gamma_member<true>(p, GL, g / S, x);
+    gamma_member<true, LEARN>(p, GL, g / S, x);
   else
-    gamma_member<false>(p, GL, g / S, x);
+    gamma_member<false, LEARN>(p, GL, g / S, x);
 }
 
 
 // Estimator step of a sequence: gamma, the estimator and the loss of every drafter,
-// positions in chunks whose rows fit the LDS arrays.
+// positions in chunks whose rows fit the LDS arrays.  LEARN: a fused HedgeSpec
+// round (the loss buffer is the learner's input too).
+template <bool LEARN>
 __device__ __forceinline__ void unit_estimate(const Params& p, int b, Lds& L) {
   const int tid = threadIdx.x, K = p.K, N = p.N;
   const int J = max(1, min(K, kRowCap / (N + 1)));
@@ -1681,7 +1688,7 @@ __device__ __forceinline__ void unit_estimate(const Params& p, int b, Lds& L) {
     }
     __syncthreads();
   }
-  if (p.lrnw != nullptr) {
+  if (LEARN) {
     // fused HedgeSpec round: the learner reads the previous round's loss from the
     // same buffer; overwrite it only once the learner is done with it (its only
     // reader here: clear the word)
@@ -1698,7 +1705,7 @@ __device__ __forceinline__ void unit_estimate(const Params& p, int b, Lds& L) {
   // every gamma unit of the sequence has published (all were read above): clear them
   unsigned long long* gw = p.gpart + static_cast<size_t>(b) * K * N * p.S * kWaves;
   for (int q = tid; q < K * N * p.S * kWaves; q += kThreads) st_agent_u64(gw + q, 0ull);
-  finish_sequence(p, b, false, L);
+  finish_sequence<LEARN>(p, b, false, L);
 }
 
 // ---------------------------------------------------------------------------
@@ -1713,7 +1720,10 @@ __device__ __forceinline__ void run_unit1(const Params& p, int u, int pre_n, Lds
   unit_draw<false, MULTI, LEARN>(p, b, u - b * p.P1, pre_n, L);
 }
 
-__device__ __forceinline__ void run_unit2(const Params& p, int v, Lds& L) { unit_estimate(p, v / p.P2, L); }
+template <bool LEARN>
+__device__ __forceinline__ void run_unit2(const Params& p, int v, Lds& L) {
+  unit_estimate<LEARN>(p, v / p.P2, L);
+}
 
 // The list is dealt in levels, the slowest slot first.  Level l covers slots
 // 0..P-1-l for rounds[l] rounds of slices (one per workgroup of those slots and
@@ -1836,7 +1846,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if (g < (gridDim.x / p.S >= 2 ? p.S : static_cast<int>(gridDim.x))) learner_steps(p, a, L);
     __syncthreads();
   }
-  if (p.mode == MODE_GAMMA) gamma_groups(p, KL.gamma);
+  if (p.mode == MODE_GAMMA) gamma_groups<LEARN>(p, KL.gamma);
   static_phase(p, G, g);
   for (int u = g; u < T1; u += G) {
     __syncthreads();
@@ -1848,7 +1858,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int T2 = p.B * p.P2;
   for (int v = (g + G - T1 % G) % G; v < T2; v += G) {
     __syncthreads();
-    run_unit2(p, v, L);
+    run_unit2<LEARN>(p, v, L);
   }
 }
 
