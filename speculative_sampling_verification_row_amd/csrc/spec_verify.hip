@@ -709,6 +709,7 @@ __host__ __device__ inline double kl_share(double c, double x, double plain) {
 // are then exact to about 1e-16 relative.  `iters` (host checks) receives the
 // number of steps taken.
 constexpr int kKlMaxSteps = 100;
+constexpr int kKlFloatSteps = 24;
 __host__ __device__ inline double gamma_star_kl(double c, double delta, int* iters = nullptr) {
   if (iters) *iters = 0;
   if (!(delta > 0.0) || !(c > 0.0)) return c;
@@ -725,6 +726,37 @@ __host__ __device__ inline double gamma_star_kl(double c, double delta, int* ite
   double g = c + sqrt(2.0 * delta) * sqrt(c * c1);
   if (g == c) return c;  // the Taylor step is below half an ulp of c: so is the root's
   if (!(g < hi)) g = mid();
+  // A start from single-precision Newton steps on the same f, whose logarithms cost
+  // a small fraction of the double ones (the double steps below, which decide the
+  // root, then take about two steps instead of five, and a root near 1 no longer
+  // costs them a run of midpoints).  Only where the Taylor step is not already
+  // close (its relative step above 1e-3) and c is a normal float; kept only if it
+  // lies strictly inside (c, 1).
+  if (g - c > 1e-3 * c && c > 1e-30) {
+    const float cf = static_cast<float>(c), lcf = static_cast<float>(lc), df = static_cast<float>(delta);
+    const float lc1f = log1pf(-cf);  // ln(1 - c)
+    float lof = cf, hif = 1.0f, gf = static_cast<float>(g);
+    for (int it = 0; it < kKlFloatSteps; ++it) {
+      if (!(gf > lof && gf < hif)) {
+        const float m = sqrtf(lof) * sqrtf(hif);
+        gf = m > lof && m < hif ? m : 0.5f * (lof + hif);
+        if (!(gf > lof && gf < hif)) break;  // the float bracket is exhausted
+      }
+      const float l1 = logf(gf) - lcf;      // ln(g / c)
+      const float l2 = log1pf(-gf) - lc1f;  // ln((1 - g) / (1 - c))
+      const float fv = gf * l1 + (1.0f - gf) * l2 - df;
+      if (fv <= 0.0f)
+        lof = gf;
+      else
+        hif = gf;
+      const float gn = gf - fv / (l1 - l2);
+      const bool done = fabsf(gn - gf) <= 1e-5f * fminf(gf - cf, 1.0f - gf);
+      gf = gn;
+      if (done) break;
+    }
+    const double gd = static_cast<double>(gf);
+    if (gd > c && gd < 1.0) g = gd;
+  }
   for (int it = 0; it < kKlMaxSteps; ++it) {
     if (iters) *iters = it + 1;
     const double d = g - c, x = d * rc, y = -d * rc1;
@@ -1009,7 +1041,8 @@ __device__ __forceinline__ double kl_positions(const Params& p, int b, bool writ
 }
 
 // With KL (exact-KL Cactus, delta > 0), the residual's gamma* is found here, while
-// the slice's loads are in flight, and completes d.w.
+// the slice's loads are in flight, and completes d.w; a bonus draw's unit 0 finds
+// every position's gamma* (outputs only) at the same point.
 // MULTI: the unit may take several slices (P1 < S); without it, slice x only,
 // in straight-line code.
 // W_TARGET (the bonus row, which has no merged statistics): each wave weighs its
@@ -1041,6 +1074,8 @@ __device__ __forceinline__ int draw_slice(const Params& p, int b, int x, Decisio
       vt[q] = buffer_load16(tr, tid * 16u, uo);
       vd[q] = MODE == W_RESID ? buffer_load16(dr, tid * 16u, uo) : make_uint4(0u, 0u, 0u, 0u);
     }
+    if (KL && MODE == W_TARGET && j == 0 && x == 0 && p.delta > 0.0 && p.gamma_star)
+      kl_positions(p, b, true, -1, L);  // the outputs only: a bonus draw needs no gamma*
     if (KL && MODE == W_RESID && SPECIAL && j == 0) {
       const double gsA = kl_positions(p, b, x == 0, d.A, L);
       const double ctA = L.dl.ct[d.A];
@@ -1154,8 +1189,9 @@ __device__ __forceinline__ void unit_draw(const Params& p, int b, int x, int pre
   const int drafter = unit_drafter<LEARN>(p, b, x, L);
   decide<KL>(p, b, x == 0, pre_n, drafter, L);
   Decision d = L.dl.d;
-  // exact-KL gamma* outputs where the draw does not find them (no residual draw)
-  if (KL && x == 0 && p.delta > 0.0 && p.gamma_star && !(d.A >= 0 && d.pair)) kl_positions(p, b, true, -1, L);
+  // exact-KL gamma* outputs of a sequence with no draw (a bonus draw finds them
+  // while its loads are in flight, a residual draw as it completes its weights)
+  if (KL && x == 0 && p.delta > 0.0 && p.gamma_star && d.A < 0) kl_positions(p, b, true, -1, L);
   int xs;
   if (d.A < 0) {
     // no draw: the totals are still exchanged, so that unit 0 knows when to clear
@@ -1169,7 +1205,7 @@ __device__ __forceinline__ void unit_draw(const Params& p, int b, int x, int pre
       p.out_token[b] = -1;
     }
   } else {
-    xs = !d.pair       ? draw_slice<W_TARGET, false, false, MULTI, LEARN>(p, b, x, d, drafter, L)
+    xs = !d.pair       ? draw_slice<W_TARGET, false, KL, MULTI, LEARN>(p, b, x, d, drafter, L)
          : d.w.special ? draw_slice<W_RESID, true, KL, MULTI, LEARN>(p, b, x, d, drafter, L)
                        : draw_slice<W_RESID, false, false, MULTI, LEARN>(p, b, x, d, drafter, L);
     if (xs < 0 && x == 0) {
