@@ -66,16 +66,20 @@ def loop_rows(x):
             "draft_tokens": dev_i32(x["draft_tokens"]), "r_accept": dev_f32(x["r"]), "u_resample": dev_f32(x["u"])}
 
 
-def small_inputs(seed):
-    w = gen.GammaWorkload("loop", B=4, K=3, N=3, V=3000, target_sigma=2.0, sigma_range=(0.3, 2.0), fused=True,
-                          draft_from="drafter0", config_id=97)
+def small_inputs(seed, big=False):
+    # big: 64 sequences of 151,936-token rows (10 slices each), more draw units than
+    # the grid holds, so the fused kernel's units of several slices run
+    w = (gen.GammaWorkload("loop", B=64, K=2, N=2, V=151936, target_sigma=2.0, sigma_range=(0.3, 2.0), fused=True,
+                           draft_from="drafter0", config_id=96) if big else
+         gen.GammaWorkload("loop", B=4, K=3, N=3, V=3000, target_sigma=2.0, sigma_range=(0.3, 2.0), fused=True,
+                           draft_from="drafter0", config_id=97))
     return w, gen.make_gamma_inputs(w, seed=seed)
 
 
-def small_loop(binding, T=24, seed=0, scheduled=False, sets=1, fused=True, eta=None):
+def small_loop(binding, T=24, seed=0, scheduled=False, sets=1, fused=True, eta=None, big=False):
     from speculative_sampling_verification_row_amd.loop import HedgeSpecLoop
-    w, x = small_inputs(seed)
-    xs = [x] + [small_inputs(seed + 100 + j)[1] for j in range(sets - 1)]
+    w, x = small_inputs(seed, big)
+    xs = [x] + [small_inputs(seed + 100 + j, big)[1] for j in range(sets - 1)]
     rng = np.random.default_rng(seed + 60)
     delays = rng.integers(0, 2 * w.K + 1, (T, w.B)).astype(np.int32)
     v = rng.random((T, w.B), dtype=np.float32)
@@ -164,6 +168,26 @@ def test_fused_round_equals_two_launches(binding, eta):
     a = small_loop(binding, T, sets=2, fused=True, eta=eta)[0]
     b = small_loop(binding, T, sets=2, fused=False, eta=eta)[0]
     assert a.fused and not b.fused
+    for t in range(T):
+        a.step()
+        b.step()
+        for x, y in zip(snapshot(a) + [to_np(a.learner.sel), to_np(a.learner.round)],
+                        snapshot(b) + [to_np(b.learner.sel), to_np(b.learner.round)]):
+            np.testing.assert_array_equal(x, y, err_msg=f"round {t}")
+    assert int(a.ws.count_nonzero().item()) == 0 and int(b.ws.count_nonzero().item()) == 0
+    a.check()
+
+
+def test_fused_round_equals_two_launches_multi_slice_units(binding):
+    """The same at 64 sequences of 151,936-token rows: 640 draw units for a grid of at
+    most 512, so each fused launch runs the instance whose draw units take several
+    slices, with the learner steps in its first gamma slot."""
+    banner("fused round vs two launches, units of several slices")
+    T = 6
+    a = small_loop(binding, T, fused=True, big=True)[0]
+    b = small_loop(binding, T, fused=False, big=True)[0]
+    S = -(-151936 // 16384)
+    assert 64 * S > 2 * torch.cuda.get_device_properties(0).multi_processor_count
     for t in range(T):
         a.step()
         b.step()
