@@ -394,9 +394,12 @@ int hedge_censored_update(double* state, double* weights, double* queue_loss, in
  * designs 1-3).  It computes exactly what hedge_censored_update (steps 1-4 above,
  * with these state arguments) followed by the fused spec_counterfactual_gamma
  * with sel = this round's selections computes, but the learner step runs inside
- * the gamma launch: the first draw unit of each sequence takes it and hands the
- * drafter to the sequence's other draw units, so a round is one kernel and no
- * node gap.
+ * the gamma launch: the waves of its first gamma slot take every sequence's step
+ * at the kernel's start (that slot then takes no gamma rows) and hand each
+ * sequence's drafter to its draw units, so a round is one kernel and no node gap.
+ * Like the other verification calls, it assumes that no other kernel holds the
+ * device's compute units while it runs (its waits between workgroups end after
+ * 2 s otherwise, with the workspace's fault word set).
  *
  * loss [B][N] and accepted_len [B] are both the previous round's outputs, which
  * the learner reads, and this round's, which the launch writes (the estimator
