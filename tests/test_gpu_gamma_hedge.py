@@ -80,6 +80,35 @@ def test_gamma_shapes(binding, V, N, K):
     compare_verify(oracle_fused_verify(x), got["accepted_len"], got["out_token"], got["accept_mask"], "fused")
 
 
+@pytest.mark.parametrize("B,K,N,V", [(16, 4, 5, 40000), (64, 2, 2, 151936)])
+def test_gamma_repeat_deterministic_one_workspace(binding, B, K, N, V):
+    """100 back-to-back fused gamma calls on one workspace give bit-identical outputs and
+    leave it zero: many gamma slots of one to three rows (16 sequences of 3-slice rows), or
+    more draw units than the grid holds (64 sequences of 10-slice rows); the first call is
+    checked against the oracle."""
+    banner(f"gamma repeat 100x B={B} K={K} N={N} V={V}")
+    w = gen.GammaWorkload("rep", B=B, K=K, N=N, V=V, target_sigma=2.0, sigma_range=(0.3, 2.0), fused=True,
+                          draft_from="drafter0", config_id=94)
+    x = gen.make_gamma_inputs(w, seed=B + V)
+    ws = binding.make_workspace(B, K, N)
+    args = (dev_bf16(x["target"]), dev_bf16(x["drafts"]), dev_i32(x["traj"]), 1.0)
+    kw = dict(sel=dev_i32(x["sel"]), draft_tokens=dev_i32(x["draft_tokens"]), r_accept=dev_f32(x["r"]),
+              u_resample=dev_f32(x["u"]), workspace=ws)
+    keys = ("gamma", "est_len", "loss", "accepted_len", "out_token", "accept_mask")
+    first = {k: to_np(v).copy() for k, v in binding.spec_counterfactual_gamma(*args, **kw).items() if k in keys}
+    for i in range(99):
+        out = binding.spec_counterfactual_gamma(*args, **kw)
+        torch.cuda.synchronize()
+        for k in keys:
+            np.testing.assert_array_equal(to_np(out[k]), first[k], err_msg=f"call {i + 2} {k}")
+    assert binding.workspace_fault(ws) == 0
+    assert int(ws.count_nonzero().item()) == 0
+    seqs = np.arange(0, B, max(1, B // 8))
+    check_gamma(first, oracle_gamma(x, seqs=seqs), seqs=seqs, label=f"repeat B={B} V={V}")
+    compare_verify(oracle_fused_verify(x, seqs=seqs), first["accepted_len"][seqs], first["out_token"][seqs],
+                   first["accept_mask"][seqs], "repeat verify")
+
+
 def test_identical_drafter_gives_gamma_one(binding):
     banner("gamma identical drafter")
     x = gen.make_gamma_inputs(gen.SMALL_MIXED, B=2, V=3000, N=2)
