@@ -70,8 +70,9 @@ int main() {
           }
         }
   printf("checked %d layouts, %d violations\n", checked, bad);
-  // phase-0 schedule: every slice of the list is dealt exactly once, and a
-  // workgroup's list ends for good at its first T0 (static_phase stops there)
+  // phase-0 schedule (slot-weighted, and the draft-tree calls' first-slot one):
+  // every slice of the list is dealt exactly once, and a workgroup's list ends
+  // for good at its first T0 (static_phase stops there)
   int sched_bad = 0, sched_checked = 0;
   const int Cs[] = {1, 3, 8, 256};
   const int T0s[] = {1, 2, 7, 100, 511, 512, 513, 5632, 24320, 100003};
@@ -82,7 +83,8 @@ int main() {
         for (int T0 : T0s) {
           const int G = P * C - dG;  // dG = 1: a grid that is not all of the slots (no weighting)
           if (G < 1) continue;
-          const Split sp = make_split(T0, C, P, G);
+          for (int tree = 0; tree < 2; ++tree) {
+          const Split sp = tree ? tree_split(T0, C, P, G) : make_split(T0, C, P, G);
           seen.assign(T0, 0);
           bool ok = true;
           for (int g = 0; g < G && ok; ++g) {
@@ -98,7 +100,8 @@ int main() {
           ++sched_checked;
           if (!ok) {
             ++sched_bad;
-            if (sched_bad < 10) printf("schedule violation P=%d C=%d G=%d T0=%d\n", P, C, G, T0);
+            if (sched_bad < 10) printf("schedule violation P=%d C=%d G=%d T0=%d tree=%d\n", P, C, G, T0, tree);
+          }
           }
         }
   printf("checked %d schedules, %d violations\n", sched_checked, sched_bad);
